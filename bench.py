@@ -1,0 +1,258 @@
+"""Benchmark of the CPR Gated DeltaNet library on one MI355X.
+
+Main line: prefill throughput (tokens/s) on B=4, T=2048, 16 q/k heads, 32 v
+heads, d=128, C=64, bf16 inputs, fp32 state and arithmetic, h0 ~ N(0, 0.02).
+A "step" is one gdn_prefill call over that batch, inputs already in HBM.
+Also reported: decode us/step for 64 sequences after a 4096-token prefill
+(256 steps, resync steps included), and the fp64 oracle's CPU throughput on a
+bounded sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+
+PREFILL = dict(N=4, T=2048, H_qk=16, H_v=32, d=128, C=64)
+DECODE = dict(N=64, P=4096, S=256, H_qk=16, H_v=32, d=128, C=64)
+
+
+def r_flops_per_token_head(d):
+    # token step per state element: alpha*s (1), fma delta*k (2), o-dot (2), next k-dot (2)
+    return 7 * d * d
+
+
+def decode_bytes_per_seq_head(d, C, G):
+    """Algorithmic HBM bytes of one decode step per (sequence, value head):
+    state read + write (fp32), the token's inputs (q, k bf16 shared by the G
+    value heads of a group; v bf16; beta, g fp32), o (fp32), the buffer append
+    (k-hat fp32 shared per group, v bf16, beta, g), and the resync (chunk
+    factors and state traffic of k_wy/k_scan) amortised over C steps."""
+    state = 2 * d * d * 4
+    token_in = (2 * d * 2) / G + d * 2 + 8
+    out = d * 4
+    append = (d * 4) / G + d * 2 + 8
+    # resync, per chunk: read buffer (k-hat fp32 / G, v bf16, beta, g), write W, U
+    # (fp32), G; then read S_chunk, W, U, k-hat, G and write S_chunk, S_run
+    wy = C * ((d * 4) / G + d * 2 + 8) + 2 * C * d * 4 + C * 4
+    scan = d * d * 4 + 2 * C * d * 4 + C * (d * 4) + C * 4 + 2 * d * d * 4
+    return state + token_in + out + append + (wy + scan) / C
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def bench_prefill(args, B, torch, make_inputs):
+    c = PREFILL
+    dev = "cuda"
+    inp = make_inputs([c["T"]] * c["N"], c["H_qk"], c["H_v"], c["d"], "bf16", seed=1,
+                      h0="normal", device=dev)
+    shape = B.make_shape(c["H_qk"], c["H_v"], c["d"], c["C"], torch.bfloat16)
+    T = inp["T"]
+    ws = torch.empty(B.workspace_bytes(shape, c["N"], T, B.OP_PREFILL), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty(T, c["H_v"], c["d"], dtype=torch.float32, device=dev)
+    cu = inp["cu_seqlens"].to(dev)
+
+    def step():
+        B.gdn_prefill(shape, inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], cu,
+                      h0=inp["h0"], ws=ws, out=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.profile_read("")  # drop anything recorded so far
+    B.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.profile_enable(False)
+    per_kernel = {}
+    for name in ["k_plan", "k_prep", "k_wy", "k_scan", "k_rec"]:
+        ms, n = B.profile_read(name)
+        per_kernel[name] = dict(avg_us=1e3 * ms / max(n, 1), launches=n)
+    ms_step = 1e3 * (t1 - t0) / args.steps
+    tokens = T
+    rec_us = per_kernel["k_rec"]["avg_us"]
+    rec_flops = r_flops_per_token_head(c["d"]) * T * c["H_v"]
+    achieved = rec_flops / (rec_us * 1e-6) / 1e12
+    return dict(ms_per_step=ms_step, value=tokens / (ms_step * 1e-3), tokens=tokens,
+                per_kernel=per_kernel,
+                roofline=dict(kernel="k_rec", bound="alu", achieved=round(achieved, 3),
+                              peak=PEAK_FP32_VECTOR_TFLOPS, unit="TFLOP/s",
+                              frac=round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4), traffic=None,
+                              algorithmic_per_launch=f"{rec_flops:.4e} flop"),
+                inputs=inp, shape=shape)
+
+
+def bench_decode(args, B, torch, make_inputs):
+    c = DECODE
+    dev = "cuda"
+    N, P, S = c["N"], c["P"], c["S"]
+    shape = B.make_shape(c["H_qk"], c["H_v"], c["d"], c["C"], torch.bfloat16)
+    pre = make_inputs([P] * N, c["H_qk"], c["H_v"], c["d"], "bf16", seed=2, h0="zero",
+                      device=dev)
+    cache = B.Cache(shape, N, dev, torch.bfloat16)
+    B.gdn_prefill(shape, pre["q"], pre["k"], pre["v"], pre["beta"], pre["g"],
+                  pre["cu_seqlens"].to(dev), cache=cache, want_hT=False)
+    del pre
+    tok = make_inputs([N] * S, c["H_qk"], c["H_v"], c["d"], "bf16", seed=3, device=dev)
+    q = tok["q"].view(S, N, c["H_qk"], c["d"])
+    k = tok["k"].view(S, N, c["H_qk"], c["d"])
+    v = tok["v"].view(S, N, c["H_v"], c["d"])
+    be = tok["beta"].view(S, N, c["H_v"])
+    g = tok["g"].view(S, N, c["H_v"])
+    o = torch.empty(N, c["H_v"], c["d"], dtype=torch.float32, device=dev)
+    ws = torch.empty(B.workspace_bytes(shape, N, 0, B.OP_DECODE), dtype=torch.uint8,
+                     device=dev)
+    snap = cache.clone()
+    torch.cuda.synchronize()
+    L = B.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cs = cache.struct()
+    pos0 = cache.pos.cpu()
+    pos_bufs = [((pos0 + s) % c["C"]).to(torch.int32).contiguous() for s in range(S)]
+    args_s = [(ctypes.c_void_p(q[s].data_ptr()), ctypes.c_void_p(k[s].data_ptr()),
+               ctypes.c_void_p(v[s].data_ptr()), ctypes.c_void_p(be[s].data_ptr()),
+               ctypes.c_void_p(g[s].data_ptr()), ctypes.c_void_p(pos_bufs[s].data_ptr()))
+              for s in range(S)]
+    shp, csp = ctypes.byref(shape), ctypes.byref(cs)
+    op, wsp, wsn = ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel()
+
+    def run_steps():
+        for s in range(S):
+            a = args_s[s]
+            rc = L.gdn_decode_step(shp, N, a[0], a[1], a[2], a[3], a[4], csp, a[5], op, wsp,
+                                   wsn, st)
+            if rc != 0:
+                raise RuntimeError(f"gdn_decode_step: {rc}")
+
+    run_steps()  # warm-up pass
+    times = []
+    per = {"k_decode": [0.0, 0], "k_wy_resync": [0.0, 0], "k_scan_resync": [0.0, 0]}
+    for rep in range(args.decode_reps):
+        for dst, src in zip(cache.tensors(), snap.tensors()):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        B.profile_read("")
+        B.profile_enable(True)
+        t0 = time.perf_counter()
+        run_steps()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        B.profile_enable(False)
+        for name in per:
+            ms, n = B.profile_read(name)
+            per[name][0] += ms
+            per[name][1] += n
+    us_step = 1e6 * min(times) / S
+    dec_us = 1e3 * per["k_decode"][0] / max(per["k_decode"][1], 1)
+    G = c["H_v"] // c["H_qk"]
+    step_bytes_alg = decode_bytes_per_seq_head(c["d"], c["C"], G) * N * c["H_v"]
+    dec_kernel_bytes = (2 * c["d"] * c["d"] * 4 + (2 * c["d"] * 2) / G + c["d"] * 2 + 8 +
+                        c["d"] * 4 + (c["d"] * 4) / G + c["d"] * 2 + 8) * N * c["H_v"]
+    achieved = dec_kernel_bytes / (dec_us * 1e-6) / 1e9
+    return dict(us_per_step=round(us_step, 2),
+                step_hbm_frac=round(step_bytes_alg / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                per_kernel={k: dict(avg_us=1e3 * v[0] / max(v[1], 1), launches=v[1])
+                            for k, v in per.items()},
+                roofline=dict(kernel="k_decode", bound="hbm", achieved=round(achieved, 1),
+                              peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None),
+                workload="decode 64 seqs x (4096 prefill + 256 steps), 16 q/k / 32 v heads, "
+                         "d128 C64 bf16")
+
+
+def cpu_baseline(inp):
+    """The fp64 oracle on sequences 0 and 1 of the prefill batch (all heads),
+    single process, BLAS limited to one thread."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import recurrent_fwd
+    from linear_attention_rnn_gated_amd.inputs import to_numpy_f64
+    seqs = [0, 1]
+    cu = inp["cu_seqlens"].cpu()
+    f = lambda t: to_numpy_f64(t.cpu()) if t is not None else None  # noqa: E731
+    args = (f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["beta"]), f(inp["g"]), cu.numpy())
+    h0 = f(inp["h0"])
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    if ctx:
+        with ctx:
+            recurrent_fwd(*args, h0=h0, seqs=seqs)
+    else:
+        recurrent_fwd(*args, h0=h0, seqs=seqs)
+    dt = time.perf_counter() - t0
+    ntok = int(sum(int(cu[n + 1] - cu[n]) for n in seqs))
+    return dict(value=round(ntok / dt, 2), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"sequences 0-1 of the prefill batch ({ntok} tokens, all 32 v heads), "
+                       f"fp64 numpy token recurrence, 1 thread, {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer shards by sequence/head without communication, see the design notes",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from linear_attention_rnn_gated_amd import binding as B
+    from linear_attention_rnn_gated_amd.inputs import make_inputs
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    B.lib()
+    pf = bench_prefill(args, B, torch, make_inputs)
+    line = {
+        "metric": "GDN prefill tokens/s (CPR; B4 T2048, 16 q/k / 32 v heads, d128, C64)",
+        "value": round(pf["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill B4 T2048 H_qk16 H_v32 d128 C64 bf16-in fp32-state",
+                   "global_batch": PREFILL["N"], "seq_len": PREFILL["T"],
+                   "parallelism": "single-gpu"},
+        "roofline": pf["roofline"],
+        "per_kernel_us": {k: round(v["avg_us"], 2) for k, v in pf["per_kernel"].items()},
+        "contract": B.contract_id(),
+    }
+    if not args.no_decode:
+        dc = bench_decode(args, B, torch, make_inputs)
+        line["decode"] = dc
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(pf["inputs"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet library, CPR schedule.
+ *
+ * The layer (Gated DeltaNet, named in the IsoExec write-up on agentlenshq.com,
+ * section "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet"; equations as
+ * published with the architecture, Yang et al., "Gated Delta Networks", ICLR
+ * 2025), per sequence and value head h, with S a d_v x d_k fp32 matrix:
+ *
+ *     alpha_t = exp(g_t)
+ *     S_t     = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t     = S_t q_t
+ *
+ * where q_t, k_t are the query/key head h / (H_v / H_qk) vectors, normalised
+ * to unit length (x / sqrt(sum x^2 + 1e-6)) when qk_l2norm is set, and q is
+ * then multiplied by `scale`.
+ *
+ * CPR ("chunkwise-parallel recurrent": the same section of the write-up, and
+ * the daily.dev digest's Q&A on CPR) keeps the token recurrence as the main
+ * computation, evaluated in parallel across C-token chunks, and has decode
+ * resynchronise its state every C tokens.  This library's reading:
+ *   - every chunk-start state comes from the chunk (WY) form of the
+ *     recurrence, scanned sequentially over the chunks of a sequence;
+ *   - every output o_t, and the state inside a chunk, comes from the token
+ *     recurrence started from that chunk's start state;
+ *   - decode runs the same token step and, after the C-th token of a chunk,
+ *     replaces its running state by the chunk form applied to the chunk-start
+ *     state and the chunk's buffered tokens.
+ * Chunks are counted from each sequence's first token.  Because all three
+ * entry points run the same device code on the same values, prefill, decode
+ * and the trainer forward give bit-identical o and final states, for any
+ * batch composition, run after run.
+ *
+ * Conventions for every call
+ *   - All tensors are dense, row-major, on the current HIP device; the caller
+ *     owns every buffer.  The library never allocates or frees device memory
+ *     in these calls; scratch comes from `ws`, sized by gdn_workspace_bytes.
+ *   - Packed layouts: q, k [T, H_qk, d_k]; v [T, H_v, d_v] in in_dtype;
+ *     beta, g [T, H_v] fp32; o [T, H_v, d_v] fp32.  States are fp32
+ *     [N, H_v, d_k, d_v] with d_v fastest, i.e. the transpose of S.
+ *   - cu_seqlens [N+1] int32: sequence n is tokens [cu[n], cu[n+1]).  It must
+ *     start at 0 and be non-decreasing.  Calls take a device copy (read by the
+ *     kernels) and a host copy (validated and used to size the launches); both
+ *     must hold the same values.  Kernels clamp every index to the buffers'
+ *     extents, so a mismatch gives wrong values but no out-of-bounds access.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call returns without waiting.
+ *   - Every argument is validated on the host before any launch; on a
+ *     validation error nothing is enqueued and nothing is written.  Shapes
+ *     outside the compiled claims return GDN_ERR_UNSUPPORTED -- they are never
+ *     run through a different arithmetic.
+ *   - Supported: d_k == d_v == 128 with C == 64, or d_k == d_v == 16 with
+ *     C == 16; H_v a multiple of H_qk; in_dtype fp32 or bf16.
+ *   - Calls that overlap on the same workspace or cache race; calls on
+ *     separate buffers may run concurrently.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = -1, /* NULL pointer, bad cu_seqlens, negative size, ... */
+  GDN_ERR_UNSUPPORTED = -2, /* shape outside the compiled claims              */
+  GDN_ERR_WORKSPACE = -3,   /* ws NULL or smaller than gdn_workspace_bytes     */
+  GDN_ERR_HIP = -4          /* a HIP runtime call failed                       */
+} gdn_status_t;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+
+typedef enum { GDN_OP_PREFILL = 0, GDN_OP_DECODE = 1, GDN_OP_FWD_BWD = 2 } gdn_op_t;
+
+/* Problem shape.  beta, g, states, o and gradients are always fp32. */
+typedef struct {
+  int32_t H_qk;      /* query/key heads                                     */
+  int32_t H_v;       /* value heads; value head h reads q/k head h/(H_v/H_qk) */
+  int32_t d_k, d_v;  /* head dimensions                                     */
+  int32_t C;         /* chunk length                                        */
+  int32_t in_dtype;  /* gdn_dtype_t of q, k, v                              */
+  int32_t qk_l2norm; /* 1: normalise q and k in-kernel; 0: use as given     */
+  float scale;       /* multiplies the (normalised) query                   */
+} gdn_shape_t;
+
+/*
+ * Decode cache of N sequences: the resumable state of token-by-token decode.
+ * It is plain device memory owned by the caller: copying it out and back in
+ * resumes decode bit-exactly.
+ */
+typedef struct {
+  float* S_run;   /* [N, H_v, d_k, d_v] running state after the last token      */
+  float* S_chunk; /* [N, H_v, d_k, d_v] state at the start of the current chunk */
+  float* kbuf;    /* [N, C, H_qk, d_k] normalised keys of the current chunk     */
+  void* vbuf;     /* [N, C, H_v, d_v] values of the current chunk, in_dtype     */
+  float* bbuf;    /* [N, C, H_v] beta of the current chunk                      */
+  float* gbuf;    /* [N, C, H_v] g of the current chunk                         */
+  int32_t* pos;   /* [N, H_v] tokens of the current chunk absorbed, 0..C-1     */
+} gdn_cache_t;
+
+/* Bytes of workspace `op` needs for n_seqs sequences of total_tokens tokens
+ * (decode: total_tokens is ignored).  0 for an invalid or unsupported shape. */
+size_t gdn_workspace_bytes(const gdn_shape_t* shape, int32_t n_seqs,
+                           int64_t total_tokens, int32_t op);
+
+/* Decode cache for n_seqs sequences with nothing decoded yet: S_run = S_chunk
+ * = h0 (or zero when h0 is NULL), pos = 0.  h0 is [N, H_v, d_k, d_v] fp32. */
+int gdn_cache_init(const gdn_shape_t* shape, int32_t n_seqs, const float* h0,
+                   gdn_cache_t* cache, void* stream);
+
+/*
+ * Rollout prefill (case "engine_prefill" in the write-up's contract section).
+ * h0 [N, H_v, d_k, d_v] nullable (zero).  Writes o; hT [N, H_v, d_k, d_v]
+ * (nullable) receives each sequence's final state.  If `cache` is non-NULL it
+ * is filled so that gdn_decode_step continues every sequence exactly where
+ * this prefill stopped (each sequence's current chunk is its last, possibly
+ * partial, chunk).
+ */
+int gdn_prefill(const gdn_shape_t* shape, int32_t n_seqs,
+                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                const void* q, const void* k, const void* v, const float* beta,
+                const float* g, const float* h0, float* o, float* hT,
+                gdn_cache_t* cache, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Rollout decode: one token for each of n_seqs sequences (case "engine
+ * decode").  q, k [N, H_qk, d_k], v [N, H_v, d_v] in in_dtype; beta, g
+ * [N, H_v] fp32; o [N, H_v, d_v] fp32.  Runs the token step on cache->S_run,
+ * appends the token to the chunk buffers and, for every sequence whose chunk
+ * is now complete, resynchronises S_run = S_chunk = chunk-form state and sets
+ * pos to 0.  pos_host ([N, H_v] mirror of cache->pos, nullable) only lets the
+ * host skip the resync launch when no sequence completes a chunk; with NULL
+ * the decision is taken on the device.  Out-of-range device pos values are
+ * clamped into [0, C).
+ */
+int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q,
+                    const void* k, const void* v, const float* beta,
+                    const float* g, gdn_cache_t* cache, const int32_t* pos_host,
+                    float* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Trainer forward + backward (case "trainer_fwd" and its gradient).  The
+ * forward runs exactly the prefill launches, so o and hT are bit-identical to
+ * gdn_prefill's.  dO [T, H_v, d_v] fp32; dhT [N, H_v, d_k, d_v] nullable
+ * (zero).  Writes dq, dk [T, H_qk, d_k], dv [T, H_v, d_v], dbeta, dg [T, H_v],
+ * dh0 [N, H_v, d_k, d_v], all fp32.  h0 nullable (zero).  The backward
+ * recomputes nothing it can keep: chunk-start states and chunk factors of the
+ * forward stay in `ws`.  No atomics: results are bitwise reproducible.
+ */
+int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs,
+                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                const void* q, const void* k, const void* v, const float* beta,
+                const float* g, const float* h0, const float* dO,
+                const float* dhT, float* o, float* hT, float* dq, float* dk,
+                float* dv, float* dbeta, float* dg, float* dh0, void* ws,
+                size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing (instrumentation).  While enabled, every launch the entry
+ * points make is bracketed by HIP events recorded on the call's stream.
+ * gdn_profile_read waits for the recorded events, returns the summed
+ * duration (ms) and launch count of the kernels whose name contains `kernel`
+ * (e.g. "k_rec"; NULL or "" = all), and forgets them.  Kernel names:
+ * k_plan, k_prep, k_wy, k_scan, k_rec, k_decode, k_wy_resync, k_scan_resync,
+ * k_cache_init and the k_bwd_* kernels of gdn_fwd_bwd.  Events are created
+ * by the library on first use and reused; no device memory is allocated.
+ * Thread-safe; records from concurrent calls are merged.
+ */
+int gdn_profile_enable(int on);
+int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches);
+
+/* Identifier of the compiled arithmetic contract (chunk lengths, epsilon,
+ * reduction orders, tiling).  Two builds give bit-identical results only if
+ * these strings are equal. */
+const char* gdn_contract_id(void);
+
+/* Human-readable text for a gdn_status_t. */
+const char* gdn_error_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,951 @@
+// Gated DeltaNet with the CPR schedule on MI355X (gfx950): kernels and C ABI.
+//
+// The layer and the schedule are described in include/gdn.h.  Two pieces of
+// arithmetic exist, and each is executed by exactly one piece of device code,
+// whichever entry point runs it:
+//
+//   R  the token step (one token, one value head, the d_v rows of the state
+//      spread one per lane).  Run by k_rec (prefill / trainer forward, state in
+//      registers for a whole chunk) and by k_decode (state streamed from HBM).
+//   B  the chunk form, giving the state at the end of a full chunk from the
+//      state at its start.  Run by k_wy (chunk factors W, U, G; parallel over
+//      chunks) and k_scan (the state update; sequential over the chunks of a
+//      sequence), both for prefill and for the decode resync.
+//
+// Equality of bits between prefill and decode rests on: identical IEEE
+// operation sequences per output element (the build uses -ffp-contract=off;
+// every fused multiply-add is an explicit fmaf), the same expf / sqrtf, the
+// same fixed summation orders, and per-item work that never depends on the
+// launch's grid or on other items.  gdn_contract_id() names this contract.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gdn.h"
+#include "gdn_plan.h"
+
+namespace {
+
+using bf16_t = uint16_t;
+
+// Read-only, wave-uniform operands are read through the constant address
+// space so the compiler issues scalar loads (the values land in SGPRs and feed
+// the VALU directly).
+using cfloat_p = const __attribute__((address_space(4))) float*;
+__device__ __forceinline__ cfloat_p as_const(const float* p) {
+  return reinterpret_cast<cfloat_p>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ float ldin(const float* p) { return *p; }
+__device__ __forceinline__ float ldin(const bf16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+
+// Largest n in [0, N) with arr[n] <= x (arr non-decreasing, arr[0] = 0): the
+// sequence that owns slot x.  Uniform across the block.
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ arr, int N, int64_t x) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (arr[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// L2 normalisation of one d-vector (d <= 128) by one full wave of 64 lanes.
+// Lane l holds elements l and l + 64.  The sum of squares is combined by a
+// butterfly, after which every lane holds the same value.  Every kernel that
+// needs a normalised q or k goes through this function, so all of them see
+// the same bits.
+template <int D, typename TIn>
+__device__ __forceinline__ void l2norm_wave(const TIn* __restrict__ x, float mul, int do_norm,
+                                            float& y0, float& y1) {
+  const int l = threadIdx.x & 63;
+  float x0 = (l < D) ? ldin(x + l) : 0.0f;
+  float x1 = (D > 64) ? ldin(x + l + 64) : 0.0f;
+  if (do_norm) {
+    float ss = fmaf(x1, x1, x0 * x0);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float r = 1.0f / sqrtf(ss + gdn::kNormEps);
+    x0 = x0 * r;
+    x1 = x1 * r;
+  }
+  y0 = x0 * mul;
+  y1 = x1 * mul;
+}
+
+// ---------------------------------------------------------------------------
+// Device planner: per-sequence prefix counts of chunks (ceil) and full chunks
+// (floor).  One thread; N is small next to the token count.
+__global__ void k_plan(const int32_t* __restrict__ cu, int N, int C, int32_t* __restrict__ cu_chunks,
+                       int32_t* __restrict__ cu_full) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  int32_t a = 0, b = 0;
+  cu_chunks[0] = 0;
+  cu_full[0] = 0;
+  for (int n = 0; n < N; ++n) {
+    int32_t L = cu[n + 1] - cu[n];
+    if (L < 0) L = 0;
+    a += (L + C - 1) / C;
+    b += L / C;
+    cu_chunks[n + 1] = a;
+    cu_full[n + 1] = b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prep: normalised k and q (times scale) in fp32, one wave per (token, q/k
+// head), written head-major and interleaved: qk[hq][t][0][:] = k-hat,
+// qk[hq][t][1][:] = q-hat.  A chunk's key/query stream for one head is then a
+// single contiguous run, read by k_rec as wave-uniform scalar loads.
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void k_prep(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                              float* __restrict__ qk, int64_t T, int H_qk,
+                                              float scale, int l2) {
+  const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // t * H_qk + hq
+  if (vec >= T * H_qk) return;
+  const int64_t t = vec / H_qk;
+  const int hq = static_cast<int>(vec - t * H_qk);
+  float* out = qk + (static_cast<int64_t>(hq) * T + t) * 2 * D;
+  const int l = threadIdx.x & 63;
+  float y0, y1;
+  l2norm_wave<D>(k + vec * D, 1.0f, l2, y0, y1);
+  if (l < D) out[l] = y0;
+  if (D > 64) out[l + 64] = y1;
+  l2norm_wave<D>(q + vec * D, scale, l2, y0, y1);
+  if (l < D) out[D + l] = y0;
+  if (D > 64) out[D + l + 64] = y1;
+}
+
+// ---------------------------------------------------------------------------
+// B, part 1 -- chunk factors.  For one full chunk of one value head, with
+// G_p the running fp32 sum of g (p ascending) and gam_p = exp(G_p):
+//   A_pr = beta_p * ((k_p . k_r) * exp(G_p - G_r))      p > r
+//   w_p  = beta_p gam_p k_p - sum_{r<p} A_pr w_r        (r ascending)
+//   u_p  = beta_p v_p       - sum_{r<p} A_pr u_r
+// Writes W, U [C, D] and G [C].  Items: every full chunk of a prefill
+// (RESYNC = false) or, for decode, every (sequence, head) whose chunk just
+// completed (pos == 0 after the token step), reading the chunk buffers.
+struct ChunkIO {
+  const float* khat;   // normalised keys, fp32 (see k_wy for the addressing)
+  const void* v;       // values, in_dtype, token stride H_v * D
+  const float* beta;   // token stride H_v
+  const float* g;      // token stride H_v
+  const int32_t* cu;   // prefill: cu_seqlens
+  const int32_t* cu_full;
+  const int32_t* pos;  // resync: cache pos [N, H_v]
+  float* W;
+  float* U;
+  float* G;
+  int N, H_qk, H_v;
+  int64_t T;           // prefill: total tokens (bounds); resync: N * C
+  int64_t max_slot;    // W/U/G slots available
+};
+
+// Start of the normalised keys of a chunk and the stride between its tokens:
+// prefill reads the prep layout [H_qk][T][2][D], resync the cache buffer
+// [N][C][H_qk][D].  Only the addressing differs; the values are the same bits.
+template <int D, bool RESYNC>
+__device__ __forceinline__ const float* key_rows(const float* base, int64_t T, int H_qk, int hq,
+                                                 int64_t tok0, int64_t& stride) {
+  if (RESYNC) {
+    stride = static_cast<int64_t>(H_qk) * D;
+    return base + (tok0 * H_qk + hq) * D;
+  }
+  stride = 2 * D;
+  return base + (static_cast<int64_t>(hq) * T + tok0) * 2 * D;
+}
+
+template <int D, int C, typename TIn, bool RESYNC>
+__global__ __launch_bounds__(256) void k_wy(ChunkIO io) {
+  constexpr int NT = 256;
+  __shared__ float sK[C][D + 1];
+  __shared__ float sA[C][C + 1];
+  __shared__ float sY[C][2 * D];  // column t: W (t < D) or U (t >= D); owned by thread t
+  __shared__ float sB[C], sG[C], sBG[C];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int hq = h / (io.H_v / io.H_qk);
+  int64_t tok0, slot;
+  if (RESYNC) {
+    const int n = blockIdx.x;
+    if (io.pos[static_cast<int64_t>(n) * io.H_v + h] != 0) return;
+    tok0 = static_cast<int64_t>(n) * C;
+    slot = n;
+  } else {
+    slot = blockIdx.x;
+    const int n = find_seq(io.cu_full, io.N, slot);
+    if (slot >= io.cu_full[io.N]) return;
+    tok0 = static_cast<int64_t>(io.cu[n]) + static_cast<int64_t>(slot - io.cu_full[n]) * C;
+  }
+  if (tok0 < 0 || tok0 + C > io.T || slot >= io.max_slot) return;
+
+  const TIn* v = static_cast<const TIn*>(io.v);
+  int64_t kst;
+  const float* krow = key_rows<D, RESYNC>(io.khat, io.T, io.H_qk, hq, tok0, kst);
+  for (int e = tid; e < C * D; e += NT) {
+    const int p = e / D, i = e % D;
+    sK[p][i] = krow[p * kst + i];
+  }
+  if (tid < C) sB[tid] = io.beta[(tok0 + tid) * io.H_v + h];
+  if (tid == 0) {
+    float acc = 0.0f;
+    for (int p = 0; p < C; ++p) {
+      acc = acc + io.g[(tok0 + p) * io.H_v + h];
+      sG[p] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < C) sBG[tid] = sB[tid] * expf(sG[tid]);
+  for (int e = tid; e < C * C; e += NT) {
+    const int p = e / C, r = e % C;
+    float a = 0.0f;
+    if (r < p) {
+      float dot = 0.0f;
+#pragma unroll 8
+      for (int i = 0; i < D; ++i) dot = fmaf(sK[p][i], sK[r][i], dot);
+      a = sB[p] * (dot * expf(sG[p] - sG[r]));
+    }
+    sA[p][r] = a;
+  }
+  __syncthreads();
+  // forward substitution: thread j < D owns column j of W, thread D + j of U
+  if (tid < 2 * D) {
+    const bool isW = tid < D;
+    const int j = isW ? tid : tid - D;
+    float* out = (isW ? io.W : io.U) + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
+    for (int p = 0; p < C; ++p) {
+      float x = isW ? sBG[p] * sK[p][j]
+                    : sB[p] * ldin(v + (tok0 + p) * io.H_v * D + static_cast<int64_t>(h) * D + j);
+      for (int r = 0; r < p; ++r) x = fmaf(-sA[p][r], sY[r][tid], x);
+      sY[p][tid] = x;
+      out[static_cast<int64_t>(p) * D + j] = x;
+    }
+  }
+  if (tid < C) io.G[(slot * io.H_v + h) * C + tid] = sG[tid];
+}
+
+// ---------------------------------------------------------------------------
+// B, part 2 -- the state update over one full chunk, for a tile of TILE rows
+// (d_v indices) of the state; rows evolve independently, so tiling is exact.
+//   Delta_pj = U_pj - sum_i W_pi S_ji                 (i ascending)
+//   Dt_pj    = Delta_pj * exp(G_last - G_p)
+//   S'_ji    = exp(G_last) S_ji  then  += Dt_pj k_pi   (p ascending, fmaf)
+// Prefill (RESYNC = false): one block per (sequence, head, tile) walks the
+// sequence's full chunks, storing each chunk-start state, the tail chunk's
+// start state, and the final state when the sequence ends on a chunk edge.
+// Resync: one step from cache S_chunk for each (sequence, head) with pos == 0,
+// writing S_chunk = S_run = result.
+struct ScanIO {
+  const float* khat;     // prefill: prep keys; resync: cache kbuf
+  const float* W;
+  const float* U;
+  const float* G;
+  const int32_t* cu;
+  const int32_t* cu_chunks;
+  const int32_t* cu_full;
+  const float* h0;       // nullable
+  float* states;         // prefill chunk-start states
+  float* hT;             // nullable
+  // cache (nullable in prefill)
+  float* S_run;
+  float* S_chunk;
+  int32_t* pos;
+  int N, H_qk, H_v;
+  int64_t T;
+  int64_t max_state_slot, max_full_slot;
+};
+
+template <int D, int C, int TILE, bool RESYNC>
+__global__ __launch_bounds__(256) void k_scan(ScanIO io) {
+  constexpr int NT = 256;
+  constexpr int NTILE = D / TILE;
+  __shared__ float sS[TILE][D + 1];
+  __shared__ float sW[C][D];
+  __shared__ float sK[C][D];
+  __shared__ float sD[C][TILE + 1];
+  __shared__ float sG[C];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x % NTILE;
+  const int h = (blockIdx.x / NTILE) % io.H_v;
+  const int n = blockIdx.x / (NTILE * io.H_v);
+  if (n >= io.N) return;
+  const int hq = h / (io.H_v / io.H_qk);
+  const int j0 = tile * TILE;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
+
+  int64_t tok0 = 0, nfull = 1, L = 0, slot0 = 0, fslot0 = 0;
+  if (RESYNC) {
+    if (io.pos[nh] != 0) return;
+    fslot0 = n;
+  } else {
+    tok0 = io.cu[n];
+    L = static_cast<int64_t>(io.cu[n + 1]) - tok0;
+    if (L < 0 || tok0 < 0 || tok0 + L > io.T) return;
+    nfull = L / C;
+    slot0 = io.cu_chunks[n];
+    fslot0 = io.cu_full[n];
+    if (slot0 + (L + C - 1) / C > io.max_state_slot || fslot0 + nfull > io.max_full_slot) return;
+  }
+
+  // load the starting state tile: S_ji = stored[i][j]
+  const float* src = RESYNC ? io.S_chunk + nh * DD : (io.h0 ? io.h0 + nh * DD : nullptr);
+  for (int e = tid; e < TILE * D; e += NT) {
+    const int i = e / TILE, jj = e % TILE;
+    sS[jj][i] = src ? src[static_cast<int64_t>(i) * D + j0 + jj] : 0.0f;
+  }
+  __syncthreads();
+
+  for (int64_t c = 0; c < nfull; ++c) {
+    if (!RESYNC) {  // chunk-start state of chunk c
+      float* dst = io.states + ((slot0 + c) * io.H_v + h) * DD;
+      for (int e = tid; e < TILE * D; e += NT) {
+        const int i = e / TILE, jj = e % TILE;
+        dst[static_cast<int64_t>(i) * D + j0 + jj] = sS[jj][i];
+      }
+    }
+    const int64_t fs = fslot0 + c;
+    const float* Wc = io.W + (fs * io.H_v + h) * static_cast<int64_t>(C) * D;
+    const float* Uc = io.U + (fs * io.H_v + h) * static_cast<int64_t>(C) * D;
+    const float* Gc = io.G + (fs * io.H_v + h) * C;
+    const int64_t ktok0 = RESYNC ? static_cast<int64_t>(n) * C : tok0 + c * C;
+    int64_t kst;
+    const float* krow = key_rows<D, RESYNC>(io.khat, io.T, io.H_qk, hq, ktok0, kst);
+    for (int e = tid; e < C * D; e += NT) {
+      const int p = e / D, i = e % D;
+      sW[p][i] = Wc[e];
+      sK[p][i] = krow[p * kst + i];
+    }
+    if (tid < C) sG[tid] = Gc[tid];
+    __syncthreads();
+    const float glast = sG[C - 1];
+    for (int e = tid; e < C * TILE; e += NT) {
+      const int p = e / TILE, jj = e % TILE;
+      float acc = 0.0f;
+#pragma unroll 8
+      for (int i = 0; i < D; ++i) acc = fmaf(sW[p][i], sS[jj][i], acc);
+      const float delta = Uc[static_cast<int64_t>(p) * D + j0 + jj] - acc;
+      sD[p][jj] = delta * expf(glast - sG[p]);
+    }
+    __syncthreads();
+    const float gam = expf(glast);
+    for (int e = tid; e < TILE * D; e += NT) {
+      const int jj = e / D, i = e % D;
+      float acc = gam * sS[jj][i];
+#pragma unroll 8
+      for (int p = 0; p < C; ++p) acc = fmaf(sD[p][jj], sK[p][i], acc);
+      sS[jj][i] = acc;  // each (jj, i) is read and written by this thread only
+    }
+    __syncthreads();
+  }
+
+  if (RESYNC) {
+    float* d1 = io.S_chunk + nh * DD;
+    float* d2 = io.S_run + nh * DD;
+    for (int e = tid; e < TILE * D; e += NT) {
+      const int i = e / TILE, jj = e % TILE;
+      const float x = sS[jj][i];
+      d1[static_cast<int64_t>(i) * D + j0 + jj] = x;
+      d2[static_cast<int64_t>(i) * D + j0 + jj] = x;
+    }
+    return;
+  }
+  const bool tail = (L % C) != 0;
+  for (int e = tid; e < TILE * D; e += NT) {
+    const int i = e / TILE, jj = e % TILE;
+    const int64_t off = static_cast<int64_t>(i) * D + j0 + jj;
+    const float x = sS[jj][i];
+    if (tail) {
+      io.states[((slot0 + nfull) * io.H_v + h) * DD + off] = x;  // tail chunk start
+      if (io.S_chunk) io.S_chunk[nh * DD + off] = x;
+    } else {
+      if (io.hT) io.hT[nh * DD + off] = x;
+      if (io.S_chunk) {
+        io.S_chunk[nh * DD + off] = x;
+        io.S_run[nh * DD + off] = x;
+      }
+    }
+  }
+  if (io.pos && tile == 0 && tid == 0) io.pos[nh] = static_cast<int32_t>(L % C);
+}
+
+// ---------------------------------------------------------------------------
+// R -- the token step, per lane = one row j (a d_v index) of the state, the
+// row's d_k entries in registers s[0..D).  For a token with a = s . k (taken
+// on the state before the token):
+//   alpha = expf(g);  u = alpha * a;  delta = beta * (v_j - u)
+//   s_i   = fmaf(delta, k_i, alpha * s_i)             i ascending
+//   o_j   = sum_i s_i q_i  (fmaf chain from 0, i ascending, updated s)
+// and the next token's a is the same kind of chain over the updated s.  The
+// key and query vectors are wave-uniform operands.
+template <int D, typename P>
+__device__ __forceinline__ float row_dot(const float (&s)[D], P x) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) a = fmaf(s[i], x[i], a);
+  return a;
+}
+
+// One token of R over a lane's row, operands as wave-uniform scalar loads:
+//   s_i = fmaf(delta, k_i, alpha * s_i);  o += s_i * q_i;  an += s_i * kn_i,
+// each chain in ascending i.  kq points at the token's [k | q] pair, kn at
+// the next token's k.  Every 8 elements an empty asm pins the accumulator
+// chains and a scheduling barrier stops the compiler from hoisting more scalar
+// loads than the SGPR file holds; neither changes any operation or its order.
+template <int D>
+__device__ __forceinline__ void r_token_pass(float (&s)[D], cfloat_p kq, cfloat_p kn, float alpha,
+                                             float delta, float& o, float& an) {
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    s[i] = fmaf(delta, kq[i], alpha * s[i]);
+    o = fmaf(s[i], kq[D + i], o);
+    an = fmaf(s[i], kn[i], an);
+    if ((i & 7) == 7) {
+      // pin both accumulator chains here so they are not sunk past the loads
+      asm volatile("" : "+v"(o), "+v"(an));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+struct RecIO {
+  const float* qk;   // prep layout [H_qk][T][2][D]
+  const void* v;
+  const float* beta;
+  const float* g;
+  const int32_t* cu;
+  const int32_t* cu_chunks;
+  const float* states;
+  float* o;
+  float* hT;       // nullable
+  // cache (nullable): the tail chunk leaves its running state and tokens
+  float* S_run;
+  float* kbuf;
+  void* vbuf;
+  float* bbuf;
+  float* gbuf;
+  int N, H_qk, H_v;
+  int64_t T, max_state_slot;
+};
+
+template <int D, int C, typename TIn>
+__global__ __launch_bounds__(64) void k_rec(RecIO io) {
+  const int slot = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int j = blockIdx.z * 64 + lane;
+  const bool act = j < D;
+  const int jc = act ? j : 0;  // inactive lanes (D < 64) read row 0 and store nothing
+  if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return;
+  const int n = find_seq(io.cu_chunks, io.N, slot);
+  const int G = io.H_v / io.H_qk;
+  const int hq = h / G;
+  const int64_t c = slot - io.cu_chunks[n];
+  const int64_t tok0 = static_cast<int64_t>(io.cu[n]) + c * C;
+  const int64_t end = io.cu[n + 1];
+  if (tok0 < 0 || end > io.T || tok0 >= end) return;
+  const int L = static_cast<int>(end - tok0 < C ? end - tok0 : C);
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const TIn* v = static_cast<const TIn*>(io.v) + (tok0 * io.H_v + h) * D + jc;
+  const float* bt = io.beta + tok0 * io.H_v + h;
+  const float* gt = io.g + tok0 * io.H_v + h;
+  float* op = io.o + (tok0 * io.H_v + h) * D + jc;
+  const int vs = io.H_v * D;  // < 2^20 (host-checked)
+  const int bs = io.H_v;
+
+  float s[D];
+  const float* st = io.states + (static_cast<int64_t>(slot) * io.H_v + h) * DD + jc;
+#pragma unroll
+  for (int i = 0; i < D; ++i) s[i] = st[i * D];
+
+  // key (t) / query (t) / key (t+1) streams, 2*D floats per token
+  cfloat_p kq = as_const(io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D);
+  float a = row_dot<D>(s, kq);
+  for (int t = 0; t < L; ++t) {
+    const float alpha = expf(*gt);
+    const float b = *bt;
+    const float vj = ldin(v);
+    const float u = alpha * a;
+    const float delta = b * (vj - u);
+    cfloat_p kn = kq + 2 * D;  // past the chunk's end on its last token: read, never used
+    float o = 0.0f, an = 0.0f;
+    r_token_pass<D>(s, kq, kn, alpha, delta, o, an);
+    if (act) *op = o;
+    a = an;
+    kq += 2 * D;
+    // opaque to the optimizer: otherwise it forwards this token's kn loads to
+    // the next token's k loads and must keep 128 values live across iterations
+    asm volatile("" : "+s"(kq));
+    gt += bs;
+    bt += bs;
+    v += vs;
+    op += vs;
+  }
+  if (L == C) return;
+  // tail chunk: the running state is the sequence's final state, and the
+  // partial chunk's tokens go to the decode buffers
+  const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
+  if (act && io.hT) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) io.hT[nh * DD + static_cast<int64_t>(i) * D + j] = s[i];
+  }
+  if (!io.S_run) return;
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) io.S_run[nh * DD + static_cast<int64_t>(i) * D + j] = s[i];
+  }
+  TIn* vb = static_cast<TIn*>(io.vbuf);
+  const TIn* vin = static_cast<const TIn*>(io.v);
+  for (int t = 0; t < L; ++t) {
+    const int64_t tk = tok0 + t;
+    const int64_t bi = static_cast<int64_t>(n) * C + t;
+    if (act) {
+      vb[(bi * io.H_v + h) * D + j] = vin[(tk * io.H_v + h) * D + j];
+      if (h % G == 0)
+        io.kbuf[(bi * io.H_qk + hq) * D + j] =
+            io.qk[((static_cast<int64_t>(hq) * io.T + tk) * 2) * D + j];
+    }
+    if (blockIdx.z == 0 && lane == 0) {
+      io.bbuf[bi * io.H_v + h] = io.beta[tk * io.H_v + h];
+      io.gbuf[bi * io.H_v + h] = io.g[tk * io.H_v + h];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode token step: one block of max(D, 64) lanes per (sequence, value
+// head); lane j owns row j.  Wave 0 normalises the token's q and k with
+// l2norm_wave (same bits as k_prep), then every lane runs R on its row of
+// S_run, exactly as k_rec does, and the token is appended to the chunk
+// buffers.  pos advances; it wraps to 0 when the chunk is complete, which is
+// what the resync launches test.
+struct DecIO {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  float* o;
+  float* S_run;
+  float* kbuf;
+  void* vbuf;
+  float* bbuf;
+  float* gbuf;
+  int32_t* pos;
+  int N, H_qk, H_v, l2;
+  float scale;
+};
+
+template <int D, int C, typename TIn>
+__global__ __launch_bounds__(D < 64 ? 64 : D) void k_decode(DecIO io) {
+  __shared__ float sq[D < 64 ? 64 : D];
+  __shared__ float sk[D < 64 ? 64 : D];
+  const int n = blockIdx.x;
+  const int h = blockIdx.y;
+  const int j = threadIdx.x;
+  const bool act = j < D;
+  const int G = io.H_v / io.H_qk;
+  const int hq = h / G;
+  const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  int p = io.pos[nh];
+  p = p < 0 ? 0 : (p >= C ? C - 1 : p);
+  if (threadIdx.x < 64) {
+    const TIn* q = static_cast<const TIn*>(io.q) + (static_cast<int64_t>(n) * io.H_qk + hq) * D;
+    const TIn* k = static_cast<const TIn*>(io.k) + (static_cast<int64_t>(n) * io.H_qk + hq) * D;
+    float y0, y1;
+    l2norm_wave<D>(q, io.scale, io.l2, y0, y1);
+    if (j < D) sq[j] = y0;
+    if (D > 64) sq[j + 64] = y1;
+    l2norm_wave<D>(k, 1.0f, io.l2, y0, y1);
+    if (j < D) sk[j] = y0;
+    if (D > 64) sk[j + 64] = y1;
+  }
+  __syncthreads();
+  const int jc = act ? j : 0;
+  float s[D];
+  float* sr = io.S_run + nh * DD;
+#pragma unroll
+  for (int i = 0; i < D; ++i) s[i] = sr[static_cast<int64_t>(i) * D + jc];
+  const TIn* v = static_cast<const TIn*>(io.v);
+  const float gt = io.g[nh];
+  const float alpha = expf(gt);
+  const float b = io.beta[nh];
+  const float vj = ldin(v + nh * D + jc);
+  const float a = row_dot<D>(s, static_cast<const float*>(sk));
+  const float u = alpha * a;
+  const float delta = b * (vj - u);
+  float o = 0.0f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    s[i] = fmaf(delta, sk[i], alpha * s[i]);
+    o = fmaf(s[i], sq[i], o);
+  }
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) sr[static_cast<int64_t>(i) * D + j] = s[i];
+    io.o[nh * D + j] = o;
+    const int64_t bt = static_cast<int64_t>(n) * C + p;
+    static_cast<TIn*>(io.vbuf)[(bt * io.H_v + h) * D + j] = v[nh * D + j];
+    if (h % G == 0) io.kbuf[(bt * io.H_qk + hq) * D + j] = sk[j];
+    if (j == 0) {
+      io.bbuf[bt * io.H_v + h] = b;
+      io.gbuf[bt * io.H_v + h] = gt;
+    }
+  }
+  __syncthreads();  // every lane has read pos
+  if (threadIdx.x == 0) io.pos[nh] = (p + 1 == C) ? 0 : p + 1;
+}
+
+// ---------------------------------------------------------------------------
+// Cache init: S_run = S_chunk = h0 (or 0), pos = 0.  Plain fill kernel (no
+// memset nodes, so the call is safe to capture in a graph).
+__global__ void k_cache_init(const float* __restrict__ h0, float* __restrict__ S_run,
+                             float* __restrict__ S_chunk, int32_t* __restrict__ pos,
+                             int64_t n_state, int64_t n_pos) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n_state;
+       e += stride) {
+    const float x = h0 ? h0[e] : 0.0f;
+    S_run[e] = x;
+    S_chunk[e] = x;
+  }
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n_pos;
+       e += stride)
+    pos[e] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing: optional HIP events around every launch.
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+// Brackets the launches made in its scope with events when timing is on.
+class Timed {
+ public:
+  Timed(const char* name, hipStream_t st) : st_(st) {
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (!p.on) return;
+    rec_.name = name;
+    rec_.a = p.get();
+    rec_.b = p.get();
+    if (rec_.a && rec_.b) {
+      (void)hipEventRecord(rec_.a, st_);
+      active_ = true;
+    }
+  }
+  ~Timed() {
+    if (!active_) return;
+    (void)hipEventRecord(rec_.b, st_);
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.recs.push_back(rec_);
+  }
+
+ private:
+  hipStream_t st_;
+  ProfRec rec_{};
+  bool active_ = false;
+};
+
+// ---------------------------------------------------------------------------
+// Host orchestration.
+
+constexpr int kTile128 = 32;  // state rows per k_scan block at d = 128
+
+template <int D>
+constexpr int scan_tile() { return D == 128 ? kTile128 : D; }
+
+template <int D, int C, typename TIn>
+int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const gdn::Layout& L,
+                   const int32_t* cu, const void* q, const void* k, const void* v,
+                   const float* beta, const float* g, const float* h0, float* o, float* hT,
+                   const gdn_cache_t* cache, char* ws, hipStream_t st) {
+  int32_t* cu_chunks = reinterpret_cast<int32_t*>(ws + L.cu_chunks);
+  int32_t* cu_full = reinterpret_cast<int32_t*>(ws + L.cu_full);
+  float* qk = reinterpret_cast<float*>(ws + L.qk);
+  float* W = reinterpret_cast<float*>(ws + L.W);
+  float* U = reinterpret_cast<float*>(ws + L.U);
+  float* Gs = reinterpret_cast<float*>(ws + L.G);
+  float* states = reinterpret_cast<float*>(ws + L.states);
+
+  {
+    Timed t_("k_plan", st);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, st, cu, N, C, cu_chunks, cu_full);
+  }
+  const int64_t nvec = cnt.T * s->H_qk;
+  if (nvec > 0) {
+    Timed t_("k_prep", st);
+    hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)), dim3(256), 0,
+                       st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
+                       s->H_qk, s->scale, s->qk_l2norm);
+  }
+  if (cnt.full > 0) {
+    ChunkIO io{};
+    io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_full;
+    io.W = W; io.U = U; io.G = Gs;
+    io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_slot = L.full_slots;
+    Timed t_("k_wy", st);
+    hipLaunchKernelGGL((k_wy<D, C, TIn, false>), dim3(static_cast<unsigned>(cnt.full), s->H_v),
+                       dim3(256), 0, st, io);
+  }
+  {
+    ScanIO io{};
+    io.khat = qk; io.W = W; io.U = U; io.G = Gs; io.cu = cu; io.cu_chunks = cu_chunks;
+    io.cu_full = cu_full; io.h0 = h0; io.states = states; io.hT = hT;
+    if (cache) { io.S_run = cache->S_run; io.S_chunk = cache->S_chunk; io.pos = cache->pos; }
+    io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
+    io.max_state_slot = L.state_slots; io.max_full_slot = L.full_slots;
+    constexpr int TILE = scan_tile<D>();
+    const int64_t blocks = static_cast<int64_t>(N) * s->H_v * (D / TILE);
+    if (blocks > 0) {
+      Timed t_("k_scan", st);
+      hipLaunchKernelGGL((k_scan<D, C, TILE, false>), dim3(static_cast<unsigned>(blocks)),
+                         dim3(256), 0, st, io);
+    }
+  }
+  if (cnt.chunks > 0) {
+    RecIO io{};
+    io.qk = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu;
+    io.cu_chunks = cu_chunks; io.states = states; io.o = o; io.hT = hT;
+    if (cache) {
+      io.S_run = cache->S_run; io.kbuf = cache->kbuf; io.vbuf = cache->vbuf;
+      io.bbuf = cache->bbuf; io.gbuf = cache->gbuf;
+    }
+    io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_state_slot = L.state_slots;
+    Timed t_("k_rec", st);
+    hipLaunchKernelGGL((k_rec<D, C, TIn>),
+                       dim3(static_cast<unsigned>(cnt.chunks), s->H_v, (D + 63) / 64), dim3(64), 0,
+                       st, io);
+  }
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+template <int D, int C, typename TIn>
+int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const void* q,
+                  const void* k, const void* v, const float* beta, const float* g,
+                  const gdn_cache_t* cache, bool resync, float* o, char* ws, hipStream_t st) {
+  DecIO io{};
+  io.q = q; io.k = k; io.v = v; io.beta = beta; io.g = g; io.o = o;
+  io.S_run = cache->S_run; io.kbuf = cache->kbuf; io.vbuf = cache->vbuf;
+  io.bbuf = cache->bbuf; io.gbuf = cache->gbuf; io.pos = cache->pos;
+  io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.l2 = s->qk_l2norm; io.scale = s->scale;
+  {
+    Timed t_("k_decode", st);
+    hipLaunchKernelGGL((k_decode<D, C, TIn>), dim3(N, s->H_v), dim3(D < 64 ? 64 : D), 0, st, io);
+  }
+  if (resync) {
+    float* W = reinterpret_cast<float*>(ws + L.W);
+    float* U = reinterpret_cast<float*>(ws + L.U);
+    float* Gs = reinterpret_cast<float*>(ws + L.G);
+    ChunkIO ci{};
+    ci.khat = cache->kbuf; ci.v = cache->vbuf; ci.beta = cache->bbuf; ci.g = cache->gbuf;
+    ci.pos = cache->pos; ci.W = W; ci.U = U; ci.G = Gs;
+    ci.N = N; ci.H_qk = s->H_qk; ci.H_v = s->H_v;
+    ci.T = static_cast<int64_t>(N) * C; ci.max_slot = N;
+    {
+      Timed t_("k_wy_resync", st);
+      hipLaunchKernelGGL((k_wy<D, C, TIn, true>), dim3(N, s->H_v), dim3(256), 0, st, ci);
+    }
+    ScanIO si{};
+    si.khat = cache->kbuf; si.W = W; si.U = U; si.G = Gs;
+    si.S_run = cache->S_run; si.S_chunk = cache->S_chunk; si.pos = cache->pos;
+    si.N = N; si.H_qk = s->H_qk; si.H_v = s->H_v; si.max_full_slot = N;
+    constexpr int TILE = scan_tile<D>();
+    Timed t_("k_scan_resync", st);
+    hipLaunchKernelGGL((k_scan<D, C, TILE, true>),
+                       dim3(static_cast<unsigned>(static_cast<int64_t>(N) * s->H_v * (D / TILE))),
+                       dim3(256), 0, st, si);
+  }
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// Calls f.template operator()<D, C, TIn>() for the shape's compiled variant.
+template <typename F>
+int dispatch(const gdn_shape_t* s, F&& f) {
+  if (s->d_k == 128 && s->C == 64) {
+    if (s->in_dtype == GDN_BF16) return f.template operator()<128, 64, bf16_t>();
+    return f.template operator()<128, 64, float>();
+  }
+  if (s->d_k == 16 && s->C == 16) {
+    if (s->in_dtype == GDN_BF16) return f.template operator()<16, 16, bf16_t>();
+    return f.template operator()<16, 16, float>();
+  }
+  return GDN_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_workspace_bytes(const gdn_shape_t* shape, int32_t n_seqs, int64_t total_tokens,
+                           int32_t op) {
+  if (gdn::check_shape(shape) != GDN_OK || n_seqs < 0) return 0;
+  if (op == GDN_OP_DECODE) total_tokens = 0;
+  if (total_tokens < 0) return 0;
+  return gdn::layout(shape, n_seqs, total_tokens, op).total;
+}
+
+int gdn_cache_init(const gdn_shape_t* shape, int32_t n_seqs, const float* h0, gdn_cache_t* cache,
+                   void* stream) {
+  int rc = gdn::check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (n_seqs < 0) return GDN_ERR_INVALID_ARG;
+  if ((rc = gdn::check_cache(cache)) != GDN_OK) return rc;
+  if (n_seqs == 0) return GDN_OK;
+  const int64_t n_state =
+      static_cast<int64_t>(n_seqs) * shape->H_v * shape->d_k * static_cast<int64_t>(shape->d_v);
+  const int64_t n_pos = static_cast<int64_t>(n_seqs) * shape->H_v;
+  int64_t blocks = (n_state + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  Timed t_("k_cache_init", static_cast<hipStream_t>(stream));
+  hipLaunchKernelGGL(k_cache_init, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), h0, cache->S_run, cache->S_chunk,
+                     cache->pos, n_state, n_pos);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_prefill(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
+                const float* beta, const float* g, const float* h0, float* o, float* hT,
+                gdn_cache_t* cache, void* ws, size_t ws_bytes, void* stream) {
+  int rc = gdn::check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host) return GDN_ERR_INVALID_ARG;
+  gdn::Counts cnt;
+  if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
+  if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
+  if (cache && (rc = gdn::check_cache(cache)) != GDN_OK) return rc;
+  const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_PREFILL);
+  if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (n_seqs == 0) return GDN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  return dispatch(shape, [&]<int D, int C, typename TIn>() {
+    return launch_prefill<D, C, TIn>(shape, n_seqs, cnt, L, cu_seqlens_dev, q, k, v, beta, g, h0,
+                                     o, hT, cache, w, st);
+  });
+}
+
+int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q, const void* k,
+                    const void* v, const float* beta, const float* g, gdn_cache_t* cache,
+                    const int32_t* pos_host, float* o, void* ws, size_t ws_bytes, void* stream) {
+  int rc = gdn::check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (n_seqs < 0) return GDN_ERR_INVALID_ARG;
+  if ((rc = gdn::check_cache(cache)) != GDN_OK) return rc;
+  if (n_seqs > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
+  if (n_seqs > 65535) return GDN_ERR_UNSUPPORTED;  // grid.x of the per-sequence launches
+  bool resync = true;
+  if (pos_host) {
+    resync = false;
+    const int64_t np = static_cast<int64_t>(n_seqs) * shape->H_v;
+    for (int64_t e = 0; e < np; ++e) {
+      if (pos_host[e] < 0 || pos_host[e] >= shape->C) return GDN_ERR_INVALID_ARG;
+      if (pos_host[e] + 1 == shape->C) resync = true;
+    }
+  }
+  const gdn::Layout L = gdn::layout(shape, n_seqs, 0, GDN_OP_DECODE);
+  if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (n_seqs == 0) return GDN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  return dispatch(shape, [&]<int D, int C, typename TIn>() {
+    return launch_decode<D, C, TIn>(shape, n_seqs, L, q, k, v, beta, g, cache, resync, o, w, st);
+  });
+}
+
+int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
+                const float* beta, const float* g, const float* h0, const float* dO,
+                const float* dhT, float* o, float* hT, float* dq, float* dk, float* dv,
+                float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+  (void)shape; (void)n_seqs; (void)cu_seqlens_dev; (void)cu_seqlens_host; (void)q; (void)k;
+  (void)v; (void)beta; (void)g; (void)h0; (void)dO; (void)dhT; (void)o; (void)hT; (void)dq;
+  (void)dk; (void)dv; (void)dbeta; (void)dg; (void)dh0; (void)ws; (void)ws_bytes; (void)stream;
+  return GDN_ERR_UNSUPPORTED;
+}
+
+int gdn_profile_enable(int on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on = on != 0;
+  return GDN_OK;
+}
+
+int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return GDN_ERR_INVALID_ARG;
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  double ms = 0.0;
+  int64_t cnt = 0;
+  int rc = GDN_OK;
+  std::vector<ProfRec> keep;
+  for (const ProfRec& r : p.recs) {
+    const bool match = !kernel || !kernel[0] || std::strstr(r.name, kernel) != nullptr;
+    if (!match) {
+      keep.push_back(r);
+      continue;
+    }
+    float t = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      rc = GDN_ERR_HIP;
+    ms += t;
+    ++cnt;
+    p.pool.push_back(r.a);
+    p.pool.push_back(r.b);
+  }
+  p.recs.swap(keep);
+  *total_ms = ms;
+  *launches = cnt;
+  return rc;
+}
+
+const char* gdn_contract_id(void) {
+  return "gdn-cpr/v1;eps=1e-6;claims=d16C16,d128C64;R=lane-row,fmaf-asc,o-after-update;"
+         "B=valu,scan-tile32;prep=wave-butterfly";
+}
+
+const char* gdn_error_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARG: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "shape outside the compiled claims";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

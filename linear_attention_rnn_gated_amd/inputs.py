@@ -27,18 +27,20 @@ def uniform_lengths(n, lo, hi, seed):
 
 
 def make_inputs(lens, H_qk, H_v, d, dtype="bf16", seed=0, h0="zero",
-                with_do=False, d_v=None):
+                with_do=False, d_v=None, device="cpu"):
     """Packed inputs for sequences of the given lengths.
 
     Returns a dict of CPU tensors: q, k [T, H_qk, d]; v [T, H_v, d_v];
     beta, g [T, H_v] fp32; h0 [N, H_v, d, d_v] fp32 or None; do [T, H_v, d_v]
-    fp32 or None; cu_seqlens int32 [N + 1]; plus the shape fields.
+    fp32 or None; cu_seqlens int32 [N + 1]; plus the shape fields.  With
+    device="cuda" the tensors are drawn there by that device's generator (same
+    recipe, different stream of numbers; used for large benchmark inputs).
     """
     d_v = d if d_v is None else d_v
-    gen = torch.Generator().manual_seed(seed)
+    gen = torch.Generator(device=device).manual_seed(seed)
     if isinstance(lens, tuple) and lens and lens[0] == "uniform":
         _, n, lo, hi = lens
-        lens = [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=gen)]
+        lens = [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=gen, device=device)]
     lens = [int(x) for x in lens]
     T = sum(lens)
     N = len(lens)
@@ -50,18 +52,19 @@ def make_inputs(lens, H_qk, H_v, d, dtype="bf16", seed=0, h0="zero",
     def unit(x):
         return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
 
-    q = unit(torch.randn(T, H_qk, d, generator=gen)).to(dt)
-    k = unit(torch.randn(T, H_qk, d, generator=gen)).to(dt)
-    v = torch.randn(T, H_v, d_v, generator=gen).to(dt)
-    beta = torch.sigmoid(torch.randn(T, H_v, generator=gen))
-    g = -torch.nn.functional.softplus(torch.randn(T, H_v, generator=gen))
+    kw = dict(generator=gen, device=device)
+    q = unit(torch.randn(T, H_qk, d, **kw)).to(dt)
+    k = unit(torch.randn(T, H_qk, d, **kw)).to(dt)
+    v = torch.randn(T, H_v, d_v, **kw).to(dt)
+    beta = torch.sigmoid(torch.randn(T, H_v, **kw))
+    g = -torch.nn.functional.softplus(torch.randn(T, H_v, **kw))
     if h0 == "normal":
-        h0t = 0.02 * torch.randn(N, H_v, d, d_v, generator=gen)
+        h0t = 0.02 * torch.randn(N, H_v, d, d_v, **kw)
     elif h0 == "zero":
         h0t = None
     else:
         raise ValueError(h0)
-    do = torch.randn(T, H_v, d_v, generator=gen) if with_do else None
+    do = torch.randn(T, H_v, d_v, **kw) if with_do else None
     return dict(q=q, k=k, v=v, beta=beta.contiguous(), g=g.contiguous(), h0=h0t,
                 do=do, cu_seqlens=cu, lens=lens, T=T, N=N, H_qk=H_qk, H_v=H_v,
                 d=d, d_v=d_v, dtype=dtype)

@@ -1,0 +1,268 @@
+"""GPU parity and bit-consistency of the forward paths (prefill, decode).
+
+Parity bar: max-abs difference to the fp64 oracle <= 2e-3 for bf16 inputs and
+<= 1e-5 for fp32 inputs, on o and on the final state.  Bit-consistency is
+exact: compared as int32 bit patterns.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gdn_helpers import (bit_equal, decode_tokens, group_slice, make_inputs, maxabs,
+                         oracle_fwd, rows_of, run_prefill, shape_for, sub_inputs, to_dev)
+from linear_attention_rnn_gated_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def check_parity(inp, o, hT, tol, seqs=None, scale=1.0, qk_l2norm=True):
+    ro, rh = oracle_fwd(inp, seqs=seqs, scale=scale, qk_l2norm=qk_l2norm)
+    if seqs is None:
+        e_o, e_h = maxabs(o, ro), maxabs(hT, rh)
+    else:
+        rows = rows_of(inp, seqs)
+        e_o = maxabs(o.cpu()[rows], ro[rows])
+        e_h = maxabs(hT.cpu()[seqs], rh[seqs])
+    say(f"  parity: max|o-oracle|={e_o:.3e} max|hT-oracle|={e_h:.3e} (tol {tol})")
+    assert np.isfinite(e_o) and np.isfinite(e_h)
+    assert e_o <= tol and e_h <= tol
+
+
+# ------------------------------------------------------------------ tiny fp32
+
+def test_tiny_fp32_prefill_parity_and_64_decode_steps_bit_identical():
+    """B=1, H=2, T=64, d=16, C=16, fp32, zero initial state."""
+    say("case: tiny fp32 d16 C16 T64")
+    inp = make_inputs([64], 2, 2, 16, "f32", seed=0, h0="zero")
+    o, hT, _ = run_prefill(inp)
+    check_parity(inp, o, hT, TOL["f32"])
+    shape = shape_for(inp)
+    cache = B.gdn_cache_init(shape, 1, "cuda", torch.float32)
+    od = decode_tokens(inp, cache, shape, 0, 64)
+    assert bit_equal(od[:, 0], o), "decode o != prefill o"
+    assert bit_equal(cache.S_run, hT), "decode state != prefill state"
+    assert bit_equal(cache.S_chunk, hT)
+
+
+# ------------------------------------------------------------------ d=128 parity
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_ragged_parity(dtype):
+    lens = [200, 64, 1, 130, 0, 129]
+    say(f"case: ragged prefill {dtype} lens={lens}")
+    inp = make_inputs(lens, 2, 4, 128, dtype, seed=11, h0="normal")
+    o, hT, _ = run_prefill(inp)
+    check_parity(inp, o, hT, TOL[dtype])
+
+
+def test_prefill_scale_without_norm():
+    say("case: scale 0.5, qk_l2norm off")
+    inp = make_inputs([150, 70], 1, 2, 128, "bf16", seed=12, h0="normal")
+    o, hT, _ = run_prefill(inp, scale=0.5, qk_l2norm=False)
+    check_parity(inp, o, hT, TOL["bf16"], scale=0.5, qk_l2norm=False)
+
+
+def test_degenerate_inputs():
+    say("case: beta = 0 with zero state gives o == 0")
+    inp = make_inputs([100, 64], 1, 2, 128, "bf16", seed=13, h0="zero")
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    o, hT, _ = run_prefill(inp)
+    assert torch.count_nonzero(o) == 0 and torch.count_nonzero(hT) == 0
+    say("case: near-reset gates (g = -30 on every 7th token)")
+    inp = make_inputs([150, 64], 1, 2, 128, "bf16", seed=14, h0="normal")
+    inp["g"][::7] = -30.0
+    o, hT, _ = run_prefill(inp)
+    check_parity(inp, o, hT, TOL["bf16"])
+    say("case: all sequences empty")
+    inp = make_inputs([0, 0], 1, 2, 128, "bf16", seed=15, h0="normal")
+    o, hT, _ = run_prefill(inp)
+    assert bit_equal(hT, inp["h0"].cuda())
+
+
+# ------------------------------------------------------------------ bit consistency
+
+@pytest.mark.parametrize("pre,use_pos_host", [(70, True), (64, False), (0, True)])
+def test_decode_continues_prefill_bit_exactly(pre, use_pos_host):
+    """Prefill `pre` tokens, decode the rest one by one; o and final states equal
+    one prefill of the whole sequence, bit for bit."""
+    total = 148
+    say(f"case: prefill {pre} + decode {total - pre}, pos_host={use_pos_host}")
+    inp = make_inputs([total] * 3, 2, 4, 128, "bf16", seed=21, h0="normal")
+    o_full, h_full, c_full = run_prefill(inp, cache=True)
+    shape = shape_for(inp)
+    if pre > 0:
+        first = dict(inp)
+        idx = torch.cat([torch.arange(n * total, n * total + pre) for n in range(3)])
+        for key in ["q", "k", "v", "beta", "g"]:
+            first[key] = inp[key][idx].contiguous()
+        first["cu_seqlens"] = torch.tensor([0, pre, 2 * pre, 3 * pre], dtype=torch.int32)
+        _, _, cache = run_prefill(first, cache=True)
+    else:
+        cache = B.gdn_cache_init(shape, 3, "cuda", torch.bfloat16, h0=inp["h0"].cuda())
+    od = decode_tokens(inp, cache, shape, pre, total - pre, use_pos_host=use_pos_host)
+    for n in range(3):
+        assert bit_equal(od[:, n], o_full[n * total + pre:(n + 1) * total]), f"o seq {n}"
+    assert bit_equal(cache.S_run, h_full)
+    # the full prefill's cache equals the decoded cache's current chunk state
+    assert bit_equal(cache.S_chunk, c_full.S_chunk)
+    assert torch.equal(cache.pos.cpu(), c_full.pos.cpu())
+
+
+def test_split_at_chunk_boundary_equals_one_prefill():
+    say("case: two prefills split at a chunk edge == one prefill")
+    inp = make_inputs([192, 256], 2, 4, 128, "bf16", seed=22, h0="normal")
+    o, hT, _ = run_prefill(inp)
+    cu = inp["cu_seqlens"].tolist()
+    a = dict(inp)
+    b = dict(inp)
+    cut = [128, 64]
+    ia = torch.cat([torch.arange(cu[n], cu[n] + cut[n]) for n in range(2)])
+    ib = torch.cat([torch.arange(cu[n] + cut[n], cu[n + 1]) for n in range(2)])
+    for key in ["q", "k", "v", "beta", "g"]:
+        a[key] = inp[key][ia].contiguous()
+        b[key] = inp[key][ib].contiguous()
+    a["cu_seqlens"] = torch.tensor([0, 128, 192], dtype=torch.int32)
+    b["cu_seqlens"] = torch.tensor([0, 64, 256], dtype=torch.int32)
+    oa, ha, _ = run_prefill(a)
+    b["h0"] = ha.cpu()
+    ob, hb, _ = run_prefill(b)
+    o_re = torch.cat([oa[:128], ob[:64], oa[128:], ob[64:]])
+    assert bit_equal(o_re, o) and bit_equal(hb, hT)
+
+
+def test_batch_composition_invariance():
+    lens = [300, 17, 64, 129, 0, 65]
+    say(f"case: packed vs alone vs reshuffled, lens={lens}")
+    inp = make_inputs(lens, 2, 4, 128, "bf16", seed=23, h0="normal")
+    o, hT, _ = run_prefill(inp)
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(lens)):
+        on, hn, _ = run_prefill(sub_inputs(inp, [n]))
+        assert bit_equal(on, o[cu[n]:cu[n + 1]]), f"alone {n}"
+        assert bit_equal(hn[0], hT[n])
+    perm = [3, 5, 1, 0, 4, 2]
+    sp = sub_inputs(inp, perm)
+    op, hp, _ = run_prefill(sp)
+    cp = sp["cu_seqlens"].tolist()
+    for i, n in enumerate(perm):
+        assert bit_equal(op[cp[i]:cp[i + 1]], o[cu[n]:cu[n + 1]]), f"reshuffled {n}"
+        assert bit_equal(hp[i], hT[n])
+
+
+def test_run_to_run_bit_identical():
+    say("case: run to run")
+    inp = make_inputs([333, 64, 1000], 2, 4, 128, "bf16", seed=24, h0="normal")
+    o1, h1, _ = run_prefill(inp)
+    o2, h2, _ = run_prefill(inp)
+    assert bit_equal(o1, o2) and bit_equal(h1, h2)
+
+
+def test_cache_checkpoint_resume():
+    say("case: decode cache saved to host and restored mid-chunk")
+    total, pre, mid = 200, 50, 40
+    inp = make_inputs([total] * 2, 1, 2, 128, "bf16", seed=25, h0="normal")
+    shape = shape_for(inp)
+    first = dict(inp)
+    idx = torch.cat([torch.arange(n * total, n * total + pre) for n in range(2)])
+    for key in ["q", "k", "v", "beta", "g"]:
+        first[key] = inp[key][idx].contiguous()
+    first["cu_seqlens"] = torch.tensor([0, pre, 2 * pre], dtype=torch.int32)
+    _, _, cache = run_prefill(first, cache=True)
+    decode_tokens(inp, cache, shape, pre, mid)
+    saved = [t.cpu() for t in cache.tensors()]
+    rest = total - pre - mid
+    o_a = decode_tokens(inp, cache, shape, pre + mid, rest)
+    restored = B.Cache(shape, 2, "cuda", torch.bfloat16)
+    for dst, src in zip(restored.tensors(), saved):
+        dst.copy_(src.cuda())
+    o_b = decode_tokens(inp, restored, shape, pre + mid, rest)
+    assert bit_equal(o_a, o_b) and bit_equal(cache.S_run, restored.S_run)
+
+
+# ------------------------------------------------------------------ full-size shapes
+
+def test_prefill_b4_t2048_full_size():
+    """B=4, T=2048, 16 q/k heads, 32 v heads, d=128, C=64, bf16, h0 ~ N(0, 0.02):
+    oracle on one q/k group of two sequences; all outputs finite."""
+    say("case: prefill B4 T2048 H16/32 d128 (sampled oracle)")
+    inp = make_inputs([2048] * 4, 16, 32, 128, "bf16", seed=1, h0="normal")
+    o, hT, _ = run_prefill(inp)
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
+    for hq in [0, 11]:
+        gi, hv = group_slice(inp, hq)
+        ro, rh = oracle_fwd(gi, seqs=[0, 3])
+        rows = rows_of(inp, [0, 3])
+        e_o = maxabs(o.cpu()[rows][:, hv], ro[rows])
+        e_h = maxabs(hT.cpu()[[0, 3]][:, hv], rh[[0, 3]])
+        say(f"  group {hq}: max|o-oracle|={e_o:.3e} max|hT-oracle|={e_h:.3e}")
+        assert e_o <= TOL["bf16"] and e_h <= TOL["bf16"]
+    o2, h2, _ = run_prefill(inp)
+    assert bit_equal(o, o2) and bit_equal(hT, h2)
+
+
+def test_decode_64_seqs_4096_plus_256_equals_single_prefill():
+    """64 sequences prefilled with 4096 tokens, then 256 decode steps; outputs and
+    states equal one 4352-token prefill bit for bit; one group checked against
+    the oracle on one sequence's decoded tokens."""
+    say("case: decode 64 x (4096 + 256) vs prefill 4352")
+    N, P, S = 64, 4096, 256
+    inp = make_inputs([P + S] * N, 16, 32, 128, "bf16", seed=2, h0="zero")
+    o_full, h_full, _ = run_prefill(inp)
+    first = dict(inp)
+    idx = torch.cat([torch.arange(n * (P + S), n * (P + S) + P) for n in range(N)])
+    for key in ["q", "k", "v", "beta", "g"]:
+        first[key] = inp[key][idx].contiguous()
+    first["cu_seqlens"] = torch.arange(0, (N + 1) * P, P, dtype=torch.int32)
+    _, _, cache = run_prefill(first, cache=True)
+    shape = shape_for(inp)
+    od = decode_tokens(inp, cache, shape, P, S)
+    for n in range(N):
+        assert bit_equal(od[:, n], o_full[n * (P + S) + P:(n + 1) * (P + S)]), f"seq {n}"
+    assert bit_equal(cache.S_run, h_full)
+    gi, hv = group_slice(inp, 5)
+    ro, rh = oracle_fwd(gi, seqs=[7])
+    e = maxabs(od[:, 7, hv].cpu(), ro[7 * (P + S) + P:8 * (P + S)])
+    eh = maxabs(h_full[7, hv].cpu(), rh[7])
+    say(f"  seq 7 group 5: max|o-oracle|={e:.3e} max|hT-oracle|={eh:.3e}")
+    assert e <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_varlen_32_seqs_packed_alone_reshuffled():
+    """32 sequences, lengths uniform in [128, 8192], packed; each sequence's
+    output equals running it alone and in a reshuffled batch, bit for bit."""
+    inp = make_inputs(("uniform", 32, 128, 8192), 16, 32, 128, "bf16", seed=4, h0="zero")
+    say(f"case: varlen 32 seqs, T={inp['T']}")
+    o, hT, _ = run_prefill(inp)
+    assert torch.isfinite(o).all()
+    cu = inp["cu_seqlens"].tolist()
+    for n in [0, 13, 31]:
+        on, hn, _ = run_prefill(sub_inputs(inp, [n]))
+        assert bit_equal(on, o[cu[n]:cu[n + 1]]) and bit_equal(hn[0], hT[n]), f"alone {n}"
+    perm = list(np.random.default_rng(0).permutation(32))
+    sp = sub_inputs(inp, perm)
+    op, hp, _ = run_prefill(sp)
+    cp = sp["cu_seqlens"].tolist()
+    for i, n in enumerate(perm):
+        assert bit_equal(op[cp[i]:cp[i + 1]], o[cu[n]:cu[n + 1]]), f"reshuffled {n}"
+        assert bit_equal(hp[i], hT[n])
+    short = int(np.argmin(inp["lens"]))
+    gi, hv = group_slice(inp, 3)
+    ro, rh = oracle_fwd(gi, seqs=[short])
+    rows = rows_of(inp, [short])
+    e = maxabs(o.cpu()[rows][:, hv], ro[rows])
+    say(f"  shortest seq {short} (len {inp['lens'][short]}): max|o-oracle|={e:.3e}")
+    assert e <= TOL["bf16"]
