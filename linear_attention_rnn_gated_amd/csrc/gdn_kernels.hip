@@ -163,8 +163,17 @@ __device__ __forceinline__ const float* key_rows(const float* base, int64_t T, i
   return base + (static_cast<int64_t>(hq) * T + tok0) * 2 * D;
 }
 
-template <int D, int C, typename TIn, bool RESYNC>
+// Item modes of the chunk-form kernels.  kFull: the full chunks of a prefill
+// (W/U/G slots = full-chunk slots).  kResync: the decode buffers.  kAll: every
+// chunk of every sequence, the last one possibly partial (trainer forward;
+// W/U/G slots = chunk slots).  A partial chunk of L < C tokens is padded with
+// rows k = 0, v = 0, beta = 0, g = 0, which leaves the chunk algebra exact;
+// a full chunk executes the same operations in every mode.
+enum Mode { kFull = 0, kResync = 1, kAll = 2 };
+
+template <int D, int C, typename TIn, int MODE>
 __global__ __launch_bounds__(256) void k_wy(ChunkIO io) {
+  constexpr bool RESYNC = MODE == kResync;
   constexpr int NT = 256;
   __shared__ float sK[C][D + 1];
   __shared__ float sA[C][C + 1];
@@ -174,31 +183,40 @@ __global__ __launch_bounds__(256) void k_wy(ChunkIO io) {
   const int h = blockIdx.y;
   const int hq = h / (io.H_v / io.H_qk);
   int64_t tok0, slot;
-  if (RESYNC) {
+  int L = C;
+  if (MODE == kResync) {
     const int n = blockIdx.x;
     if (io.pos[static_cast<int64_t>(n) * io.H_v + h] != 0) return;
     tok0 = static_cast<int64_t>(n) * C;
     slot = n;
-  } else {
+  } else if (MODE == kFull) {
     slot = blockIdx.x;
     const int n = find_seq(io.cu_full, io.N, slot);
     if (slot >= io.cu_full[io.N]) return;
     tok0 = static_cast<int64_t>(io.cu[n]) + static_cast<int64_t>(slot - io.cu_full[n]) * C;
+  } else {
+    slot = blockIdx.x;
+    if (slot >= io.cu_full[io.N]) return;  // cu_full holds the chunk prefix in this mode
+    const int n = find_seq(io.cu_full, io.N, slot);
+    tok0 = static_cast<int64_t>(io.cu[n]) + static_cast<int64_t>(slot - io.cu_full[n]) * C;
+    const int64_t rem = static_cast<int64_t>(io.cu[n + 1]) - tok0;
+    L = rem < C ? static_cast<int>(rem) : C;
+    if (L <= 0) return;
   }
-  if (tok0 < 0 || tok0 + C > io.T || slot >= io.max_slot) return;
+  if (tok0 < 0 || tok0 + L > io.T || slot >= io.max_slot) return;
 
   const TIn* v = static_cast<const TIn*>(io.v);
   int64_t kst;
   const float* krow = key_rows<D, RESYNC>(io.khat, io.T, io.H_qk, hq, tok0, kst);
   for (int e = tid; e < C * D; e += NT) {
     const int p = e / D, i = e % D;
-    sK[p][i] = krow[p * kst + i];
+    sK[p][i] = p < L ? krow[p * kst + i] : 0.0f;
   }
-  if (tid < C) sB[tid] = io.beta[(tok0 + tid) * io.H_v + h];
+  if (tid < C) sB[tid] = tid < L ? io.beta[(tok0 + tid) * io.H_v + h] : 0.0f;
   if (tid == 0) {
     float acc = 0.0f;
     for (int p = 0; p < C; ++p) {
-      acc = acc + io.g[(tok0 + p) * io.H_v + h];
+      acc = acc + (p < L ? io.g[(tok0 + p) * io.H_v + h] : 0.0f);
       sG[p] = acc;
     }
   }
@@ -222,8 +240,9 @@ __global__ __launch_bounds__(256) void k_wy(ChunkIO io) {
     const int j = isW ? tid : tid - D;
     float* out = (isW ? io.W : io.U) + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
     for (int p = 0; p < C; ++p) {
-      float x = isW ? sBG[p] * sK[p][j]
-                    : sB[p] * ldin(v + (tok0 + p) * io.H_v * D + static_cast<int64_t>(h) * D + j);
+      const float vx = p < L ? ldin(v + (tok0 + p) * io.H_v * D + static_cast<int64_t>(h) * D + j)
+                             : 0.0f;
+      float x = isW ? sBG[p] * sK[p][j] : sB[p] * vx;
       for (int r = 0; r < p; ++r) x = fmaf(-sA[p][r], sY[r][tid], x);
       sY[p][tid] = x;
       out[static_cast<int64_t>(p) * D + j] = x;
@@ -254,6 +273,7 @@ struct ScanIO {
   const float* h0;       // nullable
   float* states;         // prefill chunk-start states
   float* hT;             // nullable
+  float* Dl;             // kAll: Delta of every chunk [slot][H_v][C][D]
   // cache (nullable in prefill)
   float* S_run;
   float* S_chunk;
@@ -263,8 +283,9 @@ struct ScanIO {
   int64_t max_state_slot, max_full_slot;
 };
 
-template <int D, int C, int TILE, bool RESYNC>
+template <int D, int C, int TILE, int MODE>
 __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
+  constexpr bool RESYNC = MODE == kResync;
   constexpr int NT = 256;
   constexpr int NTILE = D / TILE;
   __shared__ float sS[TILE][D + 1];
@@ -282,7 +303,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
   const int64_t DD = static_cast<int64_t>(D) * D;
   const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
 
-  int64_t tok0 = 0, nfull = 1, L = 0, slot0 = 0, fslot0 = 0;
+  int64_t tok0 = 0, nsteps = 1, L = 0, slot0 = 0, fslot0 = 0, nchunks = 0;
   if (RESYNC) {
     if (io.pos[nh] != 0) return;
     fslot0 = n;
@@ -290,10 +311,11 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
     tok0 = io.cu[n];
     L = static_cast<int64_t>(io.cu[n + 1]) - tok0;
     if (L < 0 || tok0 < 0 || tok0 + L > io.T) return;
-    nfull = L / C;
+    nchunks = (L + C - 1) / C;
+    nsteps = MODE == kAll ? nchunks : L / C;
     slot0 = io.cu_chunks[n];
-    fslot0 = io.cu_full[n];
-    if (slot0 + (L + C - 1) / C > io.max_state_slot || fslot0 + nfull > io.max_full_slot) return;
+    fslot0 = MODE == kAll ? slot0 : io.cu_full[n];
+    if (slot0 + nchunks > io.max_state_slot || fslot0 + nsteps > io.max_full_slot) return;
   }
 
   // load the starting state tile: S_ji = stored[i][j]
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
   }
   __syncthreads();
 
-  for (int64_t c = 0; c < nfull; ++c) {
+  for (int64_t c = 0; c < nsteps; ++c) {
     if (!RESYNC) {  // chunk-start state of chunk c
       float* dst = io.states + ((slot0 + c) * io.H_v + h) * DD;
       for (int e = tid; e < TILE * D; e += NT) {
@@ -319,10 +341,11 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
     const int64_t ktok0 = RESYNC ? static_cast<int64_t>(n) * C : tok0 + c * C;
     int64_t kst;
     const float* krow = key_rows<D, RESYNC>(io.khat, io.T, io.H_qk, hq, ktok0, kst);
+    const int64_t rows = RESYNC ? C : (L - c * C < C ? L - c * C : C);  // < C: padded tail
     for (int e = tid; e < C * D; e += NT) {
       const int p = e / D, i = e % D;
       sW[p][i] = Wc[e];
-      sK[p][i] = krow[p * kst + i];
+      sK[p][i] = p < rows ? krow[p * kst + i] : 0.0f;
     }
     if (tid < C) sG[tid] = Gc[tid];
     __syncthreads();
@@ -333,6 +356,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
 #pragma unroll 8
       for (int i = 0; i < D; ++i) acc = fmaf(sW[p][i], sS[jj][i], acc);
       const float delta = Uc[static_cast<int64_t>(p) * D + j0 + jj] - acc;
+      if (MODE == kAll) io.Dl[((fs * io.H_v + h) * C + p) * static_cast<int64_t>(D) + j0 + jj] = delta;
       sD[p][jj] = delta * expf(glast - sG[p]);
     }
     __syncthreads();
@@ -359,12 +383,13 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
     return;
   }
   const bool tail = (L % C) != 0;
+  if (MODE == kAll && tail) return;  // the tail's start state was stored in the loop
   for (int e = tid; e < TILE * D; e += NT) {
     const int i = e / TILE, jj = e % TILE;
     const int64_t off = static_cast<int64_t>(i) * D + j0 + jj;
     const float x = sS[jj][i];
     if (tail) {
-      io.states[((slot0 + nfull) * io.H_v + h) * DD + off] = x;  // tail chunk start
+      io.states[((slot0 + nsteps) * io.H_v + h) * DD + off] = x;  // tail chunk start
       if (io.S_chunk) io.S_chunk[nh * DD + off] = x;
     } else {
       if (io.hT) io.hT[nh * DD + off] = x;
@@ -717,7 +742,7 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     io.W = W; io.U = U; io.G = Gs;
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_slot = L.full_slots;
     Timed t_("k_wy", st);
-    hipLaunchKernelGGL((k_wy<D, C, TIn, false>), dim3(static_cast<unsigned>(cnt.full), s->H_v),
+    hipLaunchKernelGGL((k_wy<D, C, TIn, kFull>), dim3(static_cast<unsigned>(cnt.full), s->H_v),
                        dim3(256), 0, st, io);
   }
   {
@@ -731,7 +756,7 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     const int64_t blocks = static_cast<int64_t>(N) * s->H_v * (D / TILE);
     if (blocks > 0) {
       Timed t_("k_scan", st);
-      hipLaunchKernelGGL((k_scan<D, C, TILE, false>), dim3(static_cast<unsigned>(blocks)),
+      hipLaunchKernelGGL((k_scan<D, C, TILE, kFull>), dim3(static_cast<unsigned>(blocks)),
                          dim3(256), 0, st, io);
     }
   }
@@ -776,7 +801,7 @@ int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const v
     ci.T = static_cast<int64_t>(N) * C; ci.max_slot = N;
     {
       Timed t_("k_wy_resync", st);
-      hipLaunchKernelGGL((k_wy<D, C, TIn, true>), dim3(N, s->H_v), dim3(256), 0, st, ci);
+      hipLaunchKernelGGL((k_wy<D, C, TIn, kResync>), dim3(N, s->H_v), dim3(256), 0, st, ci);
     }
     ScanIO si{};
     si.khat = cache->kbuf; si.W = W; si.U = U; si.G = Gs;
@@ -784,7 +809,7 @@ int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const v
     si.N = N; si.H_qk = s->H_qk; si.H_v = s->H_v; si.max_full_slot = N;
     constexpr int TILE = scan_tile<D>();
     Timed t_("k_scan_resync", st);
-    hipLaunchKernelGGL((k_scan<D, C, TILE, true>),
+    hipLaunchKernelGGL((k_scan<D, C, TILE, kResync>),
                        dim3(static_cast<unsigned>(static_cast<int64_t>(N) * s->H_v * (D / TILE))),
                        dim3(256), 0, st, si);
   }
