@@ -26,6 +26,7 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3
 
 PREFILL = dict(N=4, T=2048, H_qk=16, H_v=32, d=128, C=64)
 DECODE = dict(N=64, P=4096, S=256, H_qk=16, H_v=32, d=128, C=64)
+TRAIN = dict(N=8, T=4096, H_qk=16, H_v=32, d=128, C=64)
 
 
 def r_flops_per_token_head(d):
@@ -58,6 +59,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--train-steps", type=int, default=5)
     return ap.parse_args()
 
 
@@ -184,8 +187,44 @@ def bench_decode(args, B, torch, make_inputs):
                          "d128 C64 bf16")
 
 
+def bench_fwd_bwd(args, B, torch, make_inputs):
+    c = TRAIN
+    dev = "cuda"
+    inp = make_inputs([c["T"]] * c["N"], c["H_qk"], c["H_v"], c["d"], "bf16", seed=3,
+                      h0="normal", with_do=True, device=dev)
+    shape = B.make_shape(c["H_qk"], c["H_v"], c["d"], c["C"], torch.bfloat16)
+    T = inp["T"]
+    ws = torch.empty(B.workspace_bytes(shape, c["N"], T, B.OP_FWD_BWD), dtype=torch.uint8,
+                     device=dev)
+    cu = inp["cu_seqlens"].to(dev)
+
+    def step():
+        B.gdn_fwd_bwd(shape, inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], cu, inp["do"],
+                      h0=inp["h0"], ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    B.profile_read("")
+    B.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.train_steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.profile_enable(False)
+    per = {}
+    for name in ["k_prep", "k_wy", "k_scan", "k_rec", "k_bwd_prep", "k_bwd_scan", "k_bwd_mm",
+                 "k_bwd_chunk", "k_bwd_qk"]:
+        ms, n = B.profile_read(name)
+        per[name] = round(1e3 * ms / max(n, 1), 1)
+    ms_step = 1e3 * (t1 - t0) / args.train_steps
+    return dict(ms_per_step=round(ms_step, 3), tokens_per_s=round(T / (ms_step * 1e-3), 1),
+                per_kernel_us=per,
+                workload="fwd+bwd B8 T4096, 16 q/k / 32 v heads, d128 C64 bf16, dO ~ N(0,1)")
+
+
 def cpu_baseline(inp):
-    """The fp64 oracle on sequences 0 and 1 of the prefill batch (all heads),
+    """The fp64 oracle on the whole prefill batch (4 sequences, all heads),
     single process, BLAS limited to one thread."""
     import numpy as np
     try:
@@ -194,7 +233,7 @@ def cpu_baseline(inp):
         threadpool_limits = None
     from oracle import recurrent_fwd
     from linear_attention_rnn_gated_amd.inputs import to_numpy_f64
-    seqs = [0, 1]
+    seqs = list(range(int(inp["N"])))
     cu = inp["cu_seqlens"].cpu()
     f = lambda t: to_numpy_f64(t.cpu()) if t is not None else None  # noqa: E731
     args = (f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["beta"]), f(inp["g"]), cu.numpy())
@@ -209,7 +248,7 @@ def cpu_baseline(inp):
     dt = time.perf_counter() - t0
     ntok = int(sum(int(cu[n + 1] - cu[n]) for n in seqs))
     return dict(value=round(ntok / dt, 2), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"sequences 0-1 of the prefill batch ({ntok} tokens, all 32 v heads), "
+                sample=f"the whole prefill batch ({ntok} tokens, all 32 v heads), "
                        f"fp64 numpy token recurrence, 1 thread, {dt:.1f} s")
 
 
@@ -249,6 +288,8 @@ def main():
     if not args.no_decode:
         dc = bench_decode(args, B, torch, make_inputs)
         line["decode"] = dc
+    if not args.no_train:
+        line["fwd_bwd"] = bench_fwd_bwd(args, B, torch, make_inputs)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(pf["inputs"])
     print(json.dumps(line), flush=True)

@@ -631,6 +631,485 @@ __global__ __launch_bounds__(D < 64 ? 64 : D) void k_decode(DecIO io) {
 }
 
 // ---------------------------------------------------------------------------
+// Backward (gdn_fwd_bwd).  The gradient of the layer as a function, computed
+// through its chunk form (the forward's chunk factors W, U, G, its
+// chunk-start states S and Delta = U - W S^T are kept from the forward).  Per
+// chunk of L rows (padded to C with zero rows), P = (Q K^T) . Gam (r <= p),
+// Gam_pr = exp(G_p - G_r), gam_p = exp(G_p), lam_p = exp(G_last - G_p), and
+// dS' the gradient of the state at the chunk's end:
+//   dDelta = P^T dO + diag(lam) K dS'^T
+//   dS     = gam_last dS' + sum_p gam_p dO_p q_p^T - sum_p dDelta_p W_p^T
+// (the reverse scan over chunks), then per chunk the gradients of q, k, v,
+// beta and g through O, the state update and the WY solve.  No atomics; every
+// sum has a fixed order, so the result is reproducible bit for bit.
+struct BwdIO {
+  const float* qk;        // prep layout [H_qk][T][2][D] (k-hat, q-hat)
+  const void* q;          // raw inputs (norm backward)
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  const float* dO;        // [T][H_v][D]
+  const float* dhT;       // nullable [N][H_v][D][D]
+  const int32_t* cu;
+  const int32_t* cu_chunks;
+  const float* W;         // [slot][H_v][C][D]
+  const float* U;
+  const float* G;         // [slot][H_v][C]
+  const float* states;    // [slot][H_v][D][D] chunk-start states (stored layout)
+  const float* Dl;        // [slot][H_v][C][D] Delta
+  float* E;               // [slot][H_v][C][D] P^T dO
+  float* dstates;         // [slot][H_v][D][D] gradient of each chunk's end state
+  float* dD;              // [slot][H_v][C][D] dDelta, then dX_u
+  float* SdO;             // [slot][H_v][C][D] S^T dO_p
+  float* DsD;             // [slot][H_v][C][D] dS'^T Delta_p
+  float* SdD;             // [slot][H_v][C][D] S^T dDelta_p, then dX_w
+  float* dqv;             // [T][H_v][D] per value head
+  float* dkv;             // [T][H_v][D]
+  float* dv;              // [T][H_v][D]
+  float* dbeta;           // [T][H_v]
+  float* dg;              // [T][H_v]
+  float* dq;              // [T][H_qk][D]
+  float* dk;
+  float* dh0;             // [N][H_v][D][D]
+  int N, H_qk, H_v, l2;
+  float scale;
+  int64_t T, max_state_slot;
+};
+
+// Chunk item of a backward kernel: slot = blockIdx.x over every chunk.
+template <int C>
+__device__ __forceinline__ bool bwd_item(const BwdIO& io, int64_t& slot, int64_t& tok0, int& L) {
+  slot = blockIdx.x;
+  if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return false;
+  const int n = find_seq(io.cu_chunks, io.N, slot);
+  tok0 = static_cast<int64_t>(io.cu[n]) + (slot - io.cu_chunks[n]) * C;
+  const int64_t end = io.cu[n + 1];
+  if (tok0 < 0 || end > io.T || tok0 >= end) return false;
+  L = static_cast<int>(end - tok0 < C ? end - tok0 : C);
+  return true;
+}
+
+// E = P^T dO for one chunk and value head.
+template <int D, int C>
+__global__ __launch_bounds__(256) void k_bwd_prep(BwdIO io) {
+  constexpr int NT = 256;
+  __shared__ float sQ[C][D + 1];
+  __shared__ float sK[C][D + 1];
+  __shared__ float sP[C][C + 1];
+  __shared__ float sG[C];
+  int64_t slot, tok0;
+  int L;
+  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  const int tid = threadIdx.x, h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
+  for (int e = tid; e < C * D; e += NT) {
+    const int p = e / D, i = e % D;
+    sK[p][i] = p < L ? kq[p * 2 * D + i] : 0.0f;
+    sQ[p][i] = p < L ? kq[p * 2 * D + D + i] : 0.0f;
+  }
+  if (tid < C) sG[tid] = io.G[(slot * io.H_v + h) * C + tid];
+  __syncthreads();
+  for (int e = tid; e < C * C; e += NT) {
+    const int p = e / C, r = e % C;
+    float x = 0.0f;
+    if (r <= p && p < L) {
+      float d = 0.0f;
+      for (int i = 0; i < D; ++i) d = fmaf(sQ[p][i], sK[r][i], d);
+      x = d * expf(sG[p] - sG[r]);
+    }
+    sP[p][r] = x;
+  }
+  __syncthreads();
+  const float* dO = io.dO + (tok0 * io.H_v + h) * D;
+  float* E = io.E + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
+  for (int e = tid; e < C * D; e += NT) {
+    const int r = e / D, j = e % D;
+    float acc = 0.0f;
+    for (int p = r; p < L; ++p) acc = fmaf(sP[p][r], dO[static_cast<int64_t>(p) * io.H_v * D + j], acc);
+    E[e] = acc;
+  }
+}
+
+// Reverse scan of the state gradient over the chunks of a sequence, for a
+// tile of TILE rows (d_v indices) -- rows are independent here too.
+template <int D, int C, int TILE>
+__global__ __launch_bounds__(256) void k_bwd_scan(BwdIO io) {
+  constexpr int NT = 256;
+  constexpr int NTILE = D / TILE;
+  __shared__ float sS[TILE][D + 1];  // dS' rows: sS[jj][i] = stored[i][j0 + jj]
+  __shared__ float sK[C][D];
+  __shared__ float sQ[C][D];
+  __shared__ float sW[C][D];
+  __shared__ float sDD[C][TILE + 1];
+  __shared__ float sO[C][TILE + 1];
+  __shared__ float sG[C];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x % NTILE;
+  const int h = (blockIdx.x / NTILE) % io.H_v;
+  const int n = blockIdx.x / (NTILE * io.H_v);
+  if (n >= io.N) return;
+  const int hq = h / (io.H_v / io.H_qk);
+  const int j0 = tile * TILE;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
+  const int64_t s0 = io.cu[n];
+  const int64_t Lseq = static_cast<int64_t>(io.cu[n + 1]) - s0;
+  if (Lseq < 0 || s0 < 0 || s0 + Lseq > io.T) return;
+  const int64_t nchunks = (Lseq + C - 1) / C;
+  const int64_t slot0 = io.cu_chunks[n];
+  if (slot0 + nchunks > io.max_state_slot) return;
+
+  for (int e = tid; e < TILE * D; e += NT) {
+    const int i = e / TILE, jj = e % TILE;
+    sS[jj][i] = io.dhT ? io.dhT[nh * DD + static_cast<int64_t>(i) * D + j0 + jj] : 0.0f;
+  }
+  __syncthreads();
+  for (int64_t c = nchunks - 1; c >= 0; --c) {
+    const int64_t slot = slot0 + c;
+    const int64_t tok0 = s0 + c * C;
+    const int rows = static_cast<int>(Lseq - c * C < C ? Lseq - c * C : C);
+    float* dst = io.dstates + (slot * io.H_v + h) * DD;
+    for (int e = tid; e < TILE * D; e += NT) {
+      const int i = e / TILE, jj = e % TILE;
+      dst[static_cast<int64_t>(i) * D + j0 + jj] = sS[jj][i];
+    }
+    const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
+    const float* Wc = io.W + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
+    for (int e = tid; e < C * D; e += NT) {
+      const int p = e / D, i = e % D;
+      sK[p][i] = p < rows ? kq[p * 2 * D + i] : 0.0f;
+      sQ[p][i] = p < rows ? kq[p * 2 * D + D + i] : 0.0f;
+      sW[p][i] = Wc[e];
+    }
+    if (tid < C) sG[tid] = io.G[(slot * io.H_v + h) * C + tid];
+    __syncthreads();
+    for (int e = tid; e < C * TILE; e += NT) {
+      const int p = e / TILE, jj = e % TILE;
+      sO[p][jj] = p < rows ? expf(sG[p]) * io.dO[((tok0 + p) * io.H_v + h) * D + j0 + jj] : 0.0f;
+    }
+    const float glast = sG[C - 1];
+    const float* Ec = io.E + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
+    float* dDc = io.dD + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
+    for (int e = tid; e < C * TILE; e += NT) {
+      const int p = e / TILE, jj = e % TILE;
+      float d = 0.0f;
+      for (int i = 0; i < D; ++i) d = fmaf(sK[p][i], sS[jj][i], d);
+      const float x = Ec[static_cast<int64_t>(p) * D + j0 + jj] + expf(glast - sG[p]) * d;
+      sDD[p][jj] = x;
+      dDc[static_cast<int64_t>(p) * D + j0 + jj] = x;
+    }
+    __syncthreads();
+    const float gl = expf(glast);
+    for (int e = tid; e < TILE * D; e += NT) {
+      const int jj = e / D, i = e % D;
+      float acc = gl * sS[jj][i];
+      for (int p = 0; p < C; ++p) acc = fmaf(sO[p][jj], sQ[p][i], acc);
+      for (int p = 0; p < C; ++p) acc = fmaf(-sDD[p][jj], sW[p][i], acc);
+      sS[jj][i] = acc;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < TILE * D; e += NT) {
+    const int i = e / TILE, jj = e % TILE;
+    io.dh0[nh * DD + static_cast<int64_t>(i) * D + j0 + jj] = sS[jj][i];
+  }
+}
+
+// The three state products of a chunk: out_p[i] = sum_j X[i][j] Y_p[j] for
+// (X, Y) = (S, dO) -> SdO, (S, dDelta) -> SdD, (dS', Delta) -> DsD.
+template <int D, int C>
+__global__ __launch_bounds__(256) void k_bwd_mm(BwdIO io) {
+  constexpr int NT = 256;
+  __shared__ float sM[D][D + 1];
+  __shared__ float sY[C][D + 1];
+  int64_t slot, tok0;
+  int L;
+  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  const int tid = threadIdx.x, h = blockIdx.y;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const int64_t CD = static_cast<int64_t>(C) * D;
+  const int64_t sh = slot * io.H_v + h;
+  for (int prod = 0; prod < 3; ++prod) {
+    if (prod != 1) {
+      const float* X = (prod == 0 ? io.states : io.dstates) + sh * DD;
+      for (int e = tid; e < D * D; e += NT) sM[e / D][e % D] = X[e];
+    }
+    for (int e = tid; e < C * D; e += NT) {
+      const int p = e / D, j = e % D;
+      float y = 0.0f;
+      if (p < L) {
+        if (prod == 0) y = io.dO[((tok0 + p) * io.H_v + h) * D + j];
+        else if (prod == 1) y = io.dD[sh * CD + e];
+        else y = io.Dl[sh * CD + e];
+      }
+      sY[p][j] = y;
+    }
+    __syncthreads();
+    float* out = (prod == 0 ? io.SdO : prod == 1 ? io.SdD : io.DsD) + sh * CD;
+    for (int e = tid; e < C * D; e += NT) {
+      const int p = e / D, i = e % D;
+      float acc = 0.0f;
+      for (int j = 0; j < D; ++j) acc = fmaf(sM[i][j], sY[p][j], acc);
+      out[e] = acc;
+    }
+    __syncthreads();
+  }
+}
+
+// Per chunk and value head: gradients of q-hat, k-hat (per value head), v,
+// beta and g.
+template <int D, int C, typename TIn>
+__global__ __launch_bounds__(256) void k_bwd_chunk(BwdIO io) {
+  constexpr int NT = 256;
+  constexpr int CP = C + 1;
+  constexpr int DP = D + 1;
+  // LDS: K | Q QK Z (later reused as Y = [dX_w | dX_u]) | KK | A | dA | vectors
+  __shared__ float lds[C * DP + (C * DP + 2 * C * CP) + 3 * C * CP + 8 * C + 256];
+  float (*sK)[DP] = reinterpret_cast<float (*)[DP]>(lds);
+  float (*sQ)[DP] = reinterpret_cast<float (*)[DP]>(lds + C * DP);
+  float (*sQK)[CP] = reinterpret_cast<float (*)[CP]>(lds + 2 * C * DP);
+  float (*sZ)[CP] = reinterpret_cast<float (*)[CP]>(lds + 2 * C * DP + C * CP);
+  float (*sY)[2 * D] = reinterpret_cast<float (*)[2 * D]>(lds + C * DP);  // after Q, QK, Z die
+  float (*sKK)[CP] = reinterpret_cast<float (*)[CP]>(lds + 2 * C * DP + 2 * C * CP);
+  float (*sA)[CP] = reinterpret_cast<float (*)[CP]>(lds + 2 * C * DP + 3 * C * CP);
+  float (*sdA)[CP] = reinterpret_cast<float (*)[CP]>(lds + 2 * C * DP + 4 * C * CP);
+  float* vec = lds + 2 * C * DP + 5 * C * CP;
+  float* sG = vec;
+  float* sB = vec + C;
+  float* sGam = vec + 2 * C;
+  float* sLam = vec + 3 * C;
+  float* sdG = vec + 4 * C;
+  float* sdB = vec + 5 * C;
+  float* red = vec + 8 * C;  // 256 partial sums
+  static_assert(C * DP + 2 * C * CP >= C * 2 * D, "Y must fit in the Q/QK/Z region");
+
+  int64_t slot, tok0;
+  int L;
+  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  const int tid = threadIdx.x, h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const int64_t CD = static_cast<int64_t>(C) * D;
+  const int64_t sh = slot * io.H_v + h;
+  const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
+  for (int e = tid; e < C * D; e += NT) {
+    const int p = e / D, i = e % D;
+    sK[p][i] = p < L ? kq[p * 2 * D + i] : 0.0f;
+    sQ[p][i] = p < L ? kq[p * 2 * D + D + i] : 0.0f;
+  }
+  if (tid < C) {
+    sG[tid] = io.G[sh * C + tid];
+    sB[tid] = tid < L ? io.beta[(tok0 + tid) * io.H_v + h] : 0.0f;
+  }
+  // <S, dS'> (fixed-order block reduction)
+  {
+    const float* M = io.states + sh * DD;
+    const float* dM = io.dstates + sh * DD;
+    float part = 0.0f;
+    for (int e = tid; e < D * D; e += NT) part = fmaf(M[e], dM[e], part);
+    red[tid] = part;
+  }
+  __syncthreads();
+  const float glast = sG[C - 1];
+  if (tid < C) {
+    sGam[tid] = expf(sG[tid]);
+    sLam[tid] = expf(glast - sG[tid]);
+  }
+  for (int w = NT / 2; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] = red[tid] + red[tid + w];
+    __syncthreads();
+  }
+  const float MdM = red[0];
+  const float* dO = io.dO + (tok0 * io.H_v + h) * D;
+  const float* Dl = io.Dl + sh * CD;
+  for (int e = tid; e < C * C; e += NT) {
+    const int p = e / C, r = e % C;
+    float qk = 0.0f, kk = 0.0f, a = 0.0f, z = 0.0f;
+    if (r <= p && p < L) {
+      const float gam = expf(sG[p] - sG[r]);
+      float dqk = 0.0f, dkk = 0.0f, dp = 0.0f;
+      for (int i = 0; i < D; ++i) {
+        dqk = fmaf(sQ[p][i], sK[r][i], dqk);
+        dkk = fmaf(sK[p][i], sK[r][i], dkk);
+        dp = fmaf(dO[static_cast<int64_t>(p) * io.H_v * D + i], Dl[static_cast<int64_t>(r) * D + i], dp);
+      }
+      qk = dqk;
+      z = dp * gam;
+      if (r < p) {
+        kk = dkk;
+        a = sB[p] * (dkk * gam);
+      }
+    }
+    sQK[p][r] = qk;
+    sZ[p][r] = z;
+    sKK[p][r] = kk;
+    sA[p][r] = a;
+  }
+  __syncthreads();
+  const float* SdO = io.SdO + sh * CD;
+  const float* DsD = io.DsD + sh * CD;
+  // dq-hat and the Q / DsD parts of dk-hat
+  for (int e = tid; e < C * D; e += NT) {
+    const int p = e / D, i = e % D;
+    if (p >= L) continue;
+    float aq = sGam[p] * SdO[e];
+    for (int r = 0; r <= p; ++r) aq = fmaf(sZ[p][r], sK[r][i], aq);
+    io.dqv[((tok0 + p) * io.H_v + h) * D + i] = aq;
+    float ak = sLam[p] * DsD[e];
+    for (int q = p; q < L; ++q) ak = fmaf(sZ[q][p], sQ[q][i], ak);
+    io.dkv[((tok0 + p) * io.H_v + h) * D + i] = ak;
+  }
+  // dG terms from O and from the state update (needs Q, QK, Z, DsD, SdO)
+  if (tid < C) {
+    const int p = tid;
+    float x = 0.0f;
+    if (p < L) {
+      float qs = 0.0f, kd = 0.0f;
+      for (int i = 0; i < D; ++i) {
+        qs = fmaf(sQ[p][i], SdO[static_cast<int64_t>(p) * D + i], qs);
+        kd = fmaf(sK[p][i], DsD[static_cast<int64_t>(p) * D + i], kd);
+      }
+      x = sGam[p] * qs - sLam[p] * kd;
+      for (int r = 0; r < p; ++r) x = fmaf(sZ[p][r], sQK[p][r], x);
+      for (int q = p + 1; q < L; ++q) x = fmaf(-sZ[q][p], sQK[q][p], x);
+      if (p == L - 1) {
+        float s = sGam[C - 1] * MdM;
+        for (int q = 0; q < L; ++q) {
+          float kd2 = 0.0f;
+          for (int i = 0; i < D; ++i)
+            kd2 = fmaf(sK[q][i], DsD[static_cast<int64_t>(q) * D + i], kd2);
+          s = fmaf(sLam[q], kd2, s);
+        }
+        x = x + s;
+      }
+    }
+    sdG[p] = x;
+  }
+  __syncthreads();  // Q, QK, Z are dead from here; their space holds Y
+  // back substitution (I + A)^T Y = [dW | dU], dW = -SdD, dU = dDelta;
+  // thread t owns column t (t < D: dX_w, else dX_u)
+  if (tid < 2 * D) {
+    const int t = tid;
+    const bool isW = t < D;
+    const int col = isW ? t : t - D;
+    const float* rhs = isW ? io.SdD + sh * CD : io.dD + sh * CD;
+    for (int p = C - 1; p >= 0; --p) {
+      float y = 0.0f;
+      if (p < L) {
+        y = isW ? -rhs[static_cast<int64_t>(p) * D + col] : rhs[static_cast<int64_t>(p) * D + col];
+        for (int r = p + 1; r < L; ++r) y = fmaf(-sA[r][p], sY[r][t], y);
+      }
+      sY[p][t] = y;
+    }
+  }
+  __syncthreads();
+  // dA_pr = -(dX_w,p . W_r + dX_u,p . U_r), r < p
+  const float* Wc = io.W + sh * CD;
+  const float* Uc = io.U + sh * CD;
+  for (int e = tid; e < C * C; e += NT) {
+    const int p = e / C, r = e % C;
+    float x = 0.0f;
+    if (r < p && p < L) {
+      float a = 0.0f;
+      for (int i = 0; i < D; ++i) a = fmaf(sY[p][i], Wc[static_cast<int64_t>(r) * D + i], a);
+      for (int i = 0; i < D; ++i) a = fmaf(sY[p][D + i], Uc[static_cast<int64_t>(r) * D + i], a);
+      x = -a;
+    }
+    sdA[p][r] = x;
+  }
+  __syncthreads();
+  // dbeta and the remaining dG terms
+  if (tid < C) {
+    const int p = tid;
+    float db = 0.0f, dgp = sdG[p];
+    if (p < L) {
+      const TIn* vin = static_cast<const TIn*>(io.v) + ((tok0 + p) * io.H_v + h) * D;
+      float xk = 0.0f, uv = 0.0f;
+      for (int i = 0; i < D; ++i) {
+        xk = fmaf(sY[p][i], sK[p][i], xk);
+        uv = fmaf(sY[p][D + i], ldin(vin + i), uv);
+      }
+      db = sGam[p] * xk + uv;
+      dgp = fmaf(sB[p] * sGam[p], xk, dgp);
+      for (int r = 0; r < p; ++r) {
+        db = fmaf(sdA[p][r], sKK[p][r] * expf(sG[p] - sG[r]), db);
+        dgp = fmaf(sdA[p][r], sA[p][r], dgp);
+      }
+      for (int q = p + 1; q < L; ++q) dgp = fmaf(-sdA[q][p], sA[q][p], dgp);
+    }
+    sdB[p] = db;
+    sdG[p] = dgp;
+  }
+  __syncthreads();
+  // dA -> gradient of k_p . k_r  (E2_pr = dA_pr beta_p Gam_pr), in place
+  for (int e = tid; e < C * C; e += NT) {
+    const int p = e / C, r = e % C;
+    if (r < p && p < L) sdA[p][r] = sdA[p][r] * sB[p] * expf(sG[p] - sG[r]);
+  }
+  __syncthreads();
+  for (int e = tid; e < C * D; e += NT) {
+    const int p = e / D, i = e % D;
+    if (p >= L) continue;
+    const int64_t o = ((tok0 + p) * io.H_v + h) * D + i;
+    float ak = io.dkv[o];
+    ak = fmaf(sB[p] * sGam[p], sY[p][i], ak);
+    for (int r = 0; r < p; ++r) ak = fmaf(sdA[p][r], sK[r][i], ak);
+    for (int q = p + 1; q < L; ++q) ak = fmaf(sdA[q][p], sK[q][i], ak);
+    io.dkv[o] = ak;
+    io.dv[o] = sB[p] * sY[p][D + i];
+  }
+  if (tid == 0) {  // dg = reverse running sum of dG within the chunk
+    float acc = 0.0f;
+    for (int p = L - 1; p >= 0; --p) {
+      acc = acc + sdG[p];
+      io.dg[(tok0 + p) * io.H_v + h] = acc;
+      io.dbeta[(tok0 + p) * io.H_v + h] = sdB[p];
+    }
+  }
+}
+
+// Sum over the value heads of each group (ascending head order), then the L2
+// norm backward: dx = s r (dxh - n (n . dxh)), n = x r, r = (sum x^2 + eps)^-1/2.
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void k_bwd_qk(BwdIO io) {
+  const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // t*H_qk + hq
+  if (vec >= io.T * io.H_qk) return;
+  const int64_t t = vec / io.H_qk;
+  const int hq = static_cast<int>(vec - t * io.H_qk);
+  const int G = io.H_v / io.H_qk;
+  const int l = threadIdx.x & 63;
+  for (int which = 0; which < 2; ++which) {  // 0: q, 1: k
+    const float* src = which == 0 ? io.dqv : io.dkv;
+    float g0 = 0.0f, g1 = 0.0f;
+    for (int gg = 0; gg < G; ++gg) {
+      const float* row = src + (t * io.H_v + static_cast<int64_t>(hq) * G + gg) * D;
+      if (l < D) g0 = g0 + row[l];
+      if (D > 64) g1 = g1 + row[l + 64];
+    }
+    const float mul = which == 0 ? io.scale : 1.0f;
+    float* dst = (which == 0 ? io.dq : io.dk) + vec * D;
+    if (io.l2) {
+      const TIn* x = static_cast<const TIn*>(which == 0 ? io.q : io.k) + vec * D;
+      const float x0 = l < D ? ldin(x + l) : 0.0f;
+      const float x1 = D > 64 ? ldin(x + l + 64) : 0.0f;
+      float ss = fmaf(x1, x1, x0 * x0);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      const float r = 1.0f / sqrtf(ss + gdn::kNormEps);
+      const float n0 = x0 * r, n1 = x1 * r;
+      float dot = fmaf(n1, g1, n0 * g0);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+      if (l < D) dst[l] = mul * r * (g0 - n0 * dot);
+      if (D > 64) dst[l + 64] = mul * r * (g1 - n1 * dot);
+    } else {
+      if (l < D) dst[l] = mul * g0;
+      if (D > 64) dst[l + 64] = mul * g1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Cache init: S_run = S_chunk = h0 (or 0), pos = 0.  Plain fill kernel (no
 // memset nodes, so the call is safe to capture in a graph).
 __global__ void k_cache_init(const float* __restrict__ h0, float* __restrict__ S_run,
@@ -816,6 +1295,105 @@ int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const v
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+template <int D, int C, typename TIn>
+int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const gdn::Layout& L,
+                   const int32_t* cu, const void* q, const void* k, const void* v,
+                   const float* beta, const float* g, const float* h0, const float* dO,
+                   const float* dhT, float* o, float* hT, float* dq, float* dk, float* dv,
+                   float* dbeta, float* dg, float* dh0, char* ws, hipStream_t st) {
+  int32_t* cu_chunks = reinterpret_cast<int32_t*>(ws + L.cu_chunks);
+  int32_t* cu_full = reinterpret_cast<int32_t*>(ws + L.cu_full);
+  float* qk = reinterpret_cast<float*>(ws + L.qk);
+  float* W = reinterpret_cast<float*>(ws + L.W);
+  float* U = reinterpret_cast<float*>(ws + L.U);
+  float* Gs = reinterpret_cast<float*>(ws + L.G);
+  float* states = reinterpret_cast<float*>(ws + L.states);
+  float* Dl = reinterpret_cast<float*>(ws + L.Dl);
+  {
+    Timed t_("k_plan", st);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, st, cu, N, C, cu_chunks, cu_full);
+  }
+  const int64_t nvec = cnt.T * s->H_qk;
+  if (nvec > 0) {
+    Timed t_("k_prep", st);
+    hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)), dim3(256), 0,
+                       st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
+                       s->H_qk, s->scale, s->qk_l2norm);
+  }
+  if (cnt.chunks > 0) {
+    ChunkIO io{};
+    io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_chunks;
+    io.W = W; io.U = U; io.G = Gs;
+    io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_slot = L.state_slots;
+    Timed t_("k_wy", st);
+    hipLaunchKernelGGL((k_wy<D, C, TIn, kAll>), dim3(static_cast<unsigned>(cnt.chunks), s->H_v),
+                       dim3(256), 0, st, io);
+  }
+  constexpr int TILE = scan_tile<D>();
+  const int64_t sblocks = static_cast<int64_t>(N) * s->H_v * (D / TILE);
+  if (sblocks > 0) {
+    ScanIO io{};
+    io.khat = qk; io.W = W; io.U = U; io.G = Gs; io.cu = cu; io.cu_chunks = cu_chunks;
+    io.cu_full = cu_full; io.h0 = h0; io.states = states; io.hT = hT; io.Dl = Dl;
+    io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
+    io.max_state_slot = L.state_slots; io.max_full_slot = L.state_slots;
+    Timed t_("k_scan", st);
+    hipLaunchKernelGGL((k_scan<D, C, TILE, kAll>), dim3(static_cast<unsigned>(sblocks)),
+                       dim3(256), 0, st, io);
+  }
+  if (cnt.chunks > 0) {
+    RecIO io{};
+    io.qk = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu;
+    io.cu_chunks = cu_chunks; io.states = states; io.o = o; io.hT = hT;
+    io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_state_slot = L.state_slots;
+    Timed t_("k_rec", st);
+    hipLaunchKernelGGL((k_rec<D, C, TIn>),
+                       dim3(static_cast<unsigned>(cnt.chunks), s->H_v, (D + 63) / 64), dim3(64), 0,
+                       st, io);
+  }
+  // backward
+  BwdIO b{};
+  b.qk = qk; b.q = q; b.k = k; b.v = v; b.beta = beta; b.g = g; b.dO = dO; b.dhT = dhT;
+  b.cu = cu; b.cu_chunks = cu_chunks; b.W = W; b.U = U; b.G = Gs; b.states = states; b.Dl = Dl;
+  b.E = reinterpret_cast<float*>(ws + L.E);
+  b.dstates = reinterpret_cast<float*>(ws + L.dstates);
+  b.dD = reinterpret_cast<float*>(ws + L.dD);
+  b.SdO = reinterpret_cast<float*>(ws + L.SdO);
+  b.DsD = reinterpret_cast<float*>(ws + L.DsD);
+  b.SdD = reinterpret_cast<float*>(ws + L.SdD);
+  b.dqv = reinterpret_cast<float*>(ws + L.dqv);
+  b.dkv = reinterpret_cast<float*>(ws + L.dkv);
+  b.dv = dv; b.dbeta = dbeta; b.dg = dg; b.dq = dq; b.dk = dk; b.dh0 = dh0;
+  b.N = N; b.H_qk = s->H_qk; b.H_v = s->H_v; b.l2 = s->qk_l2norm; b.scale = s->scale;
+  b.T = cnt.T; b.max_state_slot = L.state_slots;
+  const dim3 cgrid(static_cast<unsigned>(cnt.chunks > 0 ? cnt.chunks : 1), s->H_v);
+  if (cnt.chunks > 0) {
+    Timed t_("k_bwd_prep", st);
+    hipLaunchKernelGGL((k_bwd_prep<D, C>), cgrid, dim3(256), 0, st, b);
+  }
+  if (sblocks > 0) {
+    Timed t_("k_bwd_scan", st);
+    hipLaunchKernelGGL((k_bwd_scan<D, C, TILE>), dim3(static_cast<unsigned>(sblocks)), dim3(256),
+                       0, st, b);
+  }
+  if (cnt.chunks > 0) {
+    {
+      Timed t_("k_bwd_mm", st);
+      hipLaunchKernelGGL((k_bwd_mm<D, C>), cgrid, dim3(256), 0, st, b);
+    }
+    {
+      Timed t_("k_bwd_chunk", st);
+      hipLaunchKernelGGL((k_bwd_chunk<D, C, TIn>), cgrid, dim3(256), 0, st, b);
+    }
+  }
+  if (nvec > 0) {
+    Timed t_("k_bwd_qk", st);
+    hipLaunchKernelGGL((k_bwd_qk<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)), dim3(256),
+                       0, st, b);
+  }
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 // Calls f.template operator()<D, C, TIn>() for the shape's compiled variant.
 template <typename F>
 int dispatch(const gdn_shape_t* s, F&& f) {
@@ -916,10 +1494,24 @@ int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seql
                 const float* beta, const float* g, const float* h0, const float* dO,
                 const float* dhT, float* o, float* hT, float* dq, float* dk, float* dv,
                 float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes, void* stream) {
-  (void)shape; (void)n_seqs; (void)cu_seqlens_dev; (void)cu_seqlens_host; (void)q; (void)k;
-  (void)v; (void)beta; (void)g; (void)h0; (void)dO; (void)dhT; (void)o; (void)hT; (void)dq;
-  (void)dk; (void)dv; (void)dbeta; (void)dg; (void)dh0; (void)ws; (void)ws_bytes; (void)stream;
-  return GDN_ERR_UNSUPPORTED;
+  int rc = gdn::check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host) return GDN_ERR_INVALID_ARG;
+  gdn::Counts cnt;
+  if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
+  if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o || !dO || !dq || !dk || !dv || !dbeta ||
+                    !dg))
+    return GDN_ERR_INVALID_ARG;
+  if (n_seqs > 0 && (!hT || !dh0)) return GDN_ERR_INVALID_ARG;
+  const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_FWD_BWD);
+  if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (n_seqs == 0) return GDN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  return dispatch(shape, [&]<int D, int C, typename TIn>() {
+    return launch_fwd_bwd<D, C, TIn>(shape, n_seqs, cnt, L, cu_seqlens_dev, q, k, v, beta, g, h0,
+                                     dO, dhT, o, hT, dq, dk, dv, dbeta, dg, dh0, w, st);
+  });
 }
 
 int gdn_profile_enable(int on) {

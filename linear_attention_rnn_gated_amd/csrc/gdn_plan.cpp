@@ -67,15 +67,22 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
   // one spare token row: the token step reads the next key one token past the
   // end of a chunk (the value is never used)
   L.qk = take(&cur, (T * Hq + 1) * 2 * d * f);
-  L.W = take(&cur, L.full_slots * Hv * C * d * f);
-  L.U = take(&cur, L.full_slots * Hv * C * d * f);
-  L.G = take(&cur, L.full_slots * Hv * C * f);
+  const int64_t wu_slots = op == GDN_OP_FWD_BWD ? L.state_slots : L.full_slots;
+  L.W = take(&cur, wu_slots * Hv * C * d * f);
+  L.U = take(&cur, wu_slots * Hv * C * d * f);
+  L.G = take(&cur, wu_slots * Hv * C * f);
   L.states = take(&cur, L.state_slots * Hv * d * d * f);
   if (op == GDN_OP_FWD_BWD) {
+    const size_t cd = L.state_slots * Hv * C * d * f;
+    L.Dl = take(&cur, cd);
+    L.E = take(&cur, cd);
     L.dstates = take(&cur, L.state_slots * Hv * d * d * f);
+    L.dD = take(&cur, cd);
+    L.SdO = take(&cur, cd);
+    L.DsD = take(&cur, cd);
+    L.SdD = take(&cur, cd);
     L.dqv = take(&cur, T * Hv * d * f);
     L.dkv = take(&cur, T * Hv * d * f);
-    L.dG = take(&cur, T * Hv * f);
   }
   L.total = cur;
   return L;

@@ -37,11 +37,16 @@ struct Layout {
   size_t U = 0;          // f32 [full_slots, H_v, C, d]
   size_t G = 0;          // f32 [full_slots, H_v, C]
   size_t states = 0;     // f32 [state_slots, H_v, d, d]  chunk-start states
-  // backward only
+  // trainer forward + backward only (W, U, G then use chunk slots)
+  size_t Dl = 0;         // f32 [state_slots, H_v, C, d]  Delta = U - W S^T
+  size_t E = 0;          // f32 [state_slots, H_v, C, d]  P^T dO
   size_t dstates = 0;    // f32 [state_slots, H_v, d, d]  gradient at chunk ends
+  size_t dD = 0;         // f32 [state_slots, H_v, C, d]  dDelta, then dX_u
+  size_t SdO = 0;        // f32 [state_slots, H_v, C, d]
+  size_t DsD = 0;        // f32 [state_slots, H_v, C, d]
+  size_t SdD = 0;        // f32 [state_slots, H_v, C, d]  then dX_w
   size_t dqv = 0;        // f32 [T, H_v, d]  per value head dq-hat
   size_t dkv = 0;        // f32 [T, H_v, d]  per value head dk-hat
-  size_t dG = 0;         // f32 [T, H_v]     gradient w.r.t. the in-chunk cumsum
   size_t total = 0;
   int64_t full_slots = 0, state_slots = 0;
 };

@@ -1,0 +1,111 @@
+"""GPU parity of gdn_fwd_bwd against the fp64 oracle's gradient, its forward
+against gdn_prefill (bit for bit), and run-to-run determinism."""
+
+import numpy as np
+import pytest
+import torch
+
+from gdn_helpers import (bit_equal, group_slice, make_inputs, maxabs, oracle_bwd, rows_of,
+                         run_prefill, shape_for, to_dev)
+from linear_attention_rnn_gated_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+GRADS = ["dq", "dk", "dv", "dbeta", "dg", "dh0"]
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def run_fwd_bwd(inp, dhT=None, scale=1.0):
+    shape = shape_for(inp, scale)
+    d = to_dev(inp)
+    return B.gdn_fwd_bwd(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"],
+                         d["do"], h0=d["h0"], dhT=None if dhT is None else dhT.cuda())
+
+
+def compare(inp, r, tol, dhT=None, seqs=None, hv=None, rows=None, scale=1.0):
+    ref = oracle_bwd(inp, seqs=seqs, dhT=None if dhT is None else dhT.numpy(), scale=scale)
+    worst = {}
+    for k in GRADS:
+        got = r[k].double().cpu().numpy()
+        want = ref[k]
+        if seqs is not None:
+            if k == "dh0":
+                got, want = got[seqs], want[seqs]
+            else:
+                got, want = got[rows], want[rows]
+        if hv is not None:
+            if k in ("dq", "dk"):
+                pass
+            elif k == "dh0":
+                got = got[:, hv]
+            else:
+                got = got[:, hv]
+        worst[k] = maxabs(got, want)
+    say("  max|grad-oracle|: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()) +
+        f" (tol {tol})")
+    for k, v in worst.items():
+        assert np.isfinite(v) and v <= tol, k
+
+
+@pytest.mark.parametrize("dtype,lens,d,Hq,Hv", [
+    ("f32", [64], 16, 2, 2),
+    ("f32", [37, 16, 5], 16, 1, 2),
+    ("bf16", [150, 64, 1, 77], 128, 2, 4),
+    ("f32", [130, 64], 128, 1, 2),
+])
+def test_fwd_bwd_parity(dtype, lens, d, Hq, Hv):
+    say(f"case: fwd_bwd {dtype} d{d} lens={lens} H {Hq}/{Hv}")
+    inp = make_inputs(lens, Hq, Hv, d, dtype, seed=31, h0="normal", with_do=True)
+    gen = torch.Generator().manual_seed(99)
+    dhT = torch.randn(len(lens), Hv, d, d, generator=gen)
+    r = run_fwd_bwd(inp, dhT=dhT)
+    compare(inp, r, TOL[dtype], dhT=dhT)
+
+
+def test_fwd_bwd_scale_and_zero_dhT():
+    say("case: fwd_bwd with scale 0.6 and no state gradient")
+    inp = make_inputs([100, 65], 1, 2, 128, "bf16", seed=32, h0="normal", with_do=True)
+    r = run_fwd_bwd(inp, scale=0.6)
+    compare(inp, r, TOL["bf16"], scale=0.6)
+
+
+def test_fwd_bwd_forward_is_prefill_and_deterministic():
+    say("case: fwd_bwd forward == prefill; two runs bit-identical")
+    inp = make_inputs([300, 17, 64, 129, 0], 2, 4, 128, "bf16", seed=33, h0="normal",
+                      with_do=True)
+    r1 = run_fwd_bwd(inp)
+    r2 = run_fwd_bwd(inp)
+    o, hT, _ = run_prefill(inp)
+    assert bit_equal(r1["o"], o) and bit_equal(r1["hT"], hT)
+    for k in ["o", "hT"] + GRADS:
+        assert bit_equal(r1[k], r2[k]), k
+
+
+def test_fwd_bwd_b8_t4096_full_size():
+    """B=8, T=4096, 16 q/k / 32 v heads, d=128, C=64, bf16, dO ~ N(0,1): oracle
+    on one q/k group of one sequence; bitwise run-to-run."""
+    say("case: fwd_bwd B8 T4096 H16/32 d128 (sampled oracle)")
+    inp = make_inputs([4096] * 8, 16, 32, 128, "bf16", seed=3, h0="normal", with_do=True)
+    r1 = run_fwd_bwd(inp)
+    for k in GRADS:
+        assert torch.isfinite(r1[k]).all(), k
+    hq, n = 6, 5
+    gi, hv = group_slice(inp, hq)
+    rows = rows_of(inp, [n])
+    sub = {k: (r1[k][:, hq:hq + 1] if k in ("dq", "dk") else
+               r1[k][:, hv] if k != "dh0" else r1[k][:, hv]) for k in GRADS}
+    compare(gi, sub, TOL["bf16"], seqs=[n], rows=rows)
+    r2 = run_fwd_bwd(inp)
+    for k in ["o"] + GRADS:
+        assert bit_equal(r1[k], r2[k]), k
