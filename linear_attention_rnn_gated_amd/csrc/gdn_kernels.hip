@@ -419,25 +419,57 @@ __device__ __forceinline__ float row_dot(const float (&s)[D], P x) {
   return a;
 }
 
+// Operands of one RB-element block of a token: k_i, q_i and the next token's
+// k_i, as wave-uniform scalar loads.
+constexpr int RB = 8;
+// s_waitcnt immediate (gfx9 encoding): lgkmcnt = 0, expcnt and vmcnt unconstrained
+constexpr int kWaitLgkm0 = (0x3 << 14) | (0x0 << 8) | (0x7 << 4) | 0xF;
+struct OpBlock {
+  float k[RB], q[RB], n[RB];
+};
+template <int D>
+__device__ __forceinline__ void load_block(OpBlock& x, cfloat_p kq, cfloat_p kn, int b) {
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    x.k[r] = kq[b * RB + r];
+    x.q[r] = kq[D + b * RB + r];
+    x.n[r] = kn[b * RB + r];
+  }
+}
+
 // One token of R over a lane's row, operands as wave-uniform scalar loads:
 //   s_i = fmaf(delta, k_i, alpha * s_i);  o += s_i * q_i;  an += s_i * kn_i,
 // each chain in ascending i.  kq points at the token's [k | q] pair, kn at
-// the next token's k.  Every 8 elements an empty asm pins the accumulator
-// chains and a scheduling barrier stops the compiler from hoisting more scalar
-// loads than the SGPR file holds; neither changes any operation or its order.
+// the next token's k.  The operands of block b+1 are loaded before block b is
+// computed (cur/nxt), and the last block prefetches block 0 of the following
+// token into `cur` for the next call.  Scheduling barriers keep that order and
+// an empty asm pins the accumulator chains at every block edge; neither
+// changes any operation or its order.
 template <int D>
-__device__ __forceinline__ void r_token_pass(float (&s)[D], cfloat_p kq, cfloat_p kn, float alpha,
-                                             float delta, float& o, float& an) {
+__device__ __forceinline__ void r_token_pass(float (&s)[D], OpBlock& cur, cfloat_p kq, cfloat_p kn,
+                                             float alpha, float delta, float& o, float& an) {
+  constexpr int NB = D / RB;
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    s[i] = fmaf(delta, kq[i], alpha * s[i]);
-    o = fmaf(s[i], kq[D + i], o);
-    an = fmaf(s[i], kn[i], an);
-    if ((i & 7) == 7) {
-      // pin both accumulator chains here so they are not sunk past the loads
-      asm volatile("" : "+v"(o), "+v"(an));
-      __builtin_amdgcn_sched_barrier(0);
+  for (int b = 0; b < NB; ++b) {
+    // Scalar loads may complete out of order, so a wait is always "all
+    // outstanding": wait for `cur` here, before `nxt` is issued, so the
+    // compute below does not also wait for the prefetch.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_sched_barrier(0);
+    OpBlock nxt;
+    if (b + 1 < NB) load_block<D>(nxt, kq, kn, b + 1);
+    else load_block<D>(nxt, kq + 2 * D, kn + 2 * D, 0);  // next token (read, maybe unused)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int i = b * RB + r;
+      s[i] = fmaf(delta, cur.k[r], alpha * s[i]);
+      o = fmaf(s[i], cur.q[r], o);
+      an = fmaf(s[i], cur.n[r], an);
     }
+    asm volatile("" : "+v"(o), "+v"(an));
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
   }
 }
 
@@ -494,6 +526,8 @@ __global__ __launch_bounds__(64) void k_rec(RecIO io) {
   // key (t) / query (t) / key (t+1) streams, 2*D floats per token
   cfloat_p kq = as_const(io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D);
   float a = row_dot<D>(s, kq);
+  OpBlock cur;
+  load_block<D>(cur, kq, kq + 2 * D, 0);
   for (int t = 0; t < L; ++t) {
     const float alpha = expf(*gt);
     const float b = *bt;
@@ -502,7 +536,7 @@ __global__ __launch_bounds__(64) void k_rec(RecIO io) {
     const float delta = b * (vj - u);
     cfloat_p kn = kq + 2 * D;  // past the chunk's end on its last token: read, never used
     float o = 0.0f, an = 0.0f;
-    r_token_pass<D>(s, kq, kn, alpha, delta, o, an);
+    r_token_pass<D>(s, cur, kq, kn, alpha, delta, o, an);
     if (act) *op = o;
     a = an;
     kq += 2 * D;

@@ -64,9 +64,9 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
   L.state_slots = T / static_cast<int64_t>(C) + N;
   L.cu_chunks = take(&cur, (N + 1) * sizeof(int32_t));
   L.cu_full = take(&cur, (N + 1) * sizeof(int32_t));
-  // one spare token row: the token step reads the next key one token past the
-  // end of a chunk (the value is never used)
-  L.qk = take(&cur, (T * Hq + 1) * 2 * d * f);
+  // two spare token rows: the token step reads (prefetches) up to two tokens
+  // past the end of a chunk; those values are never used
+  L.qk = take(&cur, (T * Hq + 2) * 2 * d * f);
   const int64_t wu_slots = op == GDN_OP_FWD_BWD ? L.state_slots : L.full_slots;
   L.W = take(&cur, wu_slots * Hv * C * d * f);
   L.U = take(&cur, wu_slots * Hv * C * d * f);

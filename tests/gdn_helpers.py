@@ -111,7 +111,8 @@ def decode_tokens(inp, cache, shape, start, steps, dev="cuda", use_pos_host=True
 
 
 __all__ = ["make_inputs", "shape_for", "to_dev", "oracle_fwd", "oracle_bwd", "rows_of",
-           "maxabs", "bits", "bit_equal", "sub_inputs", "run_prefill", "decode_tokens"]
+           "maxabs", "bits", "bit_equal", "sub_inputs", "run_prefill", "decode_tokens",
+           "group_slice"]
 
 
 def group_slice(inp, hq):

@@ -34,7 +34,7 @@ def run_fwd_bwd(inp, dhT=None, scale=1.0):
 
 
 def compare(inp, r, tol, dhT=None, seqs=None, hv=None, rows=None, scale=1.0):
-    ref = oracle_bwd(inp, seqs=seqs, dhT=None if dhT is None else dhT.numpy(), scale=scale)
+    ref = oracle_bwd(inp, seqs=seqs, dhT=dhT, scale=scale)
     worst = {}
     for k in GRADS:
         got = r[k].double().cpu().numpy()
