@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--train-steps", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 plain device copies of 1 GiB (the reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     return ap.parse_args()
 
 
@@ -260,6 +263,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": a.numel() * 4, "copies": 5}), flush=True)
+        return
     from linear_attention_rnn_gated_amd import binding as B
     from linear_attention_rnn_gated_amd.inputs import make_inputs
     assert torch.cuda.is_available(), "bench needs a GPU"

@@ -49,7 +49,8 @@
  *     outside the compiled claims return GDN_ERR_UNSUPPORTED -- they are never
  *     run through a different arithmetic.
  *   - Supported: d_k == d_v == 128 with C == 64, or d_k == d_v == 16 with
- *     C == 16; H_v a multiple of H_qk; in_dtype fp32 or bf16.
+ *     C == 16; H_v a multiple of H_qk with at most 8 value heads per q/k
+ *     head; in_dtype fp32 or bf16.
  *   - Calls that overlap on the same workspace or cache race; calls on
  *     separate buffers may run concurrently.
  */

@@ -403,6 +403,415 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
 }
 
 // ---------------------------------------------------------------------------
+// B, part 2 on the matrix cores (d = 128, C = 64): the same step as k_scan,
+//   Delta = U - W S^T            (64 x 32 x 128 per 32-row tile)
+//   S'    = gam S + Dt^T Khat    (32 x 128 x 64),  Dt_p = Delta_p * lam_p,
+// with v_mfma_f32_16x16x4_f32.  Fixed reduction order: Delta starts from U and
+// adds the 32 products of i-steps s = 0..31, lane group g supplying i =
+// 32 g + s; S' starts from gam * S and adds the 16 products of p-steps s =
+// 0..15, group g supplying p = 16 g + s.  Four waves: wave w owns rows
+// p in [16w, 16w + 16) of Delta and columns i in [32w, 32w + 32) of S'.
+// The prefill scan and the decode resync both run this kernel.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Launches are padded to a multiple of 8 blocks; consecutive virtual block
+// ids land on the same XCD (blocks are dispatched round-robin over the 8 XCDs)
+// so the tiles of one head, and the heads of one q/k group, share an L2.
+__device__ __forceinline__ int64_t xcd_block(int64_t nb8) {
+  const int64_t b = blockIdx.x;
+  return (b % 8) * (nb8 / 8) + b / 8;
+}
+
+template <int C, int MODE>
+__global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, int64_t nb8) {
+  constexpr int D = 128, TILE = 32, NTILE = D / TILE;
+  constexpr int SS = D + 4;  // row stride of sS (floats)
+  constexpr int DS = C + 4;  // row stride of sDt
+  static_assert(C == 64, "tiling assumes C = 64");
+  constexpr bool RESYNC = MODE == kResync;
+  __shared__ __attribute__((aligned(16))) float sS[TILE * SS];   // S[j][i] of the tile
+  __shared__ __attribute__((aligned(16))) float sDt[TILE * DS];  // Dt[j][p]
+  __shared__ float sG[C];
+  __shared__ float sLam[C];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t vb = xcd_block(nb8);
+  if (vb >= nblocks) return;
+  const int tile = static_cast<int>(vb % NTILE);
+  const int h = static_cast<int>((vb / NTILE) % io.H_v);
+  const int n = static_cast<int>(vb / (NTILE * io.H_v));
+  if (n >= io.N) return;
+  const int hq = h / (io.H_v / io.H_qk);
+  const int j0 = tile * TILE;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
+
+  int64_t tok0 = 0, nsteps = 1, L = 0, slot0 = 0, fslot0 = 0, nchunks = 0;
+  if (RESYNC) {
+    if (io.pos[nh] != 0) return;
+    fslot0 = n;
+  } else {
+    tok0 = io.cu[n];
+    L = static_cast<int64_t>(io.cu[n + 1]) - tok0;
+    if (L < 0 || tok0 < 0 || tok0 + L > io.T) return;
+    nchunks = (L + C - 1) / C;
+    nsteps = MODE == kAll ? nchunks : L / C;
+    slot0 = io.cu_chunks[n];
+    fslot0 = MODE == kAll ? slot0 : io.cu_full[n];
+    if (slot0 + nchunks > io.max_state_slot || fslot0 + nsteps > io.max_full_slot) return;
+  }
+
+  const float* src = RESYNC ? io.S_chunk + nh * DD : (io.h0 ? io.h0 + nh * DD : nullptr);
+  for (int e = tid; e < TILE * D; e += 256) {
+    const int i = e / TILE, jj = e % TILE;
+    sS[jj * SS + i] = src ? src[static_cast<int64_t>(i) * D + j0 + jj] : 0.0f;
+  }
+  __syncthreads();
+  // this wave's S' tiles in accumulator layout: (j = 16 jb + 4 g + r, i = 32 w + 16 ib + l16)
+  v4f accS[2][2];
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        accS[jb][ib][r] = sS[(jb * 16 + 4 * g + r) * SS + 32 * w + 16 * ib + l16];
+
+  // Operands of one chunk step, loaded one step ahead (VMEM loads complete in
+  // order, so the next step's loads overlap this step's matrix work).
+  // W, U and G of a chunk step are loaded one step ahead (VMEM loads complete
+  // in order, so they overlap the previous step's matrix work); Khat is loaded
+  // at the start of its own step and lands while Delta is computed.
+  struct StepOps {
+    float4 wa[8];      // -W rows 16 w + l16, i = 32 g + 4 s4 + (0..3)
+    float u[2][4];     // U rows 16 w + 4 g + r, columns 16 jb + l16 of the tile
+    float gv;          // G[tid] (tid < C)
+  };
+  auto load_ops = [&](StepOps& o, int64_t c) {
+    const int64_t fs = fslot0 + c;
+    const float* Wc = io.W + (fs * io.H_v + h) * static_cast<int64_t>(C) * D;
+    const float* Uc = io.U + (fs * io.H_v + h) * static_cast<int64_t>(C) * D;
+    const float* wrow = Wc + static_cast<int64_t>(16 * w + l16) * D + 32 * g;
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) o.wa[s4] = *reinterpret_cast<const float4*>(wrow + 4 * s4);
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        o.u[jb][r] = Uc[static_cast<int64_t>(16 * w + 4 * g + r) * D + j0 + 16 * jb + l16];
+    o.gv = tid < C ? io.G[(fs * io.H_v + h) * C + tid] : 0.0f;
+  };
+  auto load_khat = [&](float (&kb)[16][2], int64_t c) {
+    const int64_t ktok0 = RESYNC ? static_cast<int64_t>(n) * C : tok0 + c * C;
+    int64_t kst;
+    const float* krow = key_rows<D, RESYNC>(io.khat, io.T, io.H_qk, hq, ktok0, kst);
+    const int rows = RESYNC ? C : static_cast<int>(L - c * C < C ? L - c * C : C);
+#pragma unroll
+    for (int pq = 0; pq < 16; ++pq) {
+      const int p = 16 * g + pq;
+      const int pc = p < rows ? p : rows - 1;  // in bounds; zeroed below
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const float x = krow[pc * kst + 32 * w + 16 * ib + l16];
+        kb[pq][ib] = p < rows ? x : 0.0f;
+      }
+    }
+  };
+  StepOps cur;
+  if (nsteps > 0) load_ops(cur, 0);
+
+  for (int64_t c = 0; c < nsteps; ++c) {
+    if (!RESYNC) {  // chunk-start state of chunk c
+      float* dst = io.states + ((slot0 + c) * io.H_v + h) * DD;
+      for (int e = tid; e < TILE * D; e += 256) {
+        const int i = e / TILE, jj = e % TILE;
+        dst[static_cast<int64_t>(i) * D + j0 + jj] = sS[jj * SS + i];
+      }
+    }
+    const int64_t fs = fslot0 + c;
+    if (tid < C) sG[tid] = cur.gv;
+    float kb[16][2];
+    load_khat(kb, c);
+    StepOps nxt;
+    if (c + 1 < nsteps) load_ops(nxt, c + 1);
+    __syncthreads();
+    const float glast = sG[C - 1];
+    if (tid < C) sLam[tid] = expf(glast - sG[tid]);
+    // ---- Delta rows p = 16 w + 4 g + r, columns j = 16 jb + l16
+    v4f accD[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accD[jb][r] = cur.u[jb][r];
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) {
+      const float4 wa = cur.wa[s4];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const float4 sb = *reinterpret_cast<const float4*>(sS + (16 * jb + l16) * SS + 32 * g + 4 * s4);
+        accD[jb] = mfma4(-wa.x, sb.x, accD[jb]);
+        accD[jb] = mfma4(-wa.y, sb.y, accD[jb]);
+        accD[jb] = mfma4(-wa.z, sb.z, accD[jb]);
+        accD[jb] = mfma4(-wa.w, sb.w, accD[jb]);
+      }
+    }
+    if (MODE == kAll) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          io.Dl[((fs * io.H_v + h) * C + 16 * w + 4 * g + r) * static_cast<int64_t>(D) + j0 + 16 * jb + l16] =
+              accD[jb][r];
+    }
+    __syncthreads();  // sLam ready; every wave is done reading sS
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      v4f x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = accD[jb][r] * sLam[16 * w + 4 * g + r];
+      *reinterpret_cast<v4f*>(sDt + (16 * jb + l16) * DS + 16 * w + 4 * g) = x;
+    }
+    __syncthreads();
+    // ---- S' = gam S + Dt^T Khat, rows j = 16 jb + 4 g + r, columns i = 32 w + 16 ib + l16
+    const float gam = expf(glast);
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accS[jb][ib][r] = gam * accS[jb][ib][r];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      float4 da[2];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+        da[jb] = *reinterpret_cast<const float4*>(sDt + (16 * jb + l16) * DS + 16 * g + 4 * s4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const float a = q == 0 ? da[jb].x : q == 1 ? da[jb].y : q == 2 ? da[jb].z : da[jb].w;
+#pragma unroll
+          for (int ib = 0; ib < 2; ++ib) accS[jb][ib] = mfma4(a, kb[4 * s4 + q][ib], accS[jb][ib]);
+        }
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sS[(jb * 16 + 4 * g + r) * SS + 32 * w + 16 * ib + l16] = accS[jb][ib][r];
+    __syncthreads();
+    if (c + 1 < nsteps) cur = nxt;
+  }
+
+  if (RESYNC) {
+    float* d1 = io.S_chunk + nh * DD;
+    float* d2 = io.S_run + nh * DD;
+    for (int e = tid; e < TILE * D; e += 256) {
+      const int i = e / TILE, jj = e % TILE;
+      const float x = sS[jj * SS + i];
+      d1[static_cast<int64_t>(i) * D + j0 + jj] = x;
+      d2[static_cast<int64_t>(i) * D + j0 + jj] = x;
+    }
+    return;
+  }
+  const bool tail = (L % C) != 0;
+  if (MODE == kAll && tail) return;
+  for (int e = tid; e < TILE * D; e += 256) {
+    const int i = e / TILE, jj = e % TILE;
+    const int64_t off = static_cast<int64_t>(i) * D + j0 + jj;
+    const float x = sS[jj * SS + i];
+    if (tail) {
+      io.states[((slot0 + nsteps) * io.H_v + h) * DD + off] = x;  // tail chunk start
+      if (io.S_chunk) io.S_chunk[nh * DD + off] = x;
+    } else {
+      if (io.hT) io.hT[nh * DD + off] = x;
+      if (io.S_chunk) {
+        io.S_chunk[nh * DD + off] = x;
+        io.S_run[nh * DD + off] = x;
+      }
+    }
+  }
+  if (io.pos && tile == 0 && tid == 0) io.pos[nh] = static_cast<int32_t>(L % C);
+}
+
+// ---------------------------------------------------------------------------
+// B, part 1 on the matrix cores (d = 128, C = 64).  Same quantities as k_wy:
+//   A_pr = beta_p * ((k_p . k_r) * exp(G_p - G_r))   (p > r)
+//   [W | U] = (I + A)^-1 [diag(beta gam) K | diag(beta) V]
+// The Gram matrix comes from v_mfma_f32_16x16x4_f32 (i-steps s = 0..31, lane
+// group g supplying i = 32 g + s).  The solve is blocked by 16 rows: block
+// row b starts from its right-hand side, subtracts A[b][c] Y[c] for the solved
+// blocks c < b on the matrix cores (k-steps s = 0..3, group g supplying row
+// 4 g + s of block c), then runs forward substitution inside the block, row
+// by row, each solved row broadcast across the wave with a shuffle.  Wave w
+// owns 64 columns: W[:, 64w..] for w < 2, U[:, 64(w-2)..] for w >= 2.  Decode
+// resync runs this same kernel.
+template <int C, typename TIn, int MODE>
+__global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
+  constexpr int D = 128;
+  constexpr int KS = D + 4;  // row stride of sK
+  constexpr int AS = C + 4;  // row stride of sA
+  static_assert(C == 64, "tiling assumes C = 64");
+  constexpr bool RESYNC = MODE == kResync;
+  __shared__ __attribute__((aligned(16))) float sK[C * KS];
+  __shared__ float sA[C * AS];
+  __shared__ float sB[C], sG[C], sBG[C];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int l16 = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y;
+  const int hq = h / (io.H_v / io.H_qk);
+  int64_t tok0, slot;
+  int L = C;
+  if (MODE == kResync) {
+    const int n = blockIdx.x;
+    if (io.pos[static_cast<int64_t>(n) * io.H_v + h] != 0) return;
+    tok0 = static_cast<int64_t>(n) * C;
+    slot = n;
+  } else {
+    slot = blockIdx.x;
+    if (slot >= io.cu_full[io.N]) return;
+    const int n = find_seq(io.cu_full, io.N, slot);
+    tok0 = static_cast<int64_t>(io.cu[n]) + static_cast<int64_t>(slot - io.cu_full[n]) * C;
+    if (MODE == kAll) {
+      const int64_t rem = static_cast<int64_t>(io.cu[n + 1]) - tok0;
+      L = rem < C ? static_cast<int>(rem) : C;
+      if (L <= 0) return;
+    }
+  }
+  if (tok0 < 0 || tok0 + L > io.T || slot >= io.max_slot) return;
+
+  int64_t kst;
+  const float* krow = key_rows<D, RESYNC>(io.khat, io.T, io.H_qk, hq, tok0, kst);
+  const bool isW = w < 2;
+  const int cbase = 64 * (w & 1);
+  const TIn* v = static_cast<const TIn*>(io.v) + tok0 * io.H_v * D + static_cast<int64_t>(h) * D;
+  // values of this wave's U columns, loaded up front: (row 16 bi + 4 g + r, column cbase + 16 ct + l16)
+  float vpre[4][4][4];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * bi + 4 * g + r;
+        const int pc = p < L ? p : L - 1;
+        const float x = isW ? 0.0f : ldin(v + static_cast<int64_t>(pc) * io.H_v * D + cbase + 16 * ct + l16);
+        vpre[bi][ct][r] = p < L ? x : 0.0f;
+      }
+  // rows past a partial chunk's end read the last row (in bounds) and are zeroed
+  for (int e = tid; e < C * (D / 4); e += 256) {
+    const int p = e / (D / 4), i4 = e % (D / 4);
+    const int pc = p < L ? p : L - 1;
+    const float4 x = *reinterpret_cast<const float4*>(krow + pc * kst + 4 * i4);
+    *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) =
+        p < L ? x : float4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  if (tid < C) {
+    const int pc = tid < L ? tid : L - 1;
+    const float bx = io.beta[(tok0 + pc) * io.H_v + h];
+    const float gx = io.g[(tok0 + pc) * io.H_v + h];
+    sB[tid] = tid < L ? bx : 0.0f;
+    sBG[tid] = tid < L ? gx : 0.0f;  // raw g for now
+  }
+  __syncthreads();
+  if (tid == 0) {  // running sum of g, p ascending
+    float acc = 0.0f;
+    for (int p = 0; p < C; ++p) {
+      acc = acc + sBG[p];
+      sG[p] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < C) sBG[tid] = sB[tid] * expf(sG[tid]);
+  // Gram rows p = 16 w + 4 g + r, columns r' = 16 cb + l16 (lower blocks only)
+  {
+    v4f kk[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) kk[cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(sK + (16 * w + l16) * KS + 32 * g + 4 * s4);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        if (cb > w) continue;
+        const float4 b4 = *reinterpret_cast<const float4*>(sK + (16 * cb + l16) * KS + 32 * g + 4 * s4);
+        kk[cb] = mfma4(a4.x, b4.x, kk[cb]);
+        kk[cb] = mfma4(a4.y, b4.y, kk[cb]);
+        kk[cb] = mfma4(a4.z, b4.z, kk[cb]);
+        kk[cb] = mfma4(a4.w, b4.w, kk[cb]);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * w + 4 * g + r, q = 16 * cb + l16;
+        // operands read and exp taken unconditionally: a select, not a branch
+        const float gpq = expf(sG[p] - sG[q]);
+        const float a = sB[p] * (kk[cb][r] * gpq);
+        sA[p * AS + q] = (cb <= w && q < p) ? a : 0.0f;
+      }
+  }
+  __syncthreads();
+  float* out = (isW ? io.W : io.U) + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
+  v4f Y[4][4];  // [row block][column tile], accumulator layout
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) {
+    v4f acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * bi + 4 * g + r, col = cbase + 16 * ct + l16;
+        acc[ct][r] = isW ? sBG[p] * sK[p * KS + col] : sB[p] * vpre[bi][ct][r];
+      }
+#pragma unroll
+    for (int bj = 0; bj < bi; ++bj)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float a = -sA[(16 * bi + l16) * AS + 16 * bj + 4 * g + s4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = mfma4(a, Y[bj][ct][s4], acc[ct]);
+      }
+    // forward substitution inside the block
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) {
+      const int gp = pp >> 2, rp = pp & 3;
+      float a[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = sA[(16 * bi + 4 * g + r) * AS + 16 * bi + pp];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const float y = __shfl(acc[ct][rp], l16 + 16 * gp, 64);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float upd = fmaf(-a[r], y, acc[ct][r]);
+          acc[ct][r] = 4 * g + r > pp ? upd : acc[ct][r];
+        }
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      Y[bi][ct] = acc[ct];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        out[static_cast<int64_t>(16 * bi + 4 * g + r) * D + cbase + 16 * ct + l16] = acc[ct][r];
+    }
+  }
+  if (tid < C) io.G[(slot * io.H_v + h) * C + tid] = sG[tid];
+}
+
+// ---------------------------------------------------------------------------
 // R -- the token step, per lane = one row j (a d_v index) of the state, the
 // row's d_k entries in registers s[0..D).  For a token with a = s . k (taken
 // on the state before the token):
@@ -415,15 +824,36 @@ template <int D, typename P>
 __device__ __forceinline__ float row_dot(const float (&s)[D], P x) {
   float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < D; ++i) a = fmaf(s[i], x[i], a);
+  for (int i = 0; i < D; ++i) {
+    a = fmaf(s[i], x[i], a);
+    if ((i & 7) == 7) asm volatile("" : "+v"(a));  // keep operand reads in blocks
+  }
   return a;
+}
+
+// The decode form of one token of R (same operations and order as k_rec's
+// pass, without the next-token chain): s_i = fmaf(delta, k_i, alpha * s_i);
+// o += s_i * q_i.  k, q are in LDS; reads are kept in blocks of 8 so the
+// operands do not all become live at once.
+template <int D>
+__device__ __forceinline__ float r_update_lds(float (&s)[D], const float* k, const float* q,
+                                              float alpha, float delta) {
+  float o = 0.0f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    s[i] = fmaf(delta, k[i], alpha * s[i]);
+    o = fmaf(s[i], q[i], o);
+    if ((i & 7) == 7) {
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  return o;
 }
 
 // Operands of one RB-element block of a token: k_i, q_i and the next token's
 // k_i, as wave-uniform scalar loads.
-constexpr int RB = 8;
-// s_waitcnt immediate (gfx9 encoding): lgkmcnt = 0, expcnt and vmcnt unconstrained
-constexpr int kWaitLgkm0 = (0x3 << 14) | (0x0 << 8) | (0x7 << 4) | 0xF;
+constexpr int RB = 16;
 struct OpBlock {
   float k[RB], q[RB], n[RB];
 };
@@ -440,36 +870,30 @@ __device__ __forceinline__ void load_block(OpBlock& x, cfloat_p kq, cfloat_p kn,
 // One token of R over a lane's row, operands as wave-uniform scalar loads:
 //   s_i = fmaf(delta, k_i, alpha * s_i);  o += s_i * q_i;  an += s_i * kn_i,
 // each chain in ascending i.  kq points at the token's [k | q] pair, kn at
-// the next token's k.  The operands of block b+1 are loaded before block b is
-// computed (cur/nxt), and the last block prefetches block 0 of the following
-// token into `cur` for the next call.  Scheduling barriers keep that order and
-// an empty asm pins the accumulator chains at every block edge; neither
-// changes any operation or its order.
+// the next token's k.  The row is walked in blocks of RB elements (one
+// scalar-load wait per block, so RB is as large as the SGPR file allows); at every
+// block edge an empty asm pins the accumulator chains and a scheduling
+// barrier stops the compiler from hoisting more scalar loads than the SGPR
+// file holds.  Neither changes any operation or its order.  (Prefetching a
+// block ahead measured slower: scalar loads complete out of order, so every
+// wait is an all-outstanding wait.)
 template <int D>
-__device__ __forceinline__ void r_token_pass(float (&s)[D], OpBlock& cur, cfloat_p kq, cfloat_p kn,
-                                             float alpha, float delta, float& o, float& an) {
+__device__ __forceinline__ void r_token_pass(float (&s)[D], cfloat_p kq, cfloat_p kn, float alpha,
+                                             float delta, float& o, float& an) {
   constexpr int NB = D / RB;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    // Scalar loads may complete out of order, so a wait is always "all
-    // outstanding": wait for `cur` here, before `nxt` is issued, so the
-    // compute below does not also wait for the prefetch.
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_sched_barrier(0);
-    OpBlock nxt;
-    if (b + 1 < NB) load_block<D>(nxt, kq, kn, b + 1);
-    else load_block<D>(nxt, kq + 2 * D, kn + 2 * D, 0);  // next token (read, maybe unused)
-    __builtin_amdgcn_sched_barrier(0);
+    OpBlock x;
+    load_block<D>(x, kq, kn, b);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const int i = b * RB + r;
-      s[i] = fmaf(delta, cur.k[r], alpha * s[i]);
-      o = fmaf(s[i], cur.q[r], o);
-      an = fmaf(s[i], cur.n[r], an);
+      s[i] = fmaf(delta, x.k[r], alpha * s[i]);
+      o = fmaf(s[i], x.q[r], o);
+      an = fmaf(s[i], x.n[r], an);
     }
     asm volatile("" : "+v"(o), "+v"(an));
     __builtin_amdgcn_sched_barrier(0);
-    cur = nxt;
   }
 }
 
@@ -493,12 +917,19 @@ struct RecIO {
   int64_t T, max_state_slot;
 };
 
+// Blocks of up to 4 waves over (chunk, q/k head): a wave per (value head of
+// the group, 64-row half of d_v), so waves that read the same key/query stream
+// share a CU and its scalar cache; blockIdx.z continues a group of more than
+// 4 waves.
 template <int D, int C, typename TIn>
-__global__ __launch_bounds__(64) void k_rec(RecIO io) {
+__global__ __launch_bounds__(256) void k_rec(RecIO io) {
+  constexpr int NH = (D + 63) / 64;  // waves per value head
   const int slot = blockIdx.x;
-  const int h = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int j = blockIdx.z * 64 + lane;
+  const int wv = __builtin_amdgcn_readfirstlane(blockIdx.z * 4 + (threadIdx.x >> 6));
+  if (wv >= (io.H_v / io.H_qk) * NH) return;  // whole wave
+  const int h = blockIdx.y * (io.H_v / io.H_qk) + wv / NH;
+  const int lane = threadIdx.x & 63;
+  const int j = (wv % NH) * 64 + lane;
   const bool act = j < D;
   const int jc = act ? j : 0;  // inactive lanes (D < 64) read row 0 and store nothing
   if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return;
@@ -526,8 +957,6 @@ __global__ __launch_bounds__(64) void k_rec(RecIO io) {
   // key (t) / query (t) / key (t+1) streams, 2*D floats per token
   cfloat_p kq = as_const(io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D);
   float a = row_dot<D>(s, kq);
-  OpBlock cur;
-  load_block<D>(cur, kq, kq + 2 * D, 0);
   for (int t = 0; t < L; ++t) {
     const float alpha = expf(*gt);
     const float b = *bt;
@@ -536,7 +965,7 @@ __global__ __launch_bounds__(64) void k_rec(RecIO io) {
     const float delta = b * (vj - u);
     cfloat_p kn = kq + 2 * D;  // past the chunk's end on its last token: read, never used
     float o = 0.0f, an = 0.0f;
-    r_token_pass<D>(s, cur, kq, kn, alpha, delta, o, an);
+    r_token_pass<D>(s, kq, kn, alpha, delta, o, an);
     if (act) *op = o;
     a = an;
     kq += 2 * D;
@@ -572,7 +1001,7 @@ __global__ __launch_bounds__(64) void k_rec(RecIO io) {
         io.kbuf[(bi * io.H_qk + hq) * D + j] =
             io.qk[((static_cast<int64_t>(hq) * io.T + tk) * 2) * D + j];
     }
-    if (blockIdx.z == 0 && lane == 0) {
+    if (j == 0) {
       io.bbuf[bi * io.H_v + h] = io.beta[tk * io.H_v + h];
       io.gbuf[bi * io.H_v + h] = io.g[tk * io.H_v + h];
     }
@@ -642,12 +1071,7 @@ __global__ __launch_bounds__(D < 64 ? 64 : D) void k_decode(DecIO io) {
   const float a = row_dot<D>(s, static_cast<const float*>(sk));
   const float u = alpha * a;
   const float delta = b * (vj - u);
-  float o = 0.0f;
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    s[i] = fmaf(delta, sk[i], alpha * s[i]);
-    o = fmaf(s[i], sq[i], o);
-  }
+  const float o = r_update_lds<D>(s, sk, sq, alpha, delta);
   if (act) {
 #pragma unroll
     for (int i = 0; i < D; ++i) sr[static_cast<int64_t>(i) * D + j] = s[i];
@@ -1225,6 +1649,33 @@ constexpr int kTile128 = 32;  // state rows per k_scan block at d = 128
 template <int D>
 constexpr int scan_tile() { return D == 128 ? kTile128 : D; }
 
+// The chunk factors: matrix-core kernel at d = 128, the VALU kernel at d = 16.
+template <int D, int C, typename TIn, int MODE>
+void launch_wy(const ChunkIO& io, int64_t items, int H_v, hipStream_t st) {
+  if (items <= 0) return;
+  const dim3 grid(static_cast<unsigned>(items), H_v);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((k_wy_mfma<C, TIn, MODE>), grid, dim3(256), 0, st, io);
+  else
+    hipLaunchKernelGGL((k_wy<D, C, TIn, MODE>), grid, dim3(256), 0, st, io);
+}
+
+// The chunk-state scan: matrix-core kernel at d = 128, the VALU kernel at d = 16.
+template <int D, int C, int MODE>
+void launch_scan(const ScanIO& io, int64_t N, int H_v, hipStream_t st) {
+  constexpr int TILE = scan_tile<D>();
+  const int64_t blocks = N * H_v * (D / TILE);
+  if (blocks <= 0) return;
+  if constexpr (D == 128) {
+    const int64_t nb8 = (blocks + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_scan_mfma<C, MODE>), dim3(static_cast<unsigned>(nb8)), dim3(256), 0, st,
+                       io, blocks, nb8);
+  } else {
+    hipLaunchKernelGGL((k_scan<D, C, TILE, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256),
+                       0, st, io);
+  }
+}
+
 template <int D, int C, typename TIn>
 int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const gdn::Layout& L,
                    const int32_t* cu, const void* q, const void* k, const void* v,
@@ -1255,8 +1706,7 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     io.W = W; io.U = U; io.G = Gs;
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_slot = L.full_slots;
     Timed t_("k_wy", st);
-    hipLaunchKernelGGL((k_wy<D, C, TIn, kFull>), dim3(static_cast<unsigned>(cnt.full), s->H_v),
-                       dim3(256), 0, st, io);
+    launch_wy<D, C, TIn, kFull>(io, cnt.full, s->H_v, st);
   }
   {
     ScanIO io{};
@@ -1265,12 +1715,9 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     if (cache) { io.S_run = cache->S_run; io.S_chunk = cache->S_chunk; io.pos = cache->pos; }
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
     io.max_state_slot = L.state_slots; io.max_full_slot = L.full_slots;
-    constexpr int TILE = scan_tile<D>();
-    const int64_t blocks = static_cast<int64_t>(N) * s->H_v * (D / TILE);
-    if (blocks > 0) {
+    if (N > 0) {
       Timed t_("k_scan", st);
-      hipLaunchKernelGGL((k_scan<D, C, TILE, kFull>), dim3(static_cast<unsigned>(blocks)),
-                         dim3(256), 0, st, io);
+      launch_scan<D, C, kFull>(io, N, s->H_v, st);
     }
   }
   if (cnt.chunks > 0) {
@@ -1283,9 +1730,10 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     }
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_state_slot = L.state_slots;
     Timed t_("k_rec", st);
+    const int waves = (s->H_v / s->H_qk) * ((D + 63) / 64);
     hipLaunchKernelGGL((k_rec<D, C, TIn>),
-                       dim3(static_cast<unsigned>(cnt.chunks), s->H_v, (D + 63) / 64), dim3(64), 0,
-                       st, io);
+                       dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, (waves + 3) / 4),
+                       dim3(64 * (waves < 4 ? waves : 4)), 0, st, io);
   }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -1314,17 +1762,14 @@ int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const v
     ci.T = static_cast<int64_t>(N) * C; ci.max_slot = N;
     {
       Timed t_("k_wy_resync", st);
-      hipLaunchKernelGGL((k_wy<D, C, TIn, kResync>), dim3(N, s->H_v), dim3(256), 0, st, ci);
+      launch_wy<D, C, TIn, kResync>(ci, N, s->H_v, st);
     }
     ScanIO si{};
     si.khat = cache->kbuf; si.W = W; si.U = U; si.G = Gs;
     si.S_run = cache->S_run; si.S_chunk = cache->S_chunk; si.pos = cache->pos;
     si.N = N; si.H_qk = s->H_qk; si.H_v = s->H_v; si.max_full_slot = N;
-    constexpr int TILE = scan_tile<D>();
     Timed t_("k_scan_resync", st);
-    hipLaunchKernelGGL((k_scan<D, C, TILE, kResync>),
-                       dim3(static_cast<unsigned>(static_cast<int64_t>(N) * s->H_v * (D / TILE))),
-                       dim3(256), 0, st, si);
+    launch_scan<D, C, kResync>(si, N, s->H_v, st);
   }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -1360,8 +1805,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     io.W = W; io.U = U; io.G = Gs;
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_slot = L.state_slots;
     Timed t_("k_wy", st);
-    hipLaunchKernelGGL((k_wy<D, C, TIn, kAll>), dim3(static_cast<unsigned>(cnt.chunks), s->H_v),
-                       dim3(256), 0, st, io);
+    launch_wy<D, C, TIn, kAll>(io, cnt.chunks, s->H_v, st);
   }
   constexpr int TILE = scan_tile<D>();
   const int64_t sblocks = static_cast<int64_t>(N) * s->H_v * (D / TILE);
@@ -1372,8 +1816,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
     io.max_state_slot = L.state_slots; io.max_full_slot = L.state_slots;
     Timed t_("k_scan", st);
-    hipLaunchKernelGGL((k_scan<D, C, TILE, kAll>), dim3(static_cast<unsigned>(sblocks)),
-                       dim3(256), 0, st, io);
+    launch_scan<D, C, kAll>(io, N, s->H_v, st);
   }
   if (cnt.chunks > 0) {
     RecIO io{};
@@ -1381,9 +1824,10 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     io.cu_chunks = cu_chunks; io.states = states; io.o = o; io.hT = hT;
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_state_slot = L.state_slots;
     Timed t_("k_rec", st);
+    const int waves = (s->H_v / s->H_qk) * ((D + 63) / 64);
     hipLaunchKernelGGL((k_rec<D, C, TIn>),
-                       dim3(static_cast<unsigned>(cnt.chunks), s->H_v, (D + 63) / 64), dim3(64), 0,
-                       st, io);
+                       dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, (waves + 3) / 4),
+                       dim3(64 * (waves < 4 ? waves : 4)), 0, st, io);
   }
   // backward
   BwdIO b{};
@@ -1584,8 +2028,8 @@ int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
 }
 
 const char* gdn_contract_id(void) {
-  return "gdn-cpr/v1;eps=1e-6;claims=d16C16,d128C64;R=lane-row,fmaf-asc,o-after-update;"
-         "B=valu,scan-tile32;prep=wave-butterfly";
+  return "gdn-cpr/v5;eps=1e-6;claims=d16C16,d128C64;R=lane-row,fmaf-asc,o-after-update;"
+         "B=mfma16x16x4-wy-blocked16,mfma16x16x4-scan-tile32;prep=wave-butterfly";
 }
 
 const char* gdn_error_string(int status) {

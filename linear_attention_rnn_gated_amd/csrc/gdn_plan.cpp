@@ -14,6 +14,7 @@ int check_shape(const gdn_shape_t* s) {
   if (!std::isfinite(s->scale)) return GDN_ERR_INVALID_ARG;
   if (s->in_dtype != GDN_F32 && s->in_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (s->H_v % s->H_qk != 0) return GDN_ERR_UNSUPPORTED;
+  if (s->H_v / s->H_qk > 8) return GDN_ERR_UNSUPPORTED;  // token-step block: <= 16 waves
   if (s->d_k != s->d_v) return GDN_ERR_UNSUPPORTED;
   // keep every [.., H, d] row offset well inside 32 bits per token
   if (static_cast<int64_t>(s->H_v) * s->d_v > (1 << 20)) return GDN_ERR_UNSUPPORTED;

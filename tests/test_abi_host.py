@@ -55,6 +55,7 @@ def good_shape(**kw):
     (dict(d_k=16, d_v=16, C=64), B.GDN_ERR_UNSUPPORTED),
     (dict(d_v=16), B.GDN_ERR_UNSUPPORTED),
     (dict(H_v=3), B.GDN_ERR_UNSUPPORTED),
+    (dict(H_qk=1, H_v=16), B.GDN_ERR_UNSUPPORTED),
     (dict(H_qk=0), B.GDN_ERR_INVALID_ARG),
     (dict(in_dtype=7), B.GDN_ERR_UNSUPPORTED),
     (dict(qk_l2norm=2), B.GDN_ERR_INVALID_ARG),
