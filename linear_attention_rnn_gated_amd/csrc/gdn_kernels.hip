@@ -1526,6 +1526,545 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdIO io) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core forms of the backward for d = 128, C = 64.  The gradient is the
+// same as above; sums are taken on v_mfma_f32_16x16x4_f32 in a fixed order.
+// Tile helpers: one 16 x 16 output tile in accumulator layout (lane l holds
+// rows 4g + r, column l16; g = l / 16), K summed in steps of 4 with lane group
+// g supplying k = g K/4 + s, s = 0 .. K/4 - 1.
+//   mma_nt: a -> A[m0 + l16][0], b -> B[n0 + l16][0], both k-contiguous
+//   mma_nn: a -> A[m0 + l16][0] k-contiguous; b -> B[0][n0 + l16], row stride
+//           ldb; rows of B at or past `brows` read row brows - 1 (in bounds)
+//   mma_tn: a -> At[0][m0 + l16] (A given transposed, row stride lda); b as nn
+template <int K>
+__device__ __forceinline__ v4f mma_nt(v4f acc, const float* a, const float* b) {
+  const int g = (threadIdx.x & 63) >> 4;
+  a += g * (K / 4);
+  b += g * (K / 4);
+#pragma unroll
+  for (int s4 = 0; s4 < K / 16; ++s4) {
+    const float4 x = *reinterpret_cast<const float4*>(a + 4 * s4);
+    const float4 y = *reinterpret_cast<const float4*>(b + 4 * s4);
+    acc = mfma4(x.x, y.x, acc);
+    acc = mfma4(x.y, y.y, acc);
+    acc = mfma4(x.z, y.z, acc);
+    acc = mfma4(x.w, y.w, acc);
+  }
+  return acc;
+}
+template <int K>
+__device__ __forceinline__ v4f mma_nn(v4f acc, const float* a, const float* b, int ldb, int brows) {
+  const int g = (threadIdx.x & 63) >> 4;
+  a += g * (K / 4);
+#pragma unroll
+  for (int s4 = 0; s4 < K / 16; ++s4) {
+    const float4 x = *reinterpret_cast<const float4*>(a + 4 * s4);
+    float y[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int k = g * (K / 4) + 4 * s4 + q;
+      k = k < brows ? k : brows - 1;
+      y[q] = b[static_cast<int64_t>(k) * ldb];
+    }
+    acc = mfma4(x.x, y[0], acc);
+    acc = mfma4(x.y, y[1], acc);
+    acc = mfma4(x.z, y[2], acc);
+    acc = mfma4(x.w, y[3], acc);
+  }
+  return acc;
+}
+template <int K>
+__device__ __forceinline__ v4f mma_tn(v4f acc, const float* a, int lda, const float* b, int ldb,
+                                      int brows) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int s = 0; s < K / 4; ++s) {
+    const int k = g * (K / 4) + s;
+    const int kb = k < brows ? k : brows - 1;
+    acc = mfma4(a[k * lda], b[static_cast<int64_t>(kb) * ldb], acc);
+  }
+  return acc;
+}
+
+// E = P^T dO on the matrix cores.
+template <int C>
+__global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
+  constexpr int D = 128, S1 = D + 4, S2 = C + 4;
+  static_assert(C == 64, "tiling assumes C = 64");
+  __shared__ __attribute__((aligned(16))) float lds[2 * C * S1];  // Q | K, then dO^T | P^T
+  __shared__ float sG[C];
+  float* sQ = lds;
+  float* sK = lds + C * S1;
+  float* dOT = lds;            // [D][S2]
+  float* PT = lds + D * S2;    // [C][S2]
+  static_assert(D * S2 + C * S2 <= 2 * C * S1, "LDS reuse");
+  int64_t slot, tok0;
+  int L;
+  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  const int64_t sh = slot * io.H_v + h;
+  const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
+  for (int e = tid; e < C * (D / 4); e += 256) {
+    const int p = e / (D / 4), i4 = e % (D / 4);
+    const int pc = p < L ? p : L - 1;
+    const float4 k4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
+    const float4 q4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
+    const float4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    *reinterpret_cast<float4*>(sK + p * S1 + 4 * i4) = p < L ? k4 : z;
+    *reinterpret_cast<float4*>(sQ + p * S1 + 4 * i4) = p < L ? q4 : z;
+  }
+  if (tid < C) sG[tid] = io.G[sh * C + tid];
+  __syncthreads();
+  float P[4][4];  // rows p = 16 w + 4 g + r, columns r' = 16 nb + l16
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (nb <= w) acc = mma_nt<D>(acc, sQ + (16 * w + l16) * S1, sK + (16 * nb + l16) * S1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * w + 4 * g + r, qq = 16 * nb + l16;
+      const float x = acc[r] * expf(sG[pp] - sG[qq]);
+      P[nb][r] = (nb <= w && qq <= pp && pp < L) ? x : 0.0f;
+    }
+  }
+  __syncthreads();  // Q and K are dead
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) PT[(16 * nb + l16) * S2 + 16 * w + 4 * g + r] = P[nb][r];
+  const float* dO = io.dO + (tok0 * io.H_v + h) * D;
+  for (int e = tid; e < C * D; e += 256) {
+    const int p = e / D, j = e % D;
+    const int pc = p < L ? p : L - 1;
+    const float x = dO[static_cast<int64_t>(pc) * io.H_v * D + j];
+    dOT[j * S2 + p] = p < L ? x : 0.0f;
+  }
+  __syncthreads();
+  float* E = io.E + sh * static_cast<int64_t>(C) * D;
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = mma_nt<C>(acc, PT + (16 * w + l16) * S2, dOT + (16 * nb + l16) * S2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) E[(16 * w + 4 * g + r) * D + 16 * nb + l16] = acc[r];
+  }
+}
+
+// The three state products of a chunk on the matrix cores:
+// out[p][i] = sum_j Y[p][j] X[i][j]  for (X, Y) = (S, dO), (S, dDelta), (dS', Delta).
+template <int C>
+__global__ __launch_bounds__(256) void k_bwd_mm_m(BwdIO io) {
+  constexpr int D = 128, S1 = D + 4;
+  static_assert(C == 64, "tiling assumes C = 64");
+  __shared__ __attribute__((aligned(16))) float sY[C * S1];
+  __shared__ __attribute__((aligned(16))) float sX[D * S1];
+  int64_t slot, tok0;
+  int L;
+  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y;
+  const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
+  const int64_t sh = slot * io.H_v + h;
+  for (int prod = 0; prod < 3; ++prod) {
+    if (prod != 1) {
+      const float* X = (prod == 0 ? io.states : io.dstates) + sh * DD;
+      for (int e = tid; e < D * (D / 4); e += 256) {
+        const int i = e / (D / 4), j4 = e % (D / 4);
+        *reinterpret_cast<float4*>(sX + i * S1 + 4 * j4) = *reinterpret_cast<const float4*>(X + i * D + 4 * j4);
+      }
+    }
+    for (int e = tid; e < C * (D / 4); e += 256) {
+      const int p = e / (D / 4), j4 = e % (D / 4);
+      const int pc = p < L ? p : L - 1;
+      const float* src = prod == 0 ? io.dO + ((tok0 + pc) * io.H_v + h) * D
+                                   : (prod == 1 ? io.dD : io.Dl) + sh * CD + pc * D;
+      const float4 y = *reinterpret_cast<const float4*>(src + 4 * j4);
+      *reinterpret_cast<float4*>(sY + p * S1 + 4 * j4) = p < L ? y : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    __syncthreads();
+    float* out = (prod == 0 ? io.SdO : prod == 1 ? io.SdD : io.DsD) + sh * CD;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int nb = 2 * w + ib;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mma_nt<D>(acc, sY + (16 * mb + l16) * S1, sX + (16 * nb + l16) * S1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[(16 * mb + 4 * g + r) * D + 16 * nb + l16] = acc[r];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Reverse scan of the state gradient on the matrix cores, per (sequence,
+// head, 32-row tile of d_v):  dDelta = E + diag(lam) K dS'^T  and
+// dS = gam_last dS' + (gam dO)^T Q - dDelta^T W.
+template <int C>
+__global__ __launch_bounds__(256) void k_bwd_scan_m(BwdIO io, int64_t nblocks, int64_t nb8) {
+  constexpr int D = 128, TILE = 32, NTILE = D / TILE, S1 = D + 4, S2 = C + 4;
+  static_assert(C == 64, "tiling assumes C = 64");
+  __shared__ __attribute__((aligned(16))) float sS[TILE * S1];   // dS' rows j, columns i
+  __shared__ __attribute__((aligned(16))) float sDt[TILE * S2];  // -dDelta^T [j][p]
+  __shared__ __attribute__((aligned(16))) float sOt[TILE * S2];  // (gam dO)^T [j][p]
+  __shared__ float sG[C], sLam[C];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t vb = xcd_block(nb8);
+  if (vb >= nblocks) return;
+  const int tile = static_cast<int>(vb % NTILE);
+  const int h = static_cast<int>((vb / NTILE) % io.H_v);
+  const int n = static_cast<int>(vb / (NTILE * io.H_v));
+  if (n >= io.N) return;
+  const int hq = h / (io.H_v / io.H_qk);
+  const int j0 = tile * TILE;
+  const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
+  const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
+  const int64_t s0 = io.cu[n];
+  const int64_t Lseq = static_cast<int64_t>(io.cu[n + 1]) - s0;
+  if (Lseq < 0 || s0 < 0 || s0 + Lseq > io.T) return;
+  const int64_t nchunks = (Lseq + C - 1) / C;
+  const int64_t slot0 = io.cu_chunks[n];
+  if (slot0 + nchunks > io.max_state_slot) return;
+
+  for (int e = tid; e < TILE * D; e += 256) {
+    const int i = e / TILE, jj = e % TILE;
+    sS[jj * S1 + i] = io.dhT ? io.dhT[nh * DD + static_cast<int64_t>(i) * D + j0 + jj] : 0.0f;
+  }
+  __syncthreads();
+  v4f accS[2][2];  // rows j = 16 jb + 4 g + r, columns i = 32 w + 16 ib + l16
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accS[jb][ib][r] = sS[(16 * jb + 4 * g + r) * S1 + 32 * w + 16 * ib + l16];
+
+  for (int64_t c = nchunks - 1; c >= 0; --c) {
+    const int64_t slot = slot0 + c;
+    const int64_t sh = slot * io.H_v + h;
+    const int64_t tok0 = s0 + c * C;
+    const int rows = static_cast<int>(Lseq - c * C < C ? Lseq - c * C : C);
+    float* dst = io.dstates + sh * DD;
+    for (int e = tid; e < TILE * D; e += 256) {
+      const int i = e / TILE, jj = e % TILE;
+      dst[static_cast<int64_t>(i) * D + j0 + jj] = sS[jj * S1 + i];
+    }
+    if (tid < C) sG[tid] = io.G[sh * C + tid];
+    const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
+    __syncthreads();
+    const float glast = sG[C - 1];
+    if (tid < C) sLam[tid] = expf(glast - sG[tid]);
+    for (int e = tid; e < C * TILE; e += 256) {
+      const int p = e / TILE, jj = e % TILE;
+      const int pc = p < rows ? p : rows - 1;
+      const float x = expf(sG[p]) * io.dO[((tok0 + pc) * io.H_v + h) * D + j0 + jj];
+      sOt[jj * S2 + p] = p < rows ? x : 0.0f;
+    }
+    // dDelta rows p = 16 w + 4 g + r, columns j = 16 jb + l16
+    const int pc = 16 * w + l16 < rows ? 16 * w + l16 : rows - 1;
+    const float* Ec = io.E + sh * CD;
+    v4f accD[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      accD[jb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      accD[jb] = mma_nt<D>(accD[jb], kq + pc * 2 * D, sS + (16 * jb + l16) * S1);
+    }
+    __syncthreads();  // sLam ready; sS reads done
+    float* dDc = io.dD + sh * CD;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      v4f x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * w + 4 * g + r;
+        const float e = Ec[p * D + j0 + 16 * jb + l16];
+        const float v = fmaf(sLam[p], accD[jb][r], e);
+        x[r] = p < rows ? v : 0.0f;
+        dDc[p * D + j0 + 16 * jb + l16] = x[r];
+      }
+      *reinterpret_cast<v4f*>(sDt + (16 * jb + l16) * S2 + 16 * w + 4 * g) = -x;
+    }
+    __syncthreads();
+    const float gl = expf(glast);
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        v4f acc = gl * accS[jb][ib];
+        const int col = 32 * w + 16 * ib + l16;
+        acc = mma_nn<C>(acc, sOt + (16 * jb + l16) * S2, kq + D + col, 2 * D, rows);
+        acc = mma_nn<C>(acc, sDt + (16 * jb + l16) * S2, io.W + sh * CD + col, D, C);
+        accS[jb][ib] = acc;
+      }
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sS[(16 * jb + 4 * g + r) * S1 + 32 * w + 16 * ib + l16] = accS[jb][ib][r];
+    __syncthreads();
+  }
+  for (int e = tid; e < TILE * D; e += 256) {
+    const int i = e / TILE, jj = e % TILE;
+    io.dh0[nh * DD + static_cast<int64_t>(i) * D + j0 + jj] = sS[jj * S1 + i];
+  }
+}
+
+// Per chunk and value head, on the matrix cores: gradients of q-hat, k-hat
+// (per value head), v, beta and g.
+template <int C, typename TIn>
+__global__ __launch_bounds__(256) void k_bwd_chunk_m(BwdIO io) {
+  constexpr int D = 128, CS = C + 4, YS = 2 * D + 4;
+  static_assert(C == 64, "tiling assumes C = 64");
+  __shared__ __attribute__((aligned(16))) float sQK[C * CS];  // QK, later F = E2 + E2^T
+  __shared__ __attribute__((aligned(16))) float sKK[C * CS];
+  __shared__ __attribute__((aligned(16))) float sZ[C * CS];   // Z, later dA
+  __shared__ __attribute__((aligned(16))) float sA[C * CS];
+  __shared__ __attribute__((aligned(16))) float sY[C * YS];   // [dX_w | dX_u]
+  __shared__ float sG[C], sB[C], sGam[C], sLam[C], sdG[C], sdB[C], skd[C], red[256];
+  int64_t slot, tok0;
+  int L;
+  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
+  const int64_t sh = slot * io.H_v + h;
+  const int64_t vs = static_cast<int64_t>(io.H_v) * D;  // token stride of dO / outputs
+  const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;  // K row p: kq + 2Dp
+  const float* dO = io.dO + (tok0 * io.H_v + h) * D;
+  const float* Dl = io.Dl + sh * CD;
+  const float* SdO = io.SdO + sh * CD;
+  const float* DsD = io.DsD + sh * CD;
+  const float* Wc = io.W + sh * CD;
+  const float* Uc = io.U + sh * CD;
+  auto crow = [&](int p) { return p < L ? p : L - 1; };
+
+  if (tid < C) {
+    sG[tid] = io.G[sh * C + tid];
+    const float bx = io.beta[(tok0 + crow(tid)) * io.H_v + h];
+    sB[tid] = tid < L ? bx : 0.0f;
+  }
+  {
+    const float* M = io.states + sh * DD;
+    const float* dM = io.dstates + sh * DD;
+    float part = 0.0f;
+    for (int e = tid; e < D * D; e += 256) part = fmaf(M[e], dM[e], part);
+    red[tid] = part;
+  }
+  __syncthreads();
+  const float glast = sG[C - 1];
+  if (tid < C) {
+    sGam[tid] = expf(sG[tid]);
+    sLam[tid] = expf(glast - sG[tid]);
+  }
+  for (int wd = 128; wd >= 1; wd >>= 1) {
+    if (tid < wd) red[tid] = red[tid] + red[tid + wd];
+    __syncthreads();
+  }
+  const float MdM = red[0];
+  // ---- C x C products: rows p = 16 w + 4 g + r, columns q = 16 nb + l16
+  {
+    const int pr = crow(16 * w + l16);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      v4f qk = {0.0f, 0.0f, 0.0f, 0.0f}, kk = qk, dp = qk;
+      if (nb <= w) {
+        const int qr = crow(16 * nb + l16);
+        qk = mma_nt<D>(qk, kq + pr * 2 * D + D, kq + qr * 2 * D);
+        kk = mma_nt<D>(kk, kq + pr * 2 * D, kq + qr * 2 * D);
+        dp = mma_nt<D>(dp, dO + pr * vs, Dl + (16 * nb + l16) * D);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * w + 4 * g + r, qq = 16 * nb + l16;
+        const float gam = expf(sG[pp] - sG[qq]);
+        const bool in = nb <= w && qq <= pp && pp < L;
+        const bool strict = in && qq < pp;
+        sQK[pp * CS + qq] = in ? qk[r] : 0.0f;
+        sZ[pp * CS + qq] = in ? dp[r] * gam : 0.0f;
+        sKK[pp * CS + qq] = strict ? kk[r] : 0.0f;
+        sA[pp * CS + qq] = strict ? sB[pp] * (kk[r] * gam) : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- dq-hat = gam SdO + Z K  and  dk-hat (partial) = lam DsD + Z^T Q
+  // wave w owns columns i = 32 w + 16 ib + l16, all four row blocks
+  v4f dk[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int col = 32 * w + 16 * ib + l16;
+      v4f aq, ak;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * mb + 4 * g + r;
+        aq[r] = sGam[pp] * SdO[pp * D + col];
+        ak[r] = sLam[pp] * DsD[pp * D + col];
+      }
+      aq = mma_nn<C>(aq, sZ + (16 * mb + l16) * CS, kq + col, 2 * D, L);
+      ak = mma_tn<C>(ak, sZ + 16 * mb + l16, CS, kq + D + col, 2 * D, L);
+      dk[mb][ib] = ak;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * mb + 4 * g + r;
+        if (pp < L) io.dqv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + col] = aq[r];
+      }
+    }
+  // ---- dG terms through O and the state update
+  if (tid < C) {
+    const int pp = tid, pc = crow(pp);
+    float qs = 0.0f, kd = 0.0f;
+    for (int i = 0; i < D; ++i) {
+      qs = fmaf(kq[pc * 2 * D + D + i], SdO[pp * D + i], qs);
+      kd = fmaf(kq[pc * 2 * D + i], DsD[pp * D + i], kd);
+    }
+    skd[pp] = pp < L ? kd : 0.0f;
+    float x = sGam[pp] * qs - sLam[pp] * kd;
+    for (int r = 0; r < pp; ++r) x = fmaf(sZ[pp * CS + r], sQK[pp * CS + r], x);
+    for (int q = pp + 1; q < C; ++q) x = fmaf(-sZ[q * CS + pp], sQK[q * CS + pp], x);
+    sdG[pp] = pp < L ? x : 0.0f;
+  }
+  __syncthreads();
+  if (tid == 0 && L > 0) {
+    float sacc = sGam[C - 1] * MdM;
+    for (int q = 0; q < L; ++q) sacc = fmaf(sLam[q], skd[q], sacc);
+    sdG[L - 1] = sdG[L - 1] + sacc;
+  }
+  // ---- back substitution (I + A)^T Y = [-SdD | dDelta], blocked by 16 rows from
+  // the bottom; wave w owns columns 64 w .. 64 w + 63 of Y (w < 2: dX_w, else dX_u)
+  {
+    const int col0 = 64 * w;
+    const float* rhs = w < 2 ? io.SdD + sh * CD + col0 : io.dD + sh * CD + (col0 - D);
+    const float sgn = w < 2 ? -1.0f : 1.0f;
+    v4f Y[4][4];
+#pragma unroll
+    for (int bi = 3; bi >= 0; --bi) {
+      v4f acc[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pp = 16 * bi + 4 * g + r;
+          const float x = sgn * rhs[pp * D + 16 * ct + l16];
+          acc[ct][r] = pp < L ? x : 0.0f;
+        }
+#pragma unroll
+      for (int bj = bi + 1; bj < 4; ++bj)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const float a = -sA[(16 * bj + 4 * g + s4) * CS + 16 * bi + l16];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[ct] = mfma4(a, Y[bj][ct][s4], acc[ct]);
+        }
+#pragma unroll
+      for (int pp = 15; pp >= 0; --pp) {
+        const int gp = pp >> 2, rp = pp & 3;
+        float a[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = sA[(16 * bi + pp) * CS + 16 * bi + 4 * g + r];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const float y = __shfl(acc[ct][rp], l16 + 16 * gp, 64);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float upd = fmaf(-a[r], y, acc[ct][r]);
+            acc[ct][r] = 4 * g + r < pp ? upd : acc[ct][r];
+          }
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        Y[bi][ct] = acc[ct];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sY[(16 * bi + 4 * g + r) * YS + col0 + 16 * ct + l16] = acc[ct][r];
+      }
+    }
+  }
+  __syncthreads();
+  // ---- dA = -(dX_w W^T + dX_u U^T), strictly lower; written over Z
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (nb <= w) {
+      acc = mma_nt<D>(acc, sY + (16 * w + l16) * YS, Wc + (16 * nb + l16) * D);
+      acc = mma_nt<D>(acc, sY + (16 * w + l16) * YS + D, Uc + (16 * nb + l16) * D);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * w + 4 * g + r, qq = 16 * nb + l16;
+      sZ[pp * CS + qq] = (nb <= w && qq < pp && pp < L) ? -acc[r] : 0.0f;
+    }
+  }
+  __syncthreads();
+  // ---- dbeta, remaining dG terms, and F = E2 + E2^T with E2_pr = dA_pr beta_p Gam_pr
+  if (tid < C) {
+    const int pp = tid, pc = crow(pp);
+    const TIn* vin = static_cast<const TIn*>(io.v) + (tok0 + pc) * vs + static_cast<int64_t>(h) * D;
+    float xk = 0.0f, uv = 0.0f;
+    for (int i = 0; i < D; ++i) {
+      xk = fmaf(sY[pp * YS + i], kq[pc * 2 * D + i], xk);
+      uv = fmaf(sY[pp * YS + D + i], ldin(vin + i), uv);
+    }
+    float db = sGam[pp] * xk + uv;
+    float dgp = fmaf(sB[pp] * sGam[pp], xk, sdG[pp]);
+    for (int r = 0; r < pp; ++r) {
+      db = fmaf(sZ[pp * CS + r], sKK[pp * CS + r] * expf(sG[pp] - sG[r]), db);
+      dgp = fmaf(sZ[pp * CS + r], sA[pp * CS + r], dgp);
+    }
+    for (int q = pp + 1; q < C; ++q) dgp = fmaf(-sZ[q * CS + pp], sA[q * CS + pp], dgp);
+    sdB[pp] = pp < L ? db : 0.0f;
+    sdG[pp] = pp < L ? dgp : 0.0f;
+  }
+  for (int e = tid; e < C * C; e += 256) {
+    const int pp = e / C, q = e % C;
+    float f = 0.0f;
+    if (q < pp) f = sZ[pp * CS + q] * sB[pp] * expf(sG[pp] - sG[q]);
+    else if (q > pp) f = sZ[q * CS + pp] * sB[q] * expf(sG[q] - sG[pp]);
+    sQK[pp * CS + q] = f;
+  }
+  __syncthreads();
+  // ---- dk-hat += beta gam dX_w + F K ; dv = beta dX_u
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int col = 32 * w + 16 * ib + l16;
+      v4f ak = dk[mb][ib];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * mb + 4 * g + r;
+        ak[r] = fmaf(sB[pp] * sGam[pp], sY[pp * YS + col], ak[r]);
+      }
+      ak = mma_nn<C>(ak, sQK + (16 * mb + l16) * CS, kq + col, 2 * D, L);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * mb + 4 * g + r;
+        if (pp < L) io.dkv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + col] = ak[r];
+      }
+    }
+  for (int e = tid; e < C * D; e += 256) {
+    const int pp = e / D, j = e % D;
+    if (pp < L) io.dv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + j] = sB[pp] * sY[pp * YS + D + j];
+  }
+  if (tid == 0) {
+    float acc = 0.0f;
+    for (int pp = L - 1; pp >= 0; --pp) {
+      acc = acc + sdG[pp];
+      io.dg[(tok0 + pp) * io.H_v + h] = acc;
+      io.dbeta[(tok0 + pp) * io.H_v + h] = sdB[pp];
+    }
+  }
+}
+
 // Sum over the value heads of each group (ascending head order), then the L2
 // norm backward: dx = s r (dxh - n (n . dxh)), n = x r, r = (sum x^2 + eps)^-1/2.
 template <int D, typename TIn>
@@ -1847,21 +2386,36 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   const dim3 cgrid(static_cast<unsigned>(cnt.chunks > 0 ? cnt.chunks : 1), s->H_v);
   if (cnt.chunks > 0) {
     Timed t_("k_bwd_prep", st);
-    hipLaunchKernelGGL((k_bwd_prep<D, C>), cgrid, dim3(256), 0, st, b);
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((k_bwd_prep_m<C>), cgrid, dim3(256), 0, st, b);
+    else
+      hipLaunchKernelGGL((k_bwd_prep<D, C>), cgrid, dim3(256), 0, st, b);
   }
   if (sblocks > 0) {
     Timed t_("k_bwd_scan", st);
-    hipLaunchKernelGGL((k_bwd_scan<D, C, TILE>), dim3(static_cast<unsigned>(sblocks)), dim3(256),
-                       0, st, b);
+    if constexpr (D == 128) {
+      const int64_t nb8 = (sblocks + 7) / 8 * 8;
+      hipLaunchKernelGGL((k_bwd_scan_m<C>), dim3(static_cast<unsigned>(nb8)), dim3(256), 0, st, b,
+                         sblocks, nb8);
+    } else {
+      hipLaunchKernelGGL((k_bwd_scan<D, C, TILE>), dim3(static_cast<unsigned>(sblocks)),
+                         dim3(256), 0, st, b);
+    }
   }
   if (cnt.chunks > 0) {
     {
       Timed t_("k_bwd_mm", st);
-      hipLaunchKernelGGL((k_bwd_mm<D, C>), cgrid, dim3(256), 0, st, b);
+      if constexpr (D == 128)
+        hipLaunchKernelGGL((k_bwd_mm_m<C>), cgrid, dim3(256), 0, st, b);
+      else
+        hipLaunchKernelGGL((k_bwd_mm<D, C>), cgrid, dim3(256), 0, st, b);
     }
     {
       Timed t_("k_bwd_chunk", st);
-      hipLaunchKernelGGL((k_bwd_chunk<D, C, TIn>), cgrid, dim3(256), 0, st, b);
+      if constexpr (D == 128)
+        hipLaunchKernelGGL((k_bwd_chunk_m<C, TIn>), cgrid, dim3(256), 0, st, b);
+      else
+        hipLaunchKernelGGL((k_bwd_chunk<D, C, TIn>), cgrid, dim3(256), 0, st, b);
     }
   }
   if (nvec > 0) {
