@@ -1122,6 +1122,7 @@ struct BwdIO {
   float* SdO;             // [slot][H_v][C][D] S^T dO_p
   float* DsD;             // [slot][H_v][C][D] dS'^T Delta_p
   float* SdD;             // [slot][H_v][C][D] S^T dDelta_p, then dX_w
+  float* MdM;             // [slot][H_v] <S, dS'> of each chunk (matrix-core path)
   float* dqv;             // [T][H_v][D] per value head
   float* dkv;             // [T][H_v][D]
   float* dv;              // [T][H_v][D]
@@ -1654,12 +1655,12 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
 
 // The three state products of a chunk on the matrix cores:
 // out[p][i] = sum_j Y[p][j] X[i][j]  for (X, Y) = (S, dO), (S, dDelta), (dS', Delta).
+// Y is staged in LDS; X rows are read from L2, each feeding four 16-row tiles.
 template <int C>
 __global__ __launch_bounds__(256) void k_bwd_mm_m(BwdIO io) {
   constexpr int D = 128, S1 = D + 4;
   static_assert(C == 64, "tiling assumes C = 64");
   __shared__ __attribute__((aligned(16))) float sY[C * S1];
-  __shared__ __attribute__((aligned(16))) float sX[D * S1];
   int64_t slot, tok0;
   int L;
   if (!bwd_item<C>(io, slot, tok0, L)) return;
@@ -1669,13 +1670,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm_m(BwdIO io) {
   const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
   const int64_t sh = slot * io.H_v + h;
   for (int prod = 0; prod < 3; ++prod) {
-    if (prod != 1) {
-      const float* X = (prod == 0 ? io.states : io.dstates) + sh * DD;
-      for (int e = tid; e < D * (D / 4); e += 256) {
-        const int i = e / (D / 4), j4 = e % (D / 4);
-        *reinterpret_cast<float4*>(sX + i * S1 + 4 * j4) = *reinterpret_cast<const float4*>(X + i * D + 4 * j4);
-      }
-    }
+    const float* X = (prod == 2 ? io.dstates : io.states) + sh * DD;
     for (int e = tid; e < C * (D / 4); e += 256) {
       const int p = e / (D / 4), j4 = e % (D / 4);
       const int pc = p < L ? p : L - 1;
@@ -1686,16 +1681,48 @@ __global__ __launch_bounds__(256) void k_bwd_mm_m(BwdIO io) {
     }
     __syncthreads();
     float* out = (prod == 0 ? io.SdO : prod == 1 ? io.SdD : io.DsD) + sh * CD;
-#pragma unroll
+    float mdm = 0.0f;  // product 2: this lane's part of <S, dS'> (rows it streams)
+#pragma unroll 1
     for (int ib = 0; ib < 2; ++ib) {
       const int nb = 2 * w + ib;
+      const float* xb = X + (16 * nb + l16) * D + g * (D / 4);
+      const float* sb = io.states + sh * DD + (16 * nb + l16) * D + g * (D / 4);
+      v4f acc[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = mma_nt<D>(acc, sY + (16 * mb + l16) * S1, sX + (16 * nb + l16) * S1);
+      for (int mb = 0; mb < 4; ++mb) acc[mb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+      for (int s4 = 0; s4 < D / 16; ++s4) {
+        const float4 y = *reinterpret_cast<const float4*>(xb + 4 * s4);
+        if (prod == 2) {
+          const float4 m = *reinterpret_cast<const float4*>(sb + 4 * s4);
+          mdm = fmaf(m.x, y.x, mdm);
+          mdm = fmaf(m.y, y.y, mdm);
+          mdm = fmaf(m.z, y.z, mdm);
+          mdm = fmaf(m.w, y.w, mdm);
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[(16 * mb + 4 * g + r) * D + 16 * nb + l16] = acc[r];
+        for (int mb = 0; mb < 4; ++mb) {
+          const float4 x = *reinterpret_cast<const float4*>(sY + (16 * mb + l16) * S1 + g * (D / 4) + 4 * s4);
+          acc[mb] = mfma4(x.x, y.x, acc[mb]);
+          acc[mb] = mfma4(x.y, y.y, acc[mb]);
+          acc[mb] = mfma4(x.z, y.z, acc[mb]);
+          acc[mb] = mfma4(x.w, y.w, acc[mb]);
+        }
       }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[(16 * mb + 4 * g + r) * D + 16 * nb + l16] = acc[mb][r];
+    }
+    if (prod == 2) {  // fixed-order block reduction of <S, dS'>
+      __syncthreads();  // every wave is done reading sY
+      sY[tid] = mdm;
+      __syncthreads();
+      for (int wd = 128; wd >= 1; wd >>= 1) {
+        if (tid < wd) sY[tid] = sY[tid] + sY[tid + wd];
+        __syncthreads();
+      }
+      if (tid == 0) io.MdM[sh] = sY[0];
     }
     __syncthreads();
   }
@@ -1816,47 +1843,72 @@ __global__ __launch_bounds__(256) void k_bwd_scan_m(BwdIO io, int64_t nblocks, i
   }
 }
 
+// Sum of a value over the 4 lanes of a quad (lanes 4k .. 4k+3 of a wave) as
+// (x0 + x1) + (x2 + x3); additions commute, so all four lanes get the same bits.
+__device__ __forceinline__ float quad_sum(float x) {
+  x = x + __shfl_xor(x, 1, 64);
+  return x + __shfl_xor(x, 2, 64);
+}
+
+// Sum of a value over the 8 lanes of an octet (lanes 8k .. 8k+7 of a wave) as
+// a butterfly; additions commute, so all eight lanes get the same bits.
+__device__ __forceinline__ float oct_sum(float x) {
+  x = x + __shfl_xor(x, 1, 64);
+  x = x + __shfl_xor(x, 2, 64);
+  return x + __shfl_xor(x, 4, 64);
+}
+
 // Per chunk and value head, on the matrix cores: gradients of q-hat, k-hat
-// (per value head), v, beta and g.
+// (per value head), v, beta and g.  Eight waves (two per SIMD) share the LDS
+// tiles; row reductions use 8 lanes per row.
 template <int C, typename TIn>
-__global__ __launch_bounds__(256) void k_bwd_chunk_m(BwdIO io) {
-  constexpr int D = 128, CS = C + 4, YS = 2 * D + 4;
+__global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
+  constexpr int D = 128, CS = C + 4, KS = D + 4, YS = 2 * D + 4;
   static_assert(C == 64, "tiling assumes C = 64");
-  __shared__ __attribute__((aligned(16))) float sQK[C * CS];  // QK, later F = E2 + E2^T
-  __shared__ __attribute__((aligned(16))) float sKK[C * CS];
-  __shared__ __attribute__((aligned(16))) float sZ[C * CS];   // Z, later dA
-  __shared__ __attribute__((aligned(16))) float sA[C * CS];
-  __shared__ __attribute__((aligned(16))) float sY[C * YS];   // [dX_w | dX_u]
-  __shared__ float sG[C], sB[C], sGam[C], sLam[C], sdG[C], sdB[C], skd[C], red[256];
+  __shared__ __attribute__((aligned(16))) float sQK[C * CS];   // QK, later F = E2 + E2^T
+  __shared__ __attribute__((aligned(16))) float sKG[C * CS];   // (k_p . k_r) Gam_pr, r < p
+  __shared__ __attribute__((aligned(16))) float sZ[C * CS];    // Z, later dA
+  __shared__ __attribute__((aligned(16))) float sK[C * KS];
+  __shared__ __attribute__((aligned(16))) float sY[2 * C * KS];  // dO | Delta, then Q, then Y
+  __shared__ float sG[C], sB[C], sGam[C], sLam[C], sdG[C], sdB[C], skd[C];
+  static_assert(C * YS <= 2 * C * KS, "Y must fit");
+  float* sO = sY;
+  float* sD = sY + C * KS;
+  float* sQ = sY;
   int64_t slot, tok0;
   int L;
   if (!bwd_item<C>(io, slot, tok0, L)) return;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
   const int h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
-  const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
+  const int64_t CD = static_cast<int64_t>(C) * D;
   const int64_t sh = slot * io.H_v + h;
-  const int64_t vs = static_cast<int64_t>(io.H_v) * D;  // token stride of dO / outputs
-  const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;  // K row p: kq + 2Dp
+  const int64_t vs = static_cast<int64_t>(io.H_v) * D;
+  const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
   const float* dO = io.dO + (tok0 * io.H_v + h) * D;
   const float* Dl = io.Dl + sh * CD;
   const float* SdO = io.SdO + sh * CD;
   const float* DsD = io.DsD + sh * CD;
   const float* Wc = io.W + sh * CD;
   const float* Uc = io.U + sh * CD;
+  const float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
   auto crow = [&](int p) { return p < L ? p : L - 1; };
+  // C x C tiles of wave w: row block mb = w / 2, column blocks nb = w % 2 and w % 2 + 2
+  const int tmb = w >> 1, tnb0 = w & 1;
 
   if (tid < C) {
     sG[tid] = io.G[sh * C + tid];
     const float bx = io.beta[(tok0 + crow(tid)) * io.H_v + h];
     sB[tid] = tid < L ? bx : 0.0f;
   }
-  {
-    const float* M = io.states + sh * DD;
-    const float* dM = io.dstates + sh * DD;
-    float part = 0.0f;
-    for (int e = tid; e < D * D; e += 256) part = fmaf(M[e], dM[e], part);
-    red[tid] = part;
+  for (int e = tid; e < C * (D / 4); e += 512) {
+    const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
+    const float4 k4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
+    const float4 o4 = *reinterpret_cast<const float4*>(dO + pc * vs + 4 * i4);
+    const float4 d4 = *reinterpret_cast<const float4*>(Dl + p * D + 4 * i4);
+    *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) = p < L ? k4 : z4;
+    *reinterpret_cast<float4*>(sO + p * KS + 4 * i4) = p < L ? o4 : z4;
+    *reinterpret_cast<float4*>(sD + p * KS + 4 * i4) = p < L ? d4 : z4;
   }
   __syncthreads();
   const float glast = sG[C - 1];
@@ -1864,93 +1916,108 @@ __global__ __launch_bounds__(256) void k_bwd_chunk_m(BwdIO io) {
     sGam[tid] = expf(sG[tid]);
     sLam[tid] = expf(glast - sG[tid]);
   }
-  for (int wd = 128; wd >= 1; wd >>= 1) {
-    if (tid < wd) red[tid] = red[tid] + red[tid + wd];
-    __syncthreads();
+  const float MdM = io.MdM[sh];
+  // ---- Z = (dO Delta^T) . Gam, masked r <= p
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int nb = tnb0 + 2 * t;
+    v4f dp = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (nb <= tmb) dp = mma_nt<D>(dp, sO + (16 * tmb + l16) * KS, sD + (16 * nb + l16) * KS);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * tmb + 4 * g + r, qq = 16 * nb + l16;
+      const float gam = expf(sG[pp] - sG[qq]);
+      sZ[pp * CS + qq] = (nb <= tmb && qq <= pp && pp < L) ? dp[r] * gam : 0.0f;
+    }
   }
-  const float MdM = red[0];
-  // ---- C x C products: rows p = 16 w + 4 g + r, columns q = 16 nb + l16
+  __syncthreads();  // dO and Delta are dead
+  for (int e = tid; e < C * (D / 4); e += 512) {
+    const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
+    const float4 q4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
+    *reinterpret_cast<float4*>(sQ + p * KS + 4 * i4) = p < L ? q4 : z4;
+  }
+  __syncthreads();
+  // ---- QK (r <= p) and KK Gam (r < p)
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int nb = tnb0 + 2 * t;
+    v4f qk = {0.0f, 0.0f, 0.0f, 0.0f}, kk = qk;
+    if (nb <= tmb) {
+      qk = mma_nt<D>(qk, sQ + (16 * tmb + l16) * KS, sK + (16 * nb + l16) * KS);
+      kk = mma_nt<D>(kk, sK + (16 * tmb + l16) * KS, sK + (16 * nb + l16) * KS);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * tmb + 4 * g + r, qq = 16 * nb + l16;
+      const float gam = expf(sG[pp] - sG[qq]);
+      const bool in = nb <= tmb && qq <= pp && pp < L;
+      sQK[pp * CS + qq] = in ? qk[r] : 0.0f;
+      sKG[pp * CS + qq] = (in && qq < pp) ? kk[r] * gam : 0.0f;
+    }
+  }
+  __syncthreads();
+  // ---- dq-hat = gam SdO + Z K  and  dk-hat (partial) = lam DsD + Z^T Q; wave w
+  // owns columns i = 16 w + l16, all four row blocks
+  const int col = 16 * w + l16;
+  v4f dk[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    v4f aq, ak;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * mb + 4 * g + r;
+      aq[r] = sGam[pp] * SdO[pp * D + col];
+      ak[r] = sLam[pp] * DsD[pp * D + col];
+    }
+    aq = mma_nn<C>(aq, sZ + (16 * mb + l16) * CS, sK + col, KS, C);
+    ak = mma_tn<C>(ak, sZ + 16 * mb + l16, CS, sQ + col, KS, C);
+    dk[mb] = ak;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * mb + 4 * g + r;
+      if (pp < L) io.dqv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + col] = aq[r];
+    }
+  }
+  // ---- dG terms through O and the state update (8 lanes per row)
   {
-    const int pr = crow(16 * w + l16);
+    const int pp = tid >> 3, part = tid & 7;
+    float qs = 0.0f, kd = 0.0f, zq = 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      v4f qk = {0.0f, 0.0f, 0.0f, 0.0f}, kk = qk, dp = qk;
-      if (nb <= w) {
-        const int qr = crow(16 * nb + l16);
-        qk = mma_nt<D>(qk, kq + pr * 2 * D + D, kq + qr * 2 * D);
-        kk = mma_nt<D>(kk, kq + pr * 2 * D, kq + qr * 2 * D);
-        dp = mma_nt<D>(dp, dO + pr * vs, Dl + (16 * nb + l16) * D);
-      }
+    for (int i = 16 * part; i < 16 * part + 16; ++i) {
+      qs = fmaf(sQ[pp * KS + i], SdO[pp * D + i], qs);
+      kd = fmaf(sK[pp * KS + i], DsD[pp * D + i], kd);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * w + 4 * g + r, qq = 16 * nb + l16;
-        const float gam = expf(sG[pp] - sG[qq]);
-        const bool in = nb <= w && qq <= pp && pp < L;
-        const bool strict = in && qq < pp;
-        sQK[pp * CS + qq] = in ? qk[r] : 0.0f;
-        sZ[pp * CS + qq] = in ? dp[r] * gam : 0.0f;
-        sKK[pp * CS + qq] = strict ? kk[r] : 0.0f;
-        sA[pp * CS + qq] = strict ? sB[pp] * (kk[r] * gam) : 0.0f;
-      }
+    for (int r = 8 * part; r < 8 * part + 8; ++r) {
+      if (r < pp) zq = fmaf(sZ[pp * CS + r], sQK[pp * CS + r], zq);
+      else if (r > pp) zq = fmaf(-sZ[r * CS + pp], sQK[r * CS + pp], zq);
+    }
+    qs = oct_sum(qs);
+    kd = oct_sum(kd);
+    zq = oct_sum(zq);
+    if (part == 0) {
+      skd[pp] = pp < L ? kd : 0.0f;
+      sdG[pp] = pp < L ? (sGam[pp] * qs - sLam[pp] * kd) + zq : 0.0f;
     }
   }
-  __syncthreads();
-  // ---- dq-hat = gam SdO + Z K  and  dk-hat (partial) = lam DsD + Z^T Q
-  // wave w owns columns i = 32 w + 16 ib + l16, all four row blocks
-  v4f dk[4][2];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      const int col = 32 * w + 16 * ib + l16;
-      v4f aq, ak;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * mb + 4 * g + r;
-        aq[r] = sGam[pp] * SdO[pp * D + col];
-        ak[r] = sLam[pp] * DsD[pp * D + col];
-      }
-      aq = mma_nn<C>(aq, sZ + (16 * mb + l16) * CS, kq + col, 2 * D, L);
-      ak = mma_tn<C>(ak, sZ + 16 * mb + l16, CS, kq + D + col, 2 * D, L);
-      dk[mb][ib] = ak;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * mb + 4 * g + r;
-        if (pp < L) io.dqv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + col] = aq[r];
-      }
-    }
-  // ---- dG terms through O and the state update
-  if (tid < C) {
-    const int pp = tid, pc = crow(pp);
-    float qs = 0.0f, kd = 0.0f;
-    for (int i = 0; i < D; ++i) {
-      qs = fmaf(kq[pc * 2 * D + D + i], SdO[pp * D + i], qs);
-      kd = fmaf(kq[pc * 2 * D + i], DsD[pp * D + i], kd);
-    }
-    skd[pp] = pp < L ? kd : 0.0f;
-    float x = sGam[pp] * qs - sLam[pp] * kd;
-    for (int r = 0; r < pp; ++r) x = fmaf(sZ[pp * CS + r], sQK[pp * CS + r], x);
-    for (int q = pp + 1; q < C; ++q) x = fmaf(-sZ[q * CS + pp], sQK[q * CS + pp], x);
-    sdG[pp] = pp < L ? x : 0.0f;
-  }
-  __syncthreads();
-  if (tid == 0 && L > 0) {
+  __syncthreads();  // Q, QK, Z reads done; Y may overwrite Q
+  if (tid == 0) {
     float sacc = sGam[C - 1] * MdM;
     for (int q = 0; q < L; ++q) sacc = fmaf(sLam[q], skd[q], sacc);
     sdG[L - 1] = sdG[L - 1] + sacc;
   }
-  // ---- back substitution (I + A)^T Y = [-SdD | dDelta], blocked by 16 rows from
-  // the bottom; wave w owns columns 64 w .. 64 w + 63 of Y (w < 2: dX_w, else dX_u)
+  // ---- back substitution (I + A)^T Y = [-SdD | dDelta], A_pr = beta_p KG_pr,
+  // blocked by 16 rows from the bottom; wave w owns columns 32 w .. 32 w + 31
   {
-    const int col0 = 64 * w;
-    const float* rhs = w < 2 ? io.SdD + sh * CD + col0 : io.dD + sh * CD + (col0 - D);
-    const float sgn = w < 2 ? -1.0f : 1.0f;
-    v4f Y[4][4];
+    const int col0 = 32 * w;
+    const float* rhs = w < 4 ? io.SdD + sh * CD + col0 : io.dD + sh * CD + (col0 - D);
+    const float sgn = w < 4 ? -1.0f : 1.0f;
+    v4f Y[4][2];
 #pragma unroll
     for (int bi = 3; bi >= 0; --bi) {
-      v4f acc[4];
+      v4f acc[2];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int pp = 16 * bi + 4 * g + r;
@@ -1961,18 +2028,20 @@ __global__ __launch_bounds__(256) void k_bwd_chunk_m(BwdIO io) {
       for (int bj = bi + 1; bj < 4; ++bj)
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          const float a = -sA[(16 * bj + 4 * g + s4) * CS + 16 * bi + l16];
+          const int rr = 16 * bj + 4 * g + s4;
+          const float a = -(sB[rr] * sKG[rr * CS + 16 * bi + l16]);
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) acc[ct] = mfma4(a, Y[bj][ct][s4], acc[ct]);
+          for (int ct = 0; ct < 2; ++ct) acc[ct] = mfma4(a, Y[bj][ct][s4], acc[ct]);
         }
 #pragma unroll
       for (int pp = 15; pp >= 0; --pp) {
         const int gp = pp >> 2, rp = pp & 3;
+        const int prow = 16 * bi + pp;
         float a[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = sA[(16 * bi + pp) * CS + 16 * bi + 4 * g + r];
+        for (int r = 0; r < 4; ++r) a[r] = sB[prow] * sKG[prow * CS + 16 * bi + 4 * g + r];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int ct = 0; ct < 2; ++ct) {
           const float y = __shfl(acc[ct][rp], l16 + 16 * gp, 64);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -1982,7 +2051,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk_m(BwdIO io) {
         }
       }
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < 2; ++ct) {
         Y[bi][ct] = acc[ct];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sY[(16 * bi + 4 * g + r) * YS + col0 + 16 * ct + l16] = acc[ct][r];
@@ -1992,66 +2061,74 @@ __global__ __launch_bounds__(256) void k_bwd_chunk_m(BwdIO io) {
   __syncthreads();
   // ---- dA = -(dX_w W^T + dX_u U^T), strictly lower; written over Z
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int t = 0; t < 2; ++t) {
+    const int nb = tnb0 + 2 * t;
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (nb <= w) {
-      acc = mma_nt<D>(acc, sY + (16 * w + l16) * YS, Wc + (16 * nb + l16) * D);
-      acc = mma_nt<D>(acc, sY + (16 * w + l16) * YS + D, Uc + (16 * nb + l16) * D);
+    if (nb <= tmb) {
+      acc = mma_nt<D>(acc, sY + (16 * tmb + l16) * YS, Wc + (16 * nb + l16) * D);
+      acc = mma_nt<D>(acc, sY + (16 * tmb + l16) * YS + D, Uc + (16 * nb + l16) * D);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int pp = 16 * w + 4 * g + r, qq = 16 * nb + l16;
-      sZ[pp * CS + qq] = (nb <= w && qq < pp && pp < L) ? -acc[r] : 0.0f;
+      const int pp = 16 * tmb + 4 * g + r, qq = 16 * nb + l16;
+      sZ[pp * CS + qq] = (nb <= tmb && qq < pp && pp < L) ? -acc[r] : 0.0f;
     }
   }
   __syncthreads();
-  // ---- dbeta, remaining dG terms, and F = E2 + E2^T with E2_pr = dA_pr beta_p Gam_pr
-  if (tid < C) {
-    const int pp = tid, pc = crow(pp);
+  // ---- dbeta and the remaining dG terms (8 lanes per row); F = E2 + E2^T
+  {
+    const int pp = tid >> 3, part = tid & 7, pc = crow(pp);
     const TIn* vin = static_cast<const TIn*>(io.v) + (tok0 + pc) * vs + static_cast<int64_t>(h) * D;
-    float xk = 0.0f, uv = 0.0f;
-    for (int i = 0; i < D; ++i) {
-      xk = fmaf(sY[pp * YS + i], kq[pc * 2 * D + i], xk);
+    float xk = 0.0f, uv = 0.0f, da = 0.0f, dga = 0.0f;
+#pragma unroll
+    for (int i = 16 * part; i < 16 * part + 16; ++i) {
+      xk = fmaf(sY[pp * YS + i], sK[pp * KS + i], xk);
       uv = fmaf(sY[pp * YS + D + i], ldin(vin + i), uv);
     }
-    float db = sGam[pp] * xk + uv;
-    float dgp = fmaf(sB[pp] * sGam[pp], xk, sdG[pp]);
-    for (int r = 0; r < pp; ++r) {
-      db = fmaf(sZ[pp * CS + r], sKK[pp * CS + r] * expf(sG[pp] - sG[r]), db);
-      dgp = fmaf(sZ[pp * CS + r], sA[pp * CS + r], dgp);
+#pragma unroll
+    for (int r = 8 * part; r < 8 * part + 8; ++r) {
+      if (r < pp) {
+        da = fmaf(sZ[pp * CS + r], sKG[pp * CS + r], da);
+        dga = fmaf(sZ[pp * CS + r], sB[pp] * sKG[pp * CS + r], dga);
+      } else if (r > pp) {
+        dga = fmaf(-sZ[r * CS + pp], sB[r] * sKG[r * CS + pp], dga);
+      }
     }
-    for (int q = pp + 1; q < C; ++q) dgp = fmaf(-sZ[q * CS + pp], sA[q * CS + pp], dgp);
-    sdB[pp] = pp < L ? db : 0.0f;
-    sdG[pp] = pp < L ? dgp : 0.0f;
+    xk = oct_sum(xk);
+    uv = oct_sum(uv);
+    da = oct_sum(da);
+    dga = oct_sum(dga);
+    if (part == 0) {
+      const float db = (sGam[pp] * xk + uv) + da;
+      const float dgp = fmaf(sB[pp] * sGam[pp], xk, sdG[pp]) + dga;
+      sdB[pp] = pp < L ? db : 0.0f;
+      sdG[pp] = pp < L ? dgp : 0.0f;
+    }
   }
-  for (int e = tid; e < C * C; e += 256) {
+  for (int e = tid; e < C * C; e += 512) {
     const int pp = e / C, q = e % C;
-    float f = 0.0f;
-    if (q < pp) f = sZ[pp * CS + q] * sB[pp] * expf(sG[pp] - sG[q]);
-    else if (q > pp) f = sZ[q * CS + pp] * sB[q] * expf(sG[q] - sG[pp]);
-    sQK[pp * CS + q] = f;
+    const int hi = pp > q ? pp : q, lo = pp > q ? q : pp;
+    const float f = sZ[hi * CS + lo] * sB[hi] * expf(sG[hi] - sG[lo]);
+    sQK[pp * CS + q] = pp == q ? 0.0f : f;
   }
   __syncthreads();
   // ---- dk-hat += beta gam dX_w + F K ; dv = beta dX_u
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
+    v4f ak = dk[mb];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      const int col = 32 * w + 16 * ib + l16;
-      v4f ak = dk[mb][ib];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * mb + 4 * g + r;
-        ak[r] = fmaf(sB[pp] * sGam[pp], sY[pp * YS + col], ak[r]);
-      }
-      ak = mma_nn<C>(ak, sQK + (16 * mb + l16) * CS, kq + col, 2 * D, L);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * mb + 4 * g + r;
-        if (pp < L) io.dkv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + col] = ak[r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * mb + 4 * g + r;
+      ak[r] = fmaf(sB[pp] * sGam[pp], sY[pp * YS + col], ak[r]);
     }
-  for (int e = tid; e < C * D; e += 256) {
+    ak = mma_nn<C>(ak, sQK + (16 * mb + l16) * CS, sK + col, KS, C);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * mb + 4 * g + r;
+      if (pp < L) io.dkv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + col] = ak[r];
+    }
+  }
+  for (int e = tid; e < C * D; e += 512) {
     const int pp = e / D, j = e % D;
     if (pp < L) io.dv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + j] = sB[pp] * sY[pp * YS + D + j];
   }
@@ -2378,6 +2455,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   b.SdO = reinterpret_cast<float*>(ws + L.SdO);
   b.DsD = reinterpret_cast<float*>(ws + L.DsD);
   b.SdD = reinterpret_cast<float*>(ws + L.SdD);
+  b.MdM = reinterpret_cast<float*>(ws + L.MdM);
   b.dqv = reinterpret_cast<float*>(ws + L.dqv);
   b.dkv = reinterpret_cast<float*>(ws + L.dkv);
   b.dv = dv; b.dbeta = dbeta; b.dg = dg; b.dq = dq; b.dk = dk; b.dh0 = dh0;
@@ -2413,7 +2491,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     {
       Timed t_("k_bwd_chunk", st);
       if constexpr (D == 128)
-        hipLaunchKernelGGL((k_bwd_chunk_m<C, TIn>), cgrid, dim3(256), 0, st, b);
+        hipLaunchKernelGGL((k_bwd_chunk_m<C, TIn>), cgrid, dim3(512), 0, st, b);
       else
         hipLaunchKernelGGL((k_bwd_chunk<D, C, TIn>), cgrid, dim3(256), 0, st, b);
     }
