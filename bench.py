@@ -24,6 +24,24 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_VECTOR_TFLOPS = 157.3
 
+# HBM bytes per launch of the roofline kernels, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE readings scaled by what the same counters read for a 1 GiB device
+# copy (x2.000 and x1.000).  Each entry holds only for the kernel source it was
+# taken on (sha256 prefix of gdn_kernels.hip); for any other source the
+# traffic field is reported as null.
+MEASURED_TRAFFIC = {
+    "76c6c3866553df82": {"k_rec": 613.3e6 + 134.2e6, "k_decode": 135.9e6 + 136.4e6},
+}
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_rnn_gated_amd", "csrc", "gdn_kernels.hip")
+
+
+def measured_traffic(kernel):
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    return MEASURED_TRAFFIC.get(sha, {}).get(kernel)
+
+
 PREFILL = dict(N=4, T=2048, H_qk=16, H_v=32, d=128, C=64)
 DECODE = dict(N=64, P=4096, S=256, H_qk=16, H_v=32, d=128, C=64)
 TRAIN = dict(N=8, T=4096, H_qk=16, H_v=32, d=128, C=64)
@@ -107,7 +125,8 @@ def bench_prefill(args, B, torch, make_inputs):
                 per_kernel=per_kernel,
                 roofline=dict(kernel="k_rec", bound="alu", achieved=round(achieved, 3),
                               peak=PEAK_FP32_VECTOR_TFLOPS, unit="TFLOP/s",
-                              frac=round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4), traffic=None,
+                              frac=round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4),
+                              traffic=measured_traffic("k_rec"), traffic_unit="B per launch",
                               algorithmic_per_launch=f"{rec_flops:.4e} flop"),
                 inputs=inp, shape=shape)
 
@@ -185,7 +204,8 @@ def bench_decode(args, B, torch, make_inputs):
                             for k, v in per.items()},
                 roofline=dict(kernel="k_decode", bound="hbm", achieved=round(achieved, 1),
                               peak=PEAK_HBM_GBS, unit="GB/s",
-                              frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None),
+                              frac=round(achieved / PEAK_HBM_GBS, 4),
+                              traffic=measured_traffic("k_decode"), traffic_unit="B per launch"),
                 workload="decode 64 seqs x (4096 prefill + 256 steps), 16 q/k / 32 v heads, "
                          "d128 C64 bf16")
 
