@@ -857,7 +857,7 @@ constexpr int RB = 16;
 struct OpBlock {
   float k[RB], q[RB], n[RB];
 };
-template <int D>
+template <int D>  // D: full head dimension (offset of q after k)
 __device__ __forceinline__ void load_block(OpBlock& x, cfloat_p kq, cfloat_p kn, int b) {
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
@@ -877,10 +877,11 @@ __device__ __forceinline__ void load_block(OpBlock& x, cfloat_p kq, cfloat_p kn,
 // file holds.  Neither changes any operation or its order.  (Prefetching a
 // block ahead measured slower: scalar loads complete out of order, so every
 // wait is an all-outstanding wait.)
-template <int D>
-__device__ __forceinline__ void r_token_pass(float (&s)[D], cfloat_p kq, cfloat_p kn, float alpha,
+template <int DK, int D>  // DK: elements of the row this lane holds; D: head dimension
+__device__ __forceinline__ void r_token_pass(float (&s)[DK], cfloat_p kq, cfloat_p kn, float alpha,
                                              float delta, float& o, float& an) {
-  constexpr int NB = D / RB;
+  constexpr int NB = DK / RB;
+  static_assert(DK % RB == 0, "row part must be whole operand blocks");
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     OpBlock x;
@@ -917,29 +918,49 @@ struct RecIO {
   int64_t T, max_state_slot;
 };
 
-// Blocks of up to 4 waves over (chunk, q/k head): a wave per (value head of
-// the group, 64-row half of d_v), so waves that read the same key/query stream
-// share a CU and its scalar cache; blockIdx.z continues a group of more than
-// 4 waves.
+// How the token step splits a head's state over waves: 64-row parts of d_v
+// (one row per lane) and, at d = 128, two 64-element halves of d_k.  With the
+// d_k split, every dot product of R is the sum of two partial chains,
+//   x = chain(i = 0 .. 63) + chain(i = 64 .. 127),
+// each an ascending fmaf chain from 0; the wave pair holding the two halves of
+// the same rows exchanges its partials through LDS.  The decode step forms
+// the same two chains and the same sum.
+template <int D>
+struct RowSplit {
+  static constexpr int NH = (D + 63) / 64;   // row parts
+  static constexpr int KS = D >= 128 ? 2 : 1; // d_k parts
+  static constexpr int DK = D / KS;          // elements per lane
+  static constexpr int WPH = NH * KS;        // waves per value head
+};
+
+// Blocks over (chunk, q/k head, z): each block holds `hpb` value heads of the
+// group (waves = hpb * waves per head, at most 8), so the waves that read the
+// same key/query stream share a CU and its scalar cache; blockIdx.z continues
+// a group of more heads.  Wave (head, row part, d_k part) = index within the
+// block in that order, d_k part fastest.
 template <int D, int C, typename TIn>
-__global__ __launch_bounds__(256) void k_rec(RecIO io) {
-  constexpr int NH = (D + 63) / 64;  // waves per value head
+__global__ __launch_bounds__(512) void k_rec(RecIO io, int hpb) {
+  using RS = RowSplit<D>;
+  constexpr int DK = RS::DK, KS = RS::KS, NH = RS::NH;
+  __shared__ float xa[2][8][64];  // partial dots (parity, wave, lane)
+  __shared__ float xo[2][8][64];
   const int slot = blockIdx.x;
-  const int wv = __builtin_amdgcn_readfirstlane(blockIdx.z * 4 + (threadIdx.x >> 6));
-  if (wv >= (io.H_v / io.H_qk) * NH) return;  // whole wave
-  const int h = blockIdx.y * (io.H_v / io.H_qk) + wv / NH;
+  const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = blockIdx.z * hpb * RS::WPH + wl;
+  const int kh = wv % KS, rh = (wv / KS) % NH;
+  const int G = io.H_v / io.H_qk;
+  const int h = blockIdx.y * G + wv / RS::WPH;
   const int lane = threadIdx.x & 63;
-  const int j = (wv % NH) * 64 + lane;
+  const int j = rh * 64 + lane;
   const bool act = j < D;
   const int jc = act ? j : 0;  // inactive lanes (D < 64) read row 0 and store nothing
-  if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return;
+  if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return;  // whole block
   const int n = find_seq(io.cu_chunks, io.N, slot);
-  const int G = io.H_v / io.H_qk;
   const int hq = h / G;
   const int64_t c = slot - io.cu_chunks[n];
   const int64_t tok0 = static_cast<int64_t>(io.cu[n]) + c * C;
   const int64_t end = io.cu[n + 1];
-  if (tok0 < 0 || end > io.T || tok0 >= end) return;
+  if (tok0 < 0 || end > io.T || tok0 >= end) return;  // whole block
   const int L = static_cast<int>(end - tok0 < C ? end - tok0 : C);
   const int64_t DD = static_cast<int64_t>(D) * D;
   const TIn* v = static_cast<const TIn*>(io.v) + (tok0 * io.H_v + h) * D + jc;
@@ -948,15 +969,21 @@ __global__ __launch_bounds__(256) void k_rec(RecIO io) {
   float* op = io.o + (tok0 * io.H_v + h) * D + jc;
   const int vs = io.H_v * D;  // < 2^20 (host-checked)
   const int bs = io.H_v;
+  const int i0 = kh * DK;     // first d_k element of this wave
 
-  float s[D];
+  float s[DK];
   const float* st = io.states + (static_cast<int64_t>(slot) * io.H_v + h) * DD + jc;
 #pragma unroll
-  for (int i = 0; i < D; ++i) s[i] = st[i * D];
+  for (int i = 0; i < DK; ++i) s[i] = st[static_cast<int64_t>(i0 + i) * D];
 
   // key (t) / query (t) / key (t+1) streams, 2*D floats per token
-  cfloat_p kq = as_const(io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D);
-  float a = row_dot<D>(s, kq);
+  cfloat_p kq = as_const(io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D + i0);
+  float a = row_dot<DK>(s, kq);
+  if constexpr (KS == 2) {
+    xa[1][wl][lane] = a;
+    __syncthreads();
+    a = a + xa[1][wl ^ 1][lane];
+  }
   for (int t = 0; t < L; ++t) {
     const float alpha = expf(*gt);
     const float b = *bt;
@@ -965,12 +992,20 @@ __global__ __launch_bounds__(256) void k_rec(RecIO io) {
     const float delta = b * (vj - u);
     cfloat_p kn = kq + 2 * D;  // past the chunk's end on its last token: read, never used
     float o = 0.0f, an = 0.0f;
-    r_token_pass<D>(s, kq, kn, alpha, delta, o, an);
-    if (act) *op = o;
+    r_token_pass<DK, D>(s, kq, kn, alpha, delta, o, an);
+    if constexpr (KS == 2) {
+      const int par = t & 1;  // a slot is rewritten two barriers after it was read
+      xa[par][wl][lane] = an;
+      xo[par][wl][lane] = o;
+      __syncthreads();
+      an = an + xa[par][wl ^ 1][lane];
+      o = o + xo[par][wl ^ 1][lane];
+    }
+    if (act && kh == 0) *op = o;
     a = an;
     kq += 2 * D;
     // opaque to the optimizer: otherwise it forwards this token's kn loads to
-    // the next token's k loads and must keep 128 values live across iterations
+    // the next token's k loads and must keep the values live across iterations
     asm volatile("" : "+s"(kq));
     gt += bs;
     bt += bs;
@@ -983,13 +1018,14 @@ __global__ __launch_bounds__(256) void k_rec(RecIO io) {
   const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
   if (act && io.hT) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) io.hT[nh * DD + static_cast<int64_t>(i) * D + j] = s[i];
+    for (int i = 0; i < DK; ++i) io.hT[nh * DD + static_cast<int64_t>(i0 + i) * D + j] = s[i];
   }
   if (!io.S_run) return;
   if (act) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) io.S_run[nh * DD + static_cast<int64_t>(i) * D + j] = s[i];
+    for (int i = 0; i < DK; ++i) io.S_run[nh * DD + static_cast<int64_t>(i0 + i) * D + j] = s[i];
   }
+  if (kh != 0) return;
   TIn* vb = static_cast<TIn*>(io.vbuf);
   const TIn* vin = static_cast<const TIn*>(io.v);
   for (int t = 0; t < L; ++t) {
@@ -1032,18 +1068,30 @@ struct DecIO {
   float scale;
 };
 
+// One decode token per (sequence, value head) block; waves split the state as
+// in k_rec (row parts, and d_k halves at d = 128, whose partial dots are
+// summed in the same order).
 template <int D, int C, typename TIn>
-__global__ __launch_bounds__(D < 64 ? 64 : D) void k_decode(DecIO io) {
+__global__ __launch_bounds__(256) void k_decode(DecIO io) {
+  using RS = RowSplit<D>;
+  constexpr int DK = RS::DK, KS = RS::KS, NH = RS::NH;
+  static_assert(RS::WPH <= 4, "one block of at most 4 waves per head");
   __shared__ float sq[D < 64 ? 64 : D];
   __shared__ float sk[D < 64 ? 64 : D];
+  __shared__ float xa[4][64];
+  __shared__ float xo[4][64];
   const int n = blockIdx.x;
   const int h = blockIdx.y;
-  const int j = threadIdx.x;
+  const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kh = wl % KS, rh = wl / KS;
+  const int lane = threadIdx.x & 63;
+  const int j = rh * 64 + lane;
   const bool act = j < D;
   const int G = io.H_v / io.H_qk;
   const int hq = h / G;
   const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
   const int64_t DD = static_cast<int64_t>(D) * D;
+  const int i0 = kh * DK;
   int p = io.pos[nh];
   p = p < 0 ? 0 : (p >= C ? C - 1 : p);
   if (threadIdx.x < 64) {
@@ -1051,37 +1099,49 @@ __global__ __launch_bounds__(D < 64 ? 64 : D) void k_decode(DecIO io) {
     const TIn* k = static_cast<const TIn*>(io.k) + (static_cast<int64_t>(n) * io.H_qk + hq) * D;
     float y0, y1;
     l2norm_wave<D>(q, io.scale, io.l2, y0, y1);
-    if (j < D) sq[j] = y0;
-    if (D > 64) sq[j + 64] = y1;
+    if (lane < D) sq[lane] = y0;
+    if (D > 64) sq[lane + 64] = y1;
     l2norm_wave<D>(k, 1.0f, io.l2, y0, y1);
-    if (j < D) sk[j] = y0;
-    if (D > 64) sk[j + 64] = y1;
+    if (lane < D) sk[lane] = y0;
+    if (D > 64) sk[lane + 64] = y1;
   }
-  __syncthreads();
   const int jc = act ? j : 0;
-  float s[D];
+  float s[DK];
   float* sr = io.S_run + nh * DD;
 #pragma unroll
-  for (int i = 0; i < D; ++i) s[i] = sr[static_cast<int64_t>(i) * D + jc];
+  for (int i = 0; i < DK; ++i) s[i] = sr[static_cast<int64_t>(i0 + i) * D + jc];
+  __syncthreads();
   const TIn* v = static_cast<const TIn*>(io.v);
   const float gt = io.g[nh];
   const float alpha = expf(gt);
   const float b = io.beta[nh];
   const float vj = ldin(v + nh * D + jc);
-  const float a = row_dot<D>(s, static_cast<const float*>(sk));
+  float a = row_dot<DK>(s, static_cast<const float*>(sk) + i0);
+  if constexpr (KS == 2) {
+    xa[wl][lane] = a;
+    __syncthreads();
+    a = a + xa[wl ^ 1][lane];
+  }
   const float u = alpha * a;
   const float delta = b * (vj - u);
-  const float o = r_update_lds<D>(s, sk, sq, alpha, delta);
+  float o = r_update_lds<DK>(s, sk + i0, sq + i0, alpha, delta);
+  if constexpr (KS == 2) {
+    xo[wl][lane] = o;
+    __syncthreads();
+    o = o + xo[wl ^ 1][lane];
+  }
   if (act) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) sr[static_cast<int64_t>(i) * D + j] = s[i];
-    io.o[nh * D + j] = o;
-    const int64_t bt = static_cast<int64_t>(n) * C + p;
-    static_cast<TIn*>(io.vbuf)[(bt * io.H_v + h) * D + j] = v[nh * D + j];
-    if (h % G == 0) io.kbuf[(bt * io.H_qk + hq) * D + j] = sk[j];
-    if (j == 0) {
-      io.bbuf[bt * io.H_v + h] = b;
-      io.gbuf[bt * io.H_v + h] = gt;
+    for (int i = 0; i < DK; ++i) sr[static_cast<int64_t>(i0 + i) * D + j] = s[i];
+    if (kh == 0) {
+      io.o[nh * D + j] = o;
+      const int64_t bt = static_cast<int64_t>(n) * C + p;
+      static_cast<TIn*>(io.vbuf)[(bt * io.H_v + h) * D + j] = v[nh * D + j];
+      if (h % G == 0) io.kbuf[(bt * io.H_qk + hq) * D + j] = sk[j];
+      if (j == 0) {
+        io.bbuf[bt * io.H_v + h] = b;
+        io.gbuf[bt * io.H_v + h] = gt;
+      }
     }
   }
   __syncthreads();  // every lane has read pos
@@ -2265,6 +2325,15 @@ constexpr int kTile128 = 32;  // state rows per k_scan block at d = 128
 template <int D>
 constexpr int scan_tile() { return D == 128 ? kTile128 : D; }
 
+// Value heads per k_rec block: as many of the group as fit in 8 waves and
+// divide the group evenly (the group has at most 8 heads).
+template <int D>
+int rec_heads_per_block(int G) {
+  int hpb = 8 / RowSplit<D>::WPH;
+  while (hpb > 1 && G % hpb != 0) --hpb;
+  return hpb < G ? hpb : G;
+}
+
 // The chunk factors: matrix-core kernel at d = 128, the VALU kernel at d = 16.
 template <int D, int C, typename TIn, int MODE>
 void launch_wy(const ChunkIO& io, int64_t items, int H_v, hipStream_t st) {
@@ -2346,10 +2415,10 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     }
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_state_slot = L.state_slots;
     Timed t_("k_rec", st);
-    const int waves = (s->H_v / s->H_qk) * ((D + 63) / 64);
-    hipLaunchKernelGGL((k_rec<D, C, TIn>),
-                       dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, (waves + 3) / 4),
-                       dim3(64 * (waves < 4 ? waves : 4)), 0, st, io);
+    const int G = s->H_v / s->H_qk;
+    const int hpb = rec_heads_per_block<D>(G);
+    hipLaunchKernelGGL((k_rec<D, C, TIn>), dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb),
+                       dim3(64 * RowSplit<D>::WPH * hpb), 0, st, io, hpb);
   }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -2365,7 +2434,7 @@ int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const v
   io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.l2 = s->qk_l2norm; io.scale = s->scale;
   {
     Timed t_("k_decode", st);
-    hipLaunchKernelGGL((k_decode<D, C, TIn>), dim3(N, s->H_v), dim3(D < 64 ? 64 : D), 0, st, io);
+    hipLaunchKernelGGL((k_decode<D, C, TIn>), dim3(N, s->H_v), dim3(64 * RowSplit<D>::WPH), 0, st, io);
   }
   if (resync) {
     float* W = reinterpret_cast<float*>(ws + L.W);
@@ -2440,10 +2509,10 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     io.cu_chunks = cu_chunks; io.states = states; io.o = o; io.hT = hT;
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_state_slot = L.state_slots;
     Timed t_("k_rec", st);
-    const int waves = (s->H_v / s->H_qk) * ((D + 63) / 64);
-    hipLaunchKernelGGL((k_rec<D, C, TIn>),
-                       dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, (waves + 3) / 4),
-                       dim3(64 * (waves < 4 ? waves : 4)), 0, st, io);
+    const int G = s->H_v / s->H_qk;
+    const int hpb = rec_heads_per_block<D>(G);
+    hipLaunchKernelGGL((k_rec<D, C, TIn>), dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb),
+                       dim3(64 * RowSplit<D>::WPH * hpb), 0, st, io, hpb);
   }
   // backward
   BwdIO b{};
@@ -2660,7 +2729,7 @@ int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
 }
 
 const char* gdn_contract_id(void) {
-  return "gdn-cpr/v5;eps=1e-6;claims=d16C16,d128C64;R=lane-row,fmaf-asc,o-after-update;"
+  return "gdn-cpr/v6;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
          "B=mfma16x16x4-wy-blocked16,mfma16x16x4-scan-tile32;prep=wave-butterfly";
 }
 
