@@ -46,6 +46,26 @@ __device__ __forceinline__ float ldin(const bf16_t* p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);
 }
 
+// Raw buffer access: a 4-dword resource over [base, base + bytes) in SGPRs,
+// a per-lane byte offset and a wave-uniform byte offset.  Accesses outside
+// the range read 0 / are dropped by the hardware.
+using brsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kBufWord3 = 0x00020000;  // raw 32-bit data format (gfx9 family)
+__device__ __forceinline__ brsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kBufWord3);
+}
+__device__ __forceinline__ float ldbuf(brsrc_t r, uint32_t voff, uint32_t soff, const float*) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void stbuf(float x, brsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+__device__ __forceinline__ float ldbuf(brsrc_t r, uint32_t voff, uint32_t soff, const bf16_t*) {
+  const uint16_t x = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
 // Largest n in [0, N) with arr[n] <= x (arr non-decreasing, arr[0] = 0): the
 // sequence that owns slot x.  Uniform across the block.
 __device__ __forceinline__ int find_seq(const int32_t* __restrict__ arr, int N, int64_t x) {
@@ -939,21 +959,23 @@ struct RowSplit {
 // a group of more heads.  Wave (head, row part, d_k part) = index within the
 // block in that order, d_k part fastest.
 template <int D, int C, typename TIn>
-__global__ __launch_bounds__(512) void k_rec(RecIO io, int hpb) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k_rec(RecIO io, int hpb) {
   using RS = RowSplit<D>;
   constexpr int DK = RS::DK, KS = RS::KS, NH = RS::NH;
+  constexpr int NW = 8 / KS;       // (head, row part) pairs per block, at most
   __shared__ float xa[2][8][64];  // partial dots (parity, wave, lane)
   __shared__ float xo[2][8][64];
+  __shared__ TIn sv[NW][C][64];   // the chunk's v rows of each (head, row part)
   const int slot = blockIdx.x;
   const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wv = blockIdx.z * hpb * RS::WPH + wl;
   const int kh = wv % KS, rh = (wv / KS) % NH;
   const int G = io.H_v / io.H_qk;
   const int h = blockIdx.y * G + wv / RS::WPH;
+  const int wp = wl / KS;  // (head, row part) pair within the block
   const int lane = threadIdx.x & 63;
   const int j = rh * 64 + lane;
-  const bool act = j < D;
-  const int jc = act ? j : 0;  // inactive lanes (D < 64) read row 0 and store nothing
+  const bool act = D % 64 == 0 || j < D;
   if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return;  // whole block
   const int n = find_seq(io.cu_chunks, io.N, slot);
   const int hq = h / G;
@@ -963,13 +985,35 @@ __global__ __launch_bounds__(512) void k_rec(RecIO io, int hpb) {
   if (tok0 < 0 || end > io.T || tok0 >= end) return;  // whole block
   const int L = static_cast<int>(end - tok0 < C ? end - tok0 : C);
   const int64_t DD = static_cast<int64_t>(D) * D;
-  const TIn* v = static_cast<const TIn*>(io.v) + (tok0 * io.H_v + h) * D + jc;
-  const float* bt = io.beta + tok0 * io.H_v + h;
-  const float* gt = io.g + tok0 * io.H_v + h;
-  float* op = io.o + (tok0 * io.H_v + h) * D + jc;
   const int vs = io.H_v * D;  // < 2^20 (host-checked)
   const int bs = io.H_v;
   const int i0 = kh * DK;     // first d_k element of this wave
+  // Token operands of the chunk: g and beta as wave-uniform scalar loads, v
+  // and o through buffer resources over the chunk's rows (lane offset in a
+  // VGPR, token offset in an SGPR).
+  cfloat_p gt = as_const(io.g + tok0 * io.H_v + h);
+  cfloat_p bt = as_const(io.beta + tok0 * io.H_v + h);
+  float* obase = io.o + (tok0 * io.H_v + h) * D;
+  const uint32_t otok = static_cast<uint32_t>(vs) * 4u;
+  const brsrc_t orr = make_rsrc(obase, static_cast<uint32_t>(L - 1) * otok + D * 4u);
+  // inactive lanes (D < 64) read row 0 and store nothing; buffer offsets are
+  // the lane's part in a VGPR and the row part's and token's in an SGPR
+  const int jc = act ? j : 0;
+  const uint32_t lo4 = static_cast<uint32_t>(lane) * 4u;
+  const uint32_t ro = static_cast<uint32_t>(rh * 64) * 4u;
+  {  // stage v: pair q of the block is (head q / NH of the block, row part q % NH)
+    const int npair = static_cast<int>(blockDim.x >> 6) / KS;
+    const TIn* vin = static_cast<const TIn*>(io.v);
+    const int hb = blockIdx.y * G + blockIdx.z * hpb;  // first head of the block
+    for (int e = threadIdx.x; e < npair * C * 64; e += blockDim.x) {
+      const int q = e / (C * 64), tt = (e / 64) % C, ll = e % 64;
+      const int row = (q % NH) * 64 + ll;
+      const int tc = tt < L ? tt : L - 1;
+      sv[q][tt][ll] = row < D ? vin[(tok0 + tc) * io.H_v * D + static_cast<int64_t>(hb + q / NH) * D + row]
+                              : TIn(0);
+    }
+  }
+  __syncthreads();
 
   float s[DK];
   const float* st = io.states + (static_cast<int64_t>(slot) * io.H_v + h) * DD + jc;
@@ -984,10 +1028,17 @@ __global__ __launch_bounds__(512) void k_rec(RecIO io, int hpb) {
     __syncthreads();
     a = a + xa[1][wl ^ 1][lane];
   }
+  // g, beta and v are loaded one token ahead; the last token reloads itself
+  // rather than reading past the chunk
+  float gn = gt[0], bn = bt[0], vn = ldin(&sv[wp][0][lane]);
   for (int t = 0; t < L; ++t) {
-    const float alpha = expf(*gt);
-    const float b = *bt;
-    const float vj = ldin(v);
+    const float alpha = expf(gn);
+    const float b = bn;
+    const float vj = vn;
+    const int tn = t + 1 < L ? t + 1 : t;
+    gn = gt[tn * bs];
+    bn = bt[tn * bs];
+    vn = ldin(&sv[wp][tn][lane]);
     const float u = alpha * a;
     const float delta = b * (vj - u);
     cfloat_p kn = kq + 2 * D;  // past the chunk's end on its last token: read, never used
@@ -1001,16 +1052,12 @@ __global__ __launch_bounds__(512) void k_rec(RecIO io, int hpb) {
       an = an + xa[par][wl ^ 1][lane];
       o = o + xo[par][wl ^ 1][lane];
     }
-    if (act && kh == 0) *op = o;
+    if (act && kh == 0) stbuf(o, orr, lo4, static_cast<uint32_t>(t) * otok + ro);
     a = an;
     kq += 2 * D;
     // opaque to the optimizer: otherwise it forwards this token's kn loads to
     // the next token's k loads and must keep the values live across iterations
     asm volatile("" : "+s"(kq));
-    gt += bs;
-    bt += bs;
-    v += vs;
-    op += vs;
   }
   if (L == C) return;
   // tail chunk: the running state is the sequence's final state, and the
