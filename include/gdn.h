@@ -31,7 +31,8 @@
  * batch composition, run after run.
  *
  * Conventions for every call
- *   - All tensors are dense, row-major, on the current HIP device; the caller
+ *   - All tensors are dense, row-major, on the current HIP device, and start
+ *     at 16-byte aligned addresses (else GDN_ERR_INVALID_ARG); the caller
  *     owns every buffer.  The library never allocates or frees device memory
  *     in these calls; scratch comes from `ws`, sized by gdn_workspace_bytes.
  *   - Packed layouts: q, k [T, H_qk, d_k]; v [T, H_v, d_v] in in_dtype;

@@ -46,6 +46,12 @@ __device__ __forceinline__ float ldin(const bf16_t* p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);
 }
 
+// Component-wise select of float4 values (a ternary on the struct can turn
+// into a select of addresses in private memory).
+__device__ __forceinline__ float4 sel4(bool c, float4 a, float4 b) {
+  return float4{c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w};
+}
+
 // Raw buffer access: a 4-dword resource over [base, base + bytes) in SGPRs,
 // a per-lane byte offset and a wave-uniform byte offset.  Accesses outside
 // the range read 0 / are dropped by the hardware.
@@ -487,7 +493,10 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
   }
 
   const float* src = RESYNC ? io.S_chunk + nh * DD : (io.h0 ? io.h0 + nh * DD : nullptr);
-  for (int e = tid; e < TILE * D; e += 256) {
+  static_assert((TILE * D) % 256 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (TILE * D) / 256; ++e_) {
+    const int e = tid + 256 * e_;
     const int i = e / TILE, jj = e % TILE;
     sS[jj * SS + i] = src ? src[static_cast<int64_t>(i) * D + j0 + jj] : 0.0f;
   }
@@ -645,7 +654,10 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
   }
   const bool tail = (L % C) != 0;
   if (MODE == kAll && tail) return;
-  for (int e = tid; e < TILE * D; e += 256) {
+  static_assert((TILE * D) % 256 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (TILE * D) / 256; ++e_) {
+    const int e = tid + 256 * e_;
     const int i = e / TILE, jj = e % TILE;
     const int64_t off = static_cast<int64_t>(i) * D + j0 + jj;
     const float x = sS[jj * SS + i];
@@ -682,8 +694,12 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
   constexpr int AS = C + 4;  // row stride of sA
   static_assert(C == 64, "tiling assumes C = 64");
   constexpr bool RESYNC = MODE == kResync;
+  // V is staged (coalesced) in the space A takes later
+  constexpr int VWORDS = C * D * static_cast<int>(sizeof(TIn)) / 4, AWORDS = C * AS;
   __shared__ __attribute__((aligned(16))) float sK[C * KS];
-  __shared__ float sA[C * AS];
+  __shared__ __attribute__((aligned(16))) float sAV[AWORDS > VWORDS ? AWORDS : VWORDS];
+  float* sA = sAV;
+  TIn* sV = reinterpret_cast<TIn*>(sAV);
   __shared__ float sB[C], sG[C], sBG[C];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -715,26 +731,28 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
   const bool isW = w < 2;
   const int cbase = 64 * (w & 1);
   const TIn* v = static_cast<const TIn*>(io.v) + tok0 * io.H_v * D + static_cast<int64_t>(h) * D;
-  // values of this wave's U columns, loaded up front: (row 16 bi + 4 g + r, column cbase + 16 ct + l16)
-  float vpre[4][4][4];
-#pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = 16 * bi + 4 * g + r;
-        const int pc = p < L ? p : L - 1;
-        const float x = isW ? 0.0f : ldin(v + static_cast<int64_t>(pc) * io.H_v * D + cbase + 16 * ct + l16);
-        vpre[bi][ct][r] = p < L ? x : 0.0f;
-      }
   // rows past a partial chunk's end read the last row (in bounds) and are zeroed
-  for (int e = tid; e < C * (D / 4); e += 256) {
+  constexpr int EPV = 16 / static_cast<int>(sizeof(TIn));  // elements per 16 bytes
+  static_assert((C * (D / EPV)) % 256 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / EPV)) / 256; ++e_) {
+    const int e = tid + 256 * e_;
+    const int p = e / (D / EPV), c4 = e % (D / EPV);
+    const int pc = p < L ? p : L - 1;
+    const uint4 x = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(pc) * io.H_v * D + c4 * EPV);
+    const bool in = p < L;
+    *reinterpret_cast<uint4*>(sV + p * D + c4 * EPV) =
+        uint4{in ? x.x : 0u, in ? x.y : 0u, in ? x.z : 0u, in ? x.w : 0u};
+  }
+  static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / 4)) / 256; ++e_) {
+    const int e = tid + 256 * e_;
     const int p = e / (D / 4), i4 = e % (D / 4);
     const int pc = p < L ? p : L - 1;
     const float4 x = *reinterpret_cast<const float4*>(krow + pc * kst + 4 * i4);
     *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) =
-        p < L ? x : float4{0.0f, 0.0f, 0.0f, 0.0f};
+        sel4(p < L, x, float4{0.0f, 0.0f, 0.0f, 0.0f});
   }
   if (tid < C) {
     const int pc = tid < L ? tid : L - 1;
@@ -744,6 +762,15 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
     sBG[tid] = tid < L ? gx : 0.0f;  // raw g for now
   }
   __syncthreads();
+  // values of this wave's U columns: (row 16 bi + 4 g + r, column cbase + 16 ct + l16)
+  float vpre[4][4][4];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vpre[bi][ct][r] = isW ? 0.0f : ldin(sV + (16 * bi + 4 * g + r) * D + cbase + 16 * ct + l16);
   if (tid == 0) {  // running sum of g, p ascending
     float acc = 0.0f;
     for (int p = 0; p < C; ++p) {
@@ -1699,13 +1726,13 @@ template <int C>
 __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
   constexpr int D = 128, S1 = D + 4, S2 = C + 4;
   static_assert(C == 64, "tiling assumes C = 64");
-  __shared__ __attribute__((aligned(16))) float lds[2 * C * S1];  // Q | K, then dO^T | P^T
+  __shared__ __attribute__((aligned(16))) float lds[2 * C * S1];  // Q | K, then dO | P^T
   __shared__ float sG[C];
   float* sQ = lds;
   float* sK = lds + C * S1;
-  float* dOT = lds;            // [D][S2]
-  float* PT = lds + D * S2;    // [C][S2]
-  static_assert(D * S2 + C * S2 <= 2 * C * S1, "LDS reuse");
+  float* sO = lds;             // [C][S1]
+  float* PT = lds + C * S1;    // [C][S2]
+  static_assert(C * S2 <= C * S1, "LDS reuse");
   int64_t slot, tok0;
   int L;
   if (!bwd_item<C>(io, slot, tok0, L)) return;
@@ -1714,14 +1741,17 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
   const int h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
   const int64_t sh = slot * io.H_v + h;
   const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
-  for (int e = tid; e < C * (D / 4); e += 256) {
+  static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / 4)) / 256; ++e_) {
+    const int e = tid + 256 * e_;
     const int p = e / (D / 4), i4 = e % (D / 4);
     const int pc = p < L ? p : L - 1;
     const float4 k4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
     const float4 q4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
     const float4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    *reinterpret_cast<float4*>(sK + p * S1 + 4 * i4) = p < L ? k4 : z;
-    *reinterpret_cast<float4*>(sQ + p * S1 + 4 * i4) = p < L ? q4 : z;
+    *reinterpret_cast<float4*>(sK + p * S1 + 4 * i4) = sel4(p < L, k4, z);
+    *reinterpret_cast<float4*>(sQ + p * S1 + 4 * i4) = sel4(p < L, q4, z);
   }
   if (tid < C) sG[tid] = io.G[sh * C + tid];
   __syncthreads();
@@ -1743,95 +1773,169 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) PT[(16 * nb + l16) * S2 + 16 * w + 4 * g + r] = P[nb][r];
   const float* dO = io.dO + (tok0 * io.H_v + h) * D;
-  for (int e = tid; e < C * D; e += 256) {
-    const int p = e / D, j = e % D;
+  static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / 4)) / 256; ++e_) {
+    const int e = tid + 256 * e_;
+    const int p = e / (D / 4), i4 = e % (D / 4);
     const int pc = p < L ? p : L - 1;
-    const float x = dO[static_cast<int64_t>(pc) * io.H_v * D + j];
-    dOT[j * S2 + p] = p < L ? x : 0.0f;
+    const float4 x = *reinterpret_cast<const float4*>(dO + static_cast<int64_t>(pc) * io.H_v * D + 4 * i4);
+    *reinterpret_cast<float4*>(sO + p * S1 + 4 * i4) = sel4(p < L, x, float4{0.0f, 0.0f, 0.0f, 0.0f});
   }
   __syncthreads();
   float* E = io.E + sh * static_cast<int64_t>(C) * D;
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = mma_nt<C>(acc, PT + (16 * w + l16) * S2, dOT + (16 * nb + l16) * S2);
+    acc = mma_nn<C>(acc, PT + (16 * w + l16) * S2, sO + 16 * nb + l16, S1, C);
 #pragma unroll
     for (int r = 0; r < 4; ++r) E[(16 * w + 4 * g + r) * D + 16 * nb + l16] = acc[r];
   }
 }
 
-// The three state products of a chunk on the matrix cores:
-// out[p][i] = sum_j Y[p][j] X[i][j]  for (X, Y) = (S, dO), (S, dDelta), (dS', Delta).
-// Y is staged in LDS; X rows are read from L2, each feeding four 16-row tiles.
+// Chunk item `it` of the persistent backward kernels: items are (chunk slot,
+// value head) pairs, head fastest.  False if the item has no tokens.
 template <int C>
-__global__ __launch_bounds__(256) void k_bwd_mm_m(BwdIO io) {
-  constexpr int D = 128, S1 = D + 4;
-  static_assert(C == 64, "tiling assumes C = 64");
-  __shared__ __attribute__((aligned(16))) float sY[C * S1];
-  int64_t slot, tok0;
-  int L;
-  if (!bwd_item<C>(io, slot, tok0, L)) return;
+__device__ __forceinline__ bool bwd_item_at(const BwdIO& io, int64_t it, int64_t& slot, int& h,
+                                            int64_t& tok0, int& L) {
+  slot = it / io.H_v;
+  h = static_cast<int>(it % io.H_v);
+  if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return false;
+  const int n = find_seq(io.cu_chunks, io.N, slot);
+  tok0 = static_cast<int64_t>(io.cu[n]) + (slot - io.cu_chunks[n]) * C;
+  const int64_t end = io.cu[n + 1];
+  if (tok0 < 0 || end > io.T || tok0 >= end) return false;
+  L = static_cast<int>(end - tok0 < C ? end - tok0 : C);
+  return true;
+}
+
+// The three state products of a chunk on the matrix cores, and <S, dS'>:
+//   SdO[p][n] = sum_k dO[p][k] S[n][k]      SdD[p][n] = sum_k dDelta[p][k] S[n][k]
+//   DsD[p][n] = sum_k Delta[p][k] dS'[n][k]  MdM = sum_{n,k} S[n][k] dS'[n][k]
+// with S, dS' in their stored layout.  Persistent blocks of 8 waves walk the
+// (chunk, head) items.  The three C x D operands of an item sit in LDS (the
+// next item's are fetched into registers while the current one computes);
+// wave w streams rows 16 w .. 16 w + 15 of S and dS' from memory once, each
+// row feeding four 16-row tiles of every product.  k runs in steps of 16:
+// lane group g supplies k = 16 s + 4 g + c at component c, so each load of a
+// lane group covers 64 contiguous bytes of a row.
+template <int C>
+__global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
+  constexpr int D = 128, S1 = D + 4, NY = 3 * C * (D / 4) / 512;  // float4 per thread
+  static_assert(C == 64 && NY * 512 == 3 * C * (D / 4), "tiling assumes C = 64, D = 128");
+  __shared__ __attribute__((aligned(16))) float sY[3 * C * S1];
+  __shared__ float red[8];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y;
   const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
-  const int64_t sh = slot * io.H_v + h;
-  for (int prod = 0; prod < 3; ++prod) {
-    const float* X = (prod == 2 ? io.dstates : io.states) + sh * DD;
-    for (int e = tid; e < C * (D / 4); e += 256) {
-      const int p = e / (D / 4), j4 = e % (D / 4);
-      const int pc = p < L ? p : L - 1;
-      const float* src = prod == 0 ? io.dO + ((tok0 + pc) * io.H_v + h) * D
-                                   : (prod == 1 ? io.dD : io.Dl) + sh * CD + pc * D;
-      const float4 y = *reinterpret_cast<const float4*>(src + 4 * j4);
-      *reinterpret_cast<float4*>(sY + p * S1 + 4 * j4) = p < L ? y : float4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  // this thread's share of an item's operands: rows tid / 32 + 16 m, column
+  // quad tid % 32, of dO (m = 0..3), dDelta (m = 4..7) and Delta (m = 8..11)
+  auto load_y = [&](float4 (&y)[NY], int64_t it) {
+    int64_t slot, tok0;
+    int h, L;
+    const bool ok = bwd_item_at<C>(io, it, slot, h, tok0, L);
+    if (!ok) {  // read row 0 of item 0 (in bounds) and zero it below
+      slot = 0;
+      h = 0;
+      tok0 = 0;
+      L = 1;
     }
+    const int64_t sh = slot * io.H_v + h;
+    const int pr = tid >> 5, q4 = tid & 31;
+    const float* o0 = io.dO + (tok0 * io.H_v + h) * D + 4 * q4;
+    const float* o1 = io.dD + sh * CD + 4 * q4;
+    const float* o2 = io.Dl + sh * CD + 4 * q4;
+    const int64_t ors = static_cast<int64_t>(io.H_v) * D;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int p = pr + 16 * m;
+      const int pc = p < L ? p : L - 1;
+      const bool keep = ok && p < L;
+      const float4 x0 = *reinterpret_cast<const float4*>(o0 + pc * ors);
+      const float4 x1 = *reinterpret_cast<const float4*>(o1 + pc * D);
+      const float4 x2 = *reinterpret_cast<const float4*>(o2 + pc * D);
+      y[m] = sel4(keep, x0, z4);
+      y[4 + m] = sel4(keep, x1, z4);
+      y[8 + m] = sel4(keep, x2, z4);
+    }
+  };
+  float4 ypre[NY];
+  int64_t it = blockIdx.x;
+  if (it < nitems) load_y(ypre, it);
+  for (; it < nitems; it += gridDim.x) {
+    int64_t slot, tok0;
+    int h, L;
+    const bool ok = bwd_item_at<C>(io, it, slot, h, tok0, L);
+    __syncthreads();  // the previous item's LDS reads are done
+#pragma unroll
+    for (int m = 0; m < NY; ++m)
+      *reinterpret_cast<float4*>(sY + ((m / 4) * C + (tid >> 5) + 16 * (m % 4)) * S1 +
+                                 4 * (tid & 31)) = ypre[m];
     __syncthreads();
-    float* out = (prod == 0 ? io.SdO : prod == 1 ? io.SdD : io.DsD) + sh * CD;
-    float mdm = 0.0f;  // product 2: this lane's part of <S, dS'> (rows it streams)
-#pragma unroll 1
-    for (int ib = 0; ib < 2; ++ib) {
-      const int nb = 2 * w + ib;
-      const float* xb = X + (16 * nb + l16) * D + g * (D / 4);
-      const float* sb = io.states + sh * DD + (16 * nb + l16) * D + g * (D / 4);
-      v4f acc[4];
+    if (it + gridDim.x < nitems) load_y(ypre, it + gridDim.x);
+    if (!ok) continue;  // uniform over the block
+    const int64_t sh = slot * io.H_v + h;
+    const int n = 16 * w + l16;  // the X row this lane streams
+    const float* x1 = io.states + sh * DD + n * D + 4 * g;
+    const float* x2 = io.dstates + sh * DD + n * D + 4 * g;
+    v4f acc[3][4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int pr = 0; pr < 3; ++pr)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[pr][mb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float mdm = 0.0f;
+    float4 a1 = *reinterpret_cast<const float4*>(x1), a2 = *reinterpret_cast<const float4*>(x2);
 #pragma unroll 2
-      for (int s4 = 0; s4 < D / 16; ++s4) {
-        const float4 y = *reinterpret_cast<const float4*>(xb + 4 * s4);
-        if (prod == 2) {
-          const float4 m = *reinterpret_cast<const float4*>(sb + 4 * s4);
-          mdm = fmaf(m.x, y.x, mdm);
-          mdm = fmaf(m.y, y.y, mdm);
-          mdm = fmaf(m.z, y.z, mdm);
-          mdm = fmaf(m.w, y.w, mdm);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const float4 x = *reinterpret_cast<const float4*>(sY + (16 * mb + l16) * S1 + g * (D / 4) + 4 * s4);
-          acc[mb] = mfma4(x.x, y.x, acc[mb]);
-          acc[mb] = mfma4(x.y, y.y, acc[mb]);
-          acc[mb] = mfma4(x.z, y.z, acc[mb]);
-          acc[mb] = mfma4(x.w, y.w, acc[mb]);
-        }
+    for (int s4 = 0; s4 < D / 16; ++s4) {
+      const float4 c1 = a1, c2 = a2;
+      if (s4 + 1 < D / 16) {
+        a1 = *reinterpret_cast<const float4*>(x1 + 16 * (s4 + 1));
+        a2 = *reinterpret_cast<const float4*>(x2 + 16 * (s4 + 1));
       }
+      mdm = fmaf(c1.x, c2.x, mdm);
+      mdm = fmaf(c1.y, c2.y, mdm);
+      mdm = fmaf(c1.z, c2.z, mdm);
+      mdm = fmaf(c1.w, c2.w, mdm);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int ro = (16 * mb + l16) * S1 + 16 * s4 + 4 * g;
+        const float4 y0 = *reinterpret_cast<const float4*>(sY + ro);
+        const float4 y1 = *reinterpret_cast<const float4*>(sY + C * S1 + ro);
+        const float4 y2 = *reinterpret_cast<const float4*>(sY + 2 * C * S1 + ro);
+        acc[0][mb] = mfma4(y0.x, c1.x, acc[0][mb]);
+        acc[1][mb] = mfma4(y1.x, c1.x, acc[1][mb]);
+        acc[2][mb] = mfma4(y2.x, c2.x, acc[2][mb]);
+        acc[0][mb] = mfma4(y0.y, c1.y, acc[0][mb]);
+        acc[1][mb] = mfma4(y1.y, c1.y, acc[1][mb]);
+        acc[2][mb] = mfma4(y2.y, c2.y, acc[2][mb]);
+        acc[0][mb] = mfma4(y0.z, c1.z, acc[0][mb]);
+        acc[1][mb] = mfma4(y1.z, c1.z, acc[1][mb]);
+        acc[2][mb] = mfma4(y2.z, c2.z, acc[2][mb]);
+        acc[0][mb] = mfma4(y0.w, c1.w, acc[0][mb]);
+        acc[1][mb] = mfma4(y1.w, c1.w, acc[1][mb]);
+        acc[2][mb] = mfma4(y2.w, c2.w, acc[2][mb]);
+      }
+    }
+#pragma unroll
+    for (int pr = 0; pr < 3; ++pr) {
+      float* out = (pr == 0 ? io.SdO : pr == 1 ? io.SdD : io.DsD) + sh * CD;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[(16 * mb + 4 * g + r) * D + 16 * nb + l16] = acc[mb][r];
+        for (int r = 0; r < 4; ++r) out[(16 * mb + 4 * g + r) * D + n] = acc[pr][mb][r];
     }
-    if (prod == 2) {  // fixed-order block reduction of <S, dS'>
-      __syncthreads();  // every wave is done reading sY
-      sY[tid] = mdm;
-      __syncthreads();
-      for (int wd = 128; wd >= 1; wd >>= 1) {
-        if (tid < wd) sY[tid] = sY[tid] + sY[tid + wd];
-        __syncthreads();
-      }
-      if (tid == 0) io.MdM[sh] = sY[0];
-    }
+    // <S, dS'>: wave butterfly, then the 8 wave sums in ascending order
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mdm = mdm + __shfl_xor(mdm, off, 64);
+    if (lane == 0) red[w] = mdm;
     __syncthreads();
+    if (tid == 0) {
+      float t = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t = t + red[q];
+      io.MdM[sh] = t;
+    }
   }
 }
 
@@ -1865,7 +1969,10 @@ __global__ __launch_bounds__(256) void k_bwd_scan_m(BwdIO io, int64_t nblocks, i
   const int64_t slot0 = io.cu_chunks[n];
   if (slot0 + nchunks > io.max_state_slot) return;
 
-  for (int e = tid; e < TILE * D; e += 256) {
+  static_assert((TILE * D) % 256 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (TILE * D) / 256; ++e_) {
+    const int e = tid + 256 * e_;
     const int i = e / TILE, jj = e % TILE;
     sS[jj * S1 + i] = io.dhT ? io.dhT[nh * DD + static_cast<int64_t>(i) * D + j0 + jj] : 0.0f;
   }
@@ -1893,7 +2000,10 @@ __global__ __launch_bounds__(256) void k_bwd_scan_m(BwdIO io, int64_t nblocks, i
     __syncthreads();
     const float glast = sG[C - 1];
     if (tid < C) sLam[tid] = expf(glast - sG[tid]);
-    for (int e = tid; e < C * TILE; e += 256) {
+    static_assert((C * TILE) % 256 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * TILE) / 256; ++e_) {
+    const int e = tid + 256 * e_;
       const int p = e / TILE, jj = e % TILE;
       const int pc = p < rows ? p : rows - 1;
       const float x = expf(sG[p]) * io.dO[((tok0 + pc) * io.H_v + h) * D + j0 + jj];
@@ -2008,14 +2118,17 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     const float bx = io.beta[(tok0 + crow(tid)) * io.H_v + h];
     sB[tid] = tid < L ? bx : 0.0f;
   }
-  for (int e = tid; e < C * (D / 4); e += 512) {
+  static_assert((C * (D / 4)) % 512 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
+    const int e = tid + 512 * e_;
     const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
     const float4 k4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
     const float4 o4 = *reinterpret_cast<const float4*>(dO + pc * vs + 4 * i4);
     const float4 d4 = *reinterpret_cast<const float4*>(Dl + p * D + 4 * i4);
-    *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) = p < L ? k4 : z4;
-    *reinterpret_cast<float4*>(sO + p * KS + 4 * i4) = p < L ? o4 : z4;
-    *reinterpret_cast<float4*>(sD + p * KS + 4 * i4) = p < L ? d4 : z4;
+    *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) = sel4(p < L, k4, z4);
+    *reinterpret_cast<float4*>(sO + p * KS + 4 * i4) = sel4(p < L, o4, z4);
+    *reinterpret_cast<float4*>(sD + p * KS + 4 * i4) = sel4(p < L, d4, z4);
   }
   __syncthreads();
   const float glast = sG[C - 1];
@@ -2038,10 +2151,13 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     }
   }
   __syncthreads();  // dO and Delta are dead
-  for (int e = tid; e < C * (D / 4); e += 512) {
+  static_assert((C * (D / 4)) % 512 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
+    const int e = tid + 512 * e_;
     const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
     const float4 q4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
-    *reinterpret_cast<float4*>(sQ + p * KS + 4 * i4) = p < L ? q4 : z4;
+    *reinterpret_cast<float4*>(sQ + p * KS + 4 * i4) = sel4(p < L, q4, z4);
   }
   __syncthreads();
   // ---- QK (r <= p) and KK Gam (r < p)
@@ -2212,7 +2328,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
       sdG[pp] = pp < L ? dgp : 0.0f;
     }
   }
-  for (int e = tid; e < C * C; e += 512) {
+  static_assert((C * C) % 512 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * C) / 512; ++e_) {
+    const int e = tid + 512 * e_;
     const int pp = e / C, q = e % C;
     const int hi = pp > q ? pp : q, lo = pp > q ? q : pp;
     const float f = sZ[hi * CS + lo] * sB[hi] * expf(sG[hi] - sG[lo]);
@@ -2235,7 +2354,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
       if (pp < L) io.dkv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + col] = ak[r];
     }
   }
-  for (int e = tid; e < C * D; e += 512) {
+  static_assert((C * D) % 512 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * D) / 512; ++e_) {
+    const int e = tid + 512 * e_;
     const int pp = e / D, j = e % D;
     if (pp < L) io.dv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + j] = sB[pp] * sY[pp * YS + D + j];
   }
@@ -2371,6 +2493,9 @@ constexpr int kTile128 = 32;  // state rows per k_scan block at d = 128
 
 template <int D>
 constexpr int scan_tile() { return D == 128 ? kTile128 : D; }
+
+// Blocks of the persistent backward kernels: one per CU.
+constexpr int64_t kPersistentBlocks = 256;
 
 // Value heads per k_rec block: as many of the group as fit in 8 waves and
 // divide the group evenly (the group has at most 8 heads).
@@ -2599,8 +2724,12 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   if (cnt.chunks > 0) {
     {
       Timed t_("k_bwd_mm", st);
-      if constexpr (D == 128)
-        hipLaunchKernelGGL((k_bwd_mm_m<C>), cgrid, dim3(256), 0, st, b);
+      if constexpr (D == 128) {
+        const int64_t nitems = cnt.chunks * s->H_v;
+        const int64_t nblk = nitems < kPersistentBlocks ? nitems : kPersistentBlocks;
+        hipLaunchKernelGGL((k_bwd_mm_m<C>), dim3(static_cast<unsigned>(nblk)), dim3(512), 0, st, b,
+                           nitems);
+      }
       else
         hipLaunchKernelGGL((k_bwd_mm<D, C>), cgrid, dim3(256), 0, st, b);
     }
@@ -2650,7 +2779,7 @@ int gdn_cache_init(const gdn_shape_t* shape, int32_t n_seqs, const float* h0, gd
                    void* stream) {
   int rc = gdn::check_shape(shape);
   if (rc != GDN_OK) return rc;
-  if (n_seqs < 0) return GDN_ERR_INVALID_ARG;
+  if (n_seqs < 0 || !gdn::aligned16({h0})) return GDN_ERR_INVALID_ARG;
   if ((rc = gdn::check_cache(cache)) != GDN_OK) return rc;
   if (n_seqs == 0) return GDN_OK;
   const int64_t n_state =
@@ -2675,6 +2804,7 @@ int gdn_prefill(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seql
   gdn::Counts cnt;
   if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
   if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, h0, o, hT})) return GDN_ERR_INVALID_ARG;
   if (cache && (rc = gdn::check_cache(cache)) != GDN_OK) return rc;
   const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_PREFILL);
   if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
@@ -2695,6 +2825,7 @@ int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q, con
   if (n_seqs < 0) return GDN_ERR_INVALID_ARG;
   if ((rc = gdn::check_cache(cache)) != GDN_OK) return rc;
   if (n_seqs > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, o})) return GDN_ERR_INVALID_ARG;
   if (n_seqs > 65535) return GDN_ERR_UNSUPPORTED;  // grid.x of the per-sequence launches
   bool resync = true;
   if (pos_host) {
@@ -2729,6 +2860,8 @@ int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seql
                     !dg))
     return GDN_ERR_INVALID_ARG;
   if (n_seqs > 0 && (!hT || !dh0)) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, h0, dO, dhT, o, hT, dq, dk, dv, dbeta, dg, dh0}))
+    return GDN_ERR_INVALID_ARG;
   const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_FWD_BWD);
   if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (n_seqs == 0) return GDN_OK;

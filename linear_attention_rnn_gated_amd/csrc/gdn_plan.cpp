@@ -94,7 +94,15 @@ int check_cache(const gdn_cache_t* c) {
   if (!c || !c->S_run || !c->S_chunk || !c->kbuf || !c->vbuf || !c->bbuf || !c->gbuf ||
       !c->pos)
     return GDN_ERR_INVALID_ARG;
+  if (!aligned16({c->S_run, c->S_chunk, c->kbuf, c->vbuf, c->bbuf, c->gbuf, c->pos}))
+    return GDN_ERR_INVALID_ARG;
   return GDN_OK;
+}
+
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;  // NULL passes
+  return true;
 }
 
 }  // namespace gdn

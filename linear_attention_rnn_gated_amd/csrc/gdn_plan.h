@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <initializer_list>
 
 #include "gdn.h"
 
@@ -65,5 +66,7 @@ Layout layout(const gdn_shape_t* s, int32_t n_seqs, int64_t total_tokens, int op
 
 // Checks the pointer fields of a decode cache (all must be non-NULL).
 int check_cache(const gdn_cache_t* c);
+// True if every pointer is 16-byte aligned (NULL counts as aligned).
+bool aligned16(std::initializer_list<const void*> ptrs);
 
 }  // namespace gdn

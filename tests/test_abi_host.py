@@ -140,3 +140,16 @@ def test_cache_init_validation():
         B.GDN_ERR_INVALID_ARG
     assert L.gdn_cache_init(ctypes.byref(s), -1, None, ctypes.byref(bad), None) == \
         B.GDN_ERR_INVALID_ARG
+
+
+def test_misaligned_pointers_rejected():
+    s = good_shape()
+    L = B.lib()
+    cu = (ctypes.c_int32 * 2)(0, 10)
+    a, m = ctypes.c_void_p(16), ctypes.c_void_p(20)
+    st = L.gdn_prefill(ctypes.byref(s), 1, a, cu, a, a, m, a, a, None, a, None, None, a,
+                       1 << 40, None)
+    assert st == B.GDN_ERR_INVALID_ARG
+    cache = B.CacheStruct(16, 16, 16, 20, 16, 16, 16)
+    assert L.gdn_cache_init(ctypes.byref(s), 2, None, ctypes.byref(cache), None) == \
+        B.GDN_ERR_INVALID_ARG
