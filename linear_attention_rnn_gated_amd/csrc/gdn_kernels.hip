@@ -67,6 +67,11 @@ __device__ __forceinline__ float ldbuf(brsrc_t r, uint32_t voff, uint32_t soff, 
 __device__ __forceinline__ void stbuf(float x, brsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
 }
+__device__ __forceinline__ float4 ldbuf4(brsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return float4{__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                __uint_as_float(x[3])};
+}
 __device__ __forceinline__ float ldbuf(brsrc_t r, uint32_t voff, uint32_t soff, const bf16_t*) {
   const uint16_t x = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
@@ -1939,125 +1944,190 @@ __global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
   }
 }
 
-// Reverse scan of the state gradient on the matrix cores, per (sequence,
-// head, 32-row tile of d_v):  dDelta = E + diag(lam) K dS'^T  and
-// dS = gam_last dS' + (gam dO)^T Q - dDelta^T W.
+// Reverse scan of the state gradient on the matrix cores, one block of 8
+// waves per (sequence, value head):
+//   dDelta = E + diag(lam) K dS'^T,   dS = gam_last dS' + (gam dO)^T Q - dDelta^T W.
+// The state gradient is held transposed (rows i of d_k, columns j of d_v) in
+// accumulator layout: wave w owns columns j = 16 w .. 16 w + 15 as eight
+// 16 x 16 tiles (ib = 0..7).  In that layout accumulator register r of lane
+// group g is the B operand of the k-step that lane group g supplies as
+// k = 16 ib + 4 g + r, so dDelta (k = i) takes the state straight from
+// registers, and the update (k = p) takes dDelta and gam dO, held the same way,
+// straight from registers too.  Per chunk, K (rows p), Q^T and W^T (rows i)
+// sit in LDS and the next chunk's copies are fetched into registers while the
+// current one computes.
 template <int C>
-__global__ __launch_bounds__(256) void k_bwd_scan_m(BwdIO io, int64_t nblocks, int64_t nb8) {
-  constexpr int D = 128, TILE = 32, NTILE = D / TILE, S1 = D + 4, S2 = C + 4;
-  static_assert(C == 64, "tiling assumes C = 64");
-  __shared__ __attribute__((aligned(16))) float sS[TILE * S1];   // dS' rows j, columns i
-  __shared__ __attribute__((aligned(16))) float sDt[TILE * S2];  // -dDelta^T [j][p]
-  __shared__ __attribute__((aligned(16))) float sOt[TILE * S2];  // (gam dO)^T [j][p]
-  __shared__ float sG[C], sLam[C];
+__global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
+  constexpr int D = 128, KS = D + 4, TS = C + 4, NQ = C * D / 4 / 512;  // float4 per thread
+  static_assert(C == 64 && NQ == 4, "tiling assumes C = 64, D = 128");
+  __shared__ __attribute__((aligned(16))) float sK[C * KS];   // K[p][i]
+  __shared__ __attribute__((aligned(16))) float sQT[D * TS];  // Q[p][i] at [i][p]
+  __shared__ __attribute__((aligned(16))) float sWT[D * TS];  // W[p][i] at [i][p]
+  __shared__ float sGam[C], sLam[C];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t vb = xcd_block(nb8);
-  if (vb >= nblocks) return;
-  const int tile = static_cast<int>(vb % NTILE);
-  const int h = static_cast<int>((vb / NTILE) % io.H_v);
-  const int n = static_cast<int>(vb / (NTILE * io.H_v));
+  const int64_t nh = blockIdx.x;
+  const int n = static_cast<int>(nh / io.H_v), h = static_cast<int>(nh % io.H_v);
   if (n >= io.N) return;
   const int hq = h / (io.H_v / io.H_qk);
-  const int j0 = tile * TILE;
   const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
-  const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
   const int64_t s0 = io.cu[n];
   const int64_t Lseq = static_cast<int64_t>(io.cu[n + 1]) - s0;
   if (Lseq < 0 || s0 < 0 || s0 + Lseq > io.T) return;
   const int64_t nchunks = (Lseq + C - 1) / C;
   const int64_t slot0 = io.cu_chunks[n];
   if (slot0 + nchunks > io.max_state_slot) return;
+  const int j = 16 * w + l16;  // this lane's column of d_v
+  const float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  static_assert((TILE * D) % 256 == 0, "whole rounds");
+  // Buffer offsets (bytes): a lane part in a VGPR, a wave-uniform part in an
+  // SGPR.  Rows past a partial chunk's end are outside the range of the
+  // chunk's K/Q and dO resources (range-checked lane offsets) and read 0.
+  const uint32_t fj = 4u * static_cast<uint32_t>(4 * g * D + j);   // (p or i = 4 g, j) of [.][D]
+  const uint32_t fq = 4u * static_cast<uint32_t>((tid >> 5) * 2 * D + 4 * (tid & 31));
+  const uint32_t fw = 4u * static_cast<uint32_t>((tid >> 5) * D + 4 * (tid & 31));
+  const uint32_t ostride = static_cast<uint32_t>(io.H_v) * D * 4u;  // dO row stride
+  const uint32_t fo = 4u * static_cast<uint32_t>(j) + static_cast<uint32_t>(4 * g) * ostride;
+  // chunk operands: this thread's rows p = tid / 32 + 16 m and column quad tid % 32
+  struct Ops {
+    float4 k[NQ], q[NQ], wv[NQ];
+    float gv, glast;  // G[tid] (tid < C) and G[C - 1]
+  };
+  auto rows_of = [&](int64_t c) { return static_cast<int>(Lseq - c * C < C ? Lseq - c * C : C); };
+  auto load_ops = [&](Ops& o, int64_t c) {
+    const int64_t sh = (slot0 + c) * io.H_v + h;
+    const int rows = rows_of(c);
+    const brsrc_t rq = make_rsrc(io.qk + (static_cast<int64_t>(hq) * io.T + s0 + c * C) * 2 * D,
+                                 static_cast<uint32_t>(rows) * 2 * D * 4u);
+    const brsrc_t rw = make_rsrc(io.W + sh * CD, C * D * 4u);
 #pragma unroll
-  for (int e_ = 0; e_ < (TILE * D) / 256; ++e_) {
-    const int e = tid + 256 * e_;
-    const int i = e / TILE, jj = e % TILE;
-    sS[jj * S1 + i] = io.dhT ? io.dhT[nh * DD + static_cast<int64_t>(i) * D + j0 + jj] : 0.0f;
-  }
-  __syncthreads();
-  v4f accS[2][2];  // rows j = 16 jb + 4 g + r, columns i = 32 w + 16 ib + l16
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) accS[jb][ib][r] = sS[(16 * jb + 4 * g + r) * S1 + 32 * w + 16 * ib + l16];
-
-  for (int64_t c = nchunks - 1; c >= 0; --c) {
-    const int64_t slot = slot0 + c;
-    const int64_t sh = slot * io.H_v + h;
-    const int64_t tok0 = s0 + c * C;
-    const int rows = static_cast<int>(Lseq - c * C < C ? Lseq - c * C : C);
-    float* dst = io.dstates + sh * DD;
-    for (int e = tid; e < TILE * D; e += 256) {
-      const int i = e / TILE, jj = e % TILE;
-      dst[static_cast<int64_t>(i) * D + j0 + jj] = sS[jj * S1 + i];
+    for (int m = 0; m < NQ; ++m) {
+      const uint32_t mq = fq + static_cast<uint32_t>(16 * m * 2 * D * 4);
+      o.k[m] = ldbuf4(rq, mq, 0u);
+      o.q[m] = ldbuf4(rq, mq + D * 4u, 0u);
+      o.wv[m] = ldbuf4(rw, fw, static_cast<uint32_t>(16 * m * D * 4));  // padded rows of W are 0
     }
-    if (tid < C) sG[tid] = io.G[sh * C + tid];
-    const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
-    __syncthreads();
-    const float glast = sG[C - 1];
-    if (tid < C) sLam[tid] = expf(glast - sG[tid]);
-    static_assert((C * TILE) % 256 == 0, "whole rounds");
+    o.gv = tid < C ? io.G[sh * C + tid] : 0.0f;
+    o.glast = io.G[sh * C + C - 1];
+  };
+  // E and dO of a chunk in accumulator layout: (p = 16 pb + 4 g + r, j)
+  auto load_ed = [&](float (&e)[4][4], float (&d)[4][4], int64_t c) {
+    const int64_t sh = (slot0 + c) * io.H_v + h;
+    const int rows = rows_of(c);
+    const brsrc_t re = make_rsrc(io.E + sh * CD, C * D * 4u);
+    const brsrc_t ro = make_rsrc(io.dO + ((s0 + c * C) * io.H_v + h) * D,
+                                 static_cast<uint32_t>(rows - 1) * ostride + D * 4u);
 #pragma unroll
-  for (int e_ = 0; e_ < (C * TILE) / 256; ++e_) {
-    const int e = tid + 256 * e_;
-      const int p = e / TILE, jj = e % TILE;
-      const int pc = p < rows ? p : rows - 1;
-      const float x = expf(sG[p]) * io.dO[((tok0 + pc) * io.H_v + h) * D + j0 + jj];
-      sOt[jj * S2 + p] = p < rows ? x : 0.0f;
-    }
-    // dDelta rows p = 16 w + 4 g + r, columns j = 16 jb + l16
-    const int pc = 16 * w + l16 < rows ? 16 * w + l16 : rows - 1;
-    const float* Ec = io.E + sh * CD;
-    v4f accD[2];
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      accD[jb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      accD[jb] = mma_nt<D>(accD[jb], kq + pc * 2 * D, sS + (16 * jb + l16) * S1);
-    }
-    __syncthreads();  // sLam ready; sS reads done
-    float* dDc = io.dD + sh * CD;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      v4f x;
+    for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = 16 * w + 4 * g + r;
-        const float e = Ec[p * D + j0 + 16 * jb + l16];
-        const float v = fmaf(sLam[p], accD[jb][r], e);
-        x[r] = p < rows ? v : 0.0f;
-        dDc[p * D + j0 + 16 * jb + l16] = x[r];
+        e[pb][r] = ldbuf(re, fj, static_cast<uint32_t>((16 * pb + r) * D * 4), static_cast<const float*>(nullptr));
+        d[pb][r] = ldbuf(ro, fo + static_cast<uint32_t>(16 * pb + r) * ostride, 0u,
+                         static_cast<const float*>(nullptr));
       }
-      *reinterpret_cast<v4f*>(sDt + (16 * jb + l16) * S2 + 16 * w + 4 * g) = -x;
+  };
+
+  // state gradient dS'^T tiles: (i = 16 ib + 4 g + r, j)
+  v4f st[8];
+  {
+    const brsrc_t rh = make_rsrc(io.dhT ? io.dhT + nh * DD : io.dh0, io.dhT ? D * D * 4u : 0u);
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)  // no dhT: an empty range reads 0
+        st[ib][r] = ldbuf(rh, fj, static_cast<uint32_t>((16 * ib + r) * D * 4), static_cast<const float*>(nullptr));
+  }
+
+  Ops nx;
+  if (nchunks > 0) load_ops(nx, nchunks - 1);
+  for (int64_t c = nchunks - 1; c >= 0; --c) {
+    const int64_t sh = (slot0 + c) * io.H_v + h;
+    const int rows = rows_of(c);
+    __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const int p = (tid >> 5) + 16 * m, i = 4 * (tid & 31);
+      *reinterpret_cast<float4*>(sK + p * KS + i) = nx.k[m];
+      sQT[(i + 0) * TS + p] = nx.q[m].x;
+      sQT[(i + 1) * TS + p] = nx.q[m].y;
+      sQT[(i + 2) * TS + p] = nx.q[m].z;
+      sQT[(i + 3) * TS + p] = nx.q[m].w;
+      sWT[(i + 0) * TS + p] = nx.wv[m].x;
+      sWT[(i + 1) * TS + p] = nx.wv[m].y;
+      sWT[(i + 2) * TS + p] = nx.wv[m].z;
+      sWT[(i + 3) * TS + p] = nx.wv[m].w;
     }
-    __syncthreads();
+    const float gcur = nx.gv, glast = nx.glast;
+    float ec[4][4], dc[4][4];  // land while dDelta is computed
+    load_ed(ec, dc, c);
+    if (tid < C) {
+      sLam[tid] = expf(glast - gcur);
+      sGam[tid] = expf(gcur);
+    }
+    if (c > 0) load_ops(nx, c - 1);  // the next chunk's operands land while this one computes
+    // this chunk's incoming state gradient
+    const brsrc_t rs = make_rsrc(io.dstates + sh * DD, D * D * 4u);
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rs, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+    __syncthreads();  // sGam, sLam ready
+    // dDelta tiles (p = 16 pb + 4 g + r, j): k = i from the state registers
+    v4f dd[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      dd[pb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib) {
+        const float4 a = *reinterpret_cast<const float4*>(sK + (16 * pb + l16) * KS + 16 * ib + 4 * g);
+        dd[pb] = mfma4(a.x, st[ib][0], dd[pb]);
+        dd[pb] = mfma4(a.y, st[ib][1], dd[pb]);
+        dd[pb] = mfma4(a.z, st[ib][2], dd[pb]);
+        dd[pb] = mfma4(a.w, st[ib][3], dd[pb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep operand reads per tile
+    }
+    const brsrc_t rd = make_rsrc(io.dD + sh * CD, C * D * 4u);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * pb + 4 * g + r;
+        const float v = fmaf(sLam[p], dd[pb][r], ec[pb][r]);
+        dd[pb][r] = p < rows ? v : 0.0f;
+        stbuf(dd[pb][r], rd, fj, static_cast<uint32_t>((16 * pb + r) * D * 4));
+        dc[pb][r] = sGam[p] * dc[pb][r];  // gam dO
+      }
+    // dS^T = gam_last dS'^T + Q^T (gam dO) - W^T dDelta: k = p from registers
     const float gl = expf(glast);
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int ib = 0; ib < 8; ++ib) {
+      v4f acc = gl * st[ib];
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        v4f acc = gl * accS[jb][ib];
-        const int col = 32 * w + 16 * ib + l16;
-        acc = mma_nn<C>(acc, sOt + (16 * jb + l16) * S2, kq + D + col, 2 * D, rows);
-        acc = mma_nn<C>(acc, sDt + (16 * jb + l16) * S2, io.W + sh * CD + col, D, C);
-        accS[jb][ib] = acc;
+      for (int pb = 0; pb < 4; ++pb) {
+        const float4 aq = *reinterpret_cast<const float4*>(sQT + (16 * ib + l16) * TS + 16 * pb + 4 * g);
+        acc = mfma4(aq.x, dc[pb][0], acc);
+        acc = mfma4(aq.y, dc[pb][1], acc);
+        acc = mfma4(aq.z, dc[pb][2], acc);
+        acc = mfma4(aq.w, dc[pb][3], acc);
       }
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sS[(16 * jb + 4 * g + r) * S1 + 32 * w + 16 * ib + l16] = accS[jb][ib][r];
-    __syncthreads();
+      for (int pb = 0; pb < 4; ++pb) {
+        const float4 aw = *reinterpret_cast<const float4*>(sWT + (16 * ib + l16) * TS + 16 * pb + 4 * g);
+        acc = mfma4(-aw.x, dd[pb][0], acc);
+        acc = mfma4(-aw.y, dd[pb][1], acc);
+        acc = mfma4(-aw.z, dd[pb][2], acc);
+        acc = mfma4(-aw.w, dd[pb][3], acc);
+      }
+      st[ib] = acc;
+      __builtin_amdgcn_sched_barrier(0);  // keep operand reads per tile
+    }
   }
-  for (int e = tid; e < TILE * D; e += 256) {
-    const int i = e / TILE, jj = e % TILE;
-    io.dh0[nh * DD + static_cast<int64_t>(i) * D + j0 + jj] = sS[jj * S1 + i];
-  }
+  const brsrc_t r0 = make_rsrc(io.dh0 + nh * DD, D * D * 4u);
+#pragma unroll
+  for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) stbuf(st[ib][r], r0, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
 }
 
 // Sum of a value over the 4 lanes of a quad (lanes 4k .. 4k+3 of a wave) as
@@ -2087,7 +2157,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   __shared__ __attribute__((aligned(16))) float sZ[C * CS];    // Z, later dA
   __shared__ __attribute__((aligned(16))) float sK[C * KS];
   __shared__ __attribute__((aligned(16))) float sY[2 * C * KS];  // dO | Delta, then Q, then Y
-  __shared__ float sG[C], sB[C], sGam[C], sLam[C], sdG[C], sdB[C], skd[C];
+  __shared__ float sG[C], sB[C], sGam[C], sLam[C], sdB[C], skd[C];
+  __shared__ __attribute__((aligned(16))) float sdG[C];
   static_assert(C * YS <= 2 * C * KS, "Y must fit");
   float* sO = sY;
   float* sD = sY + C * KS;
@@ -2361,13 +2432,32 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     const int pp = e / D, j = e % D;
     if (pp < L) io.dv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + j] = sB[pp] * sY[pp * YS + D + j];
   }
+  // dg: reverse running sum over the chunk (p descending), taken by one lane
+  // from registers; then every lane stores its token
   if (tid == 0) {
-    float acc = 0.0f;
-    for (int pp = L - 1; pp >= 0; --pp) {
-      acc = acc + sdG[pp];
-      io.dg[(tok0 + pp) * io.H_v + h] = acc;
-      io.dbeta[(tok0 + pp) * io.H_v + h] = sdB[pp];
+    float x[C];
+#pragma unroll
+    for (int q4 = 0; q4 < C / 4; ++q4) {
+      const float4 t4 = *reinterpret_cast<const float4*>(sdG + 4 * q4);
+      x[4 * q4] = t4.x;
+      x[4 * q4 + 1] = t4.y;
+      x[4 * q4 + 2] = t4.z;
+      x[4 * q4 + 3] = t4.w;
     }
+    float acc = 0.0f;
+#pragma unroll
+    for (int pp = C - 1; pp >= 0; --pp) {  // rows at or past L hold 0: acc + 0 is exact
+      acc = acc + x[pp];
+      x[pp] = acc;
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < C / 4; ++q4)
+      *reinterpret_cast<float4*>(sdG + 4 * q4) = float4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+  }
+  __syncthreads();
+  if (tid < L) {
+    io.dg[(tok0 + tid) * io.H_v + h] = sdG[tid];
+    io.dbeta[(tok0 + tid) * io.H_v + h] = sdB[tid];
   }
 }
 
@@ -2713,9 +2803,8 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   if (sblocks > 0) {
     Timed t_("k_bwd_scan", st);
     if constexpr (D == 128) {
-      const int64_t nb8 = (sblocks + 7) / 8 * 8;
-      hipLaunchKernelGGL((k_bwd_scan_m<C>), dim3(static_cast<unsigned>(nb8)), dim3(256), 0, st, b,
-                         sblocks, nb8);
+      hipLaunchKernelGGL((k_bwd_scan_m<C>), dim3(static_cast<unsigned>(N * s->H_v)), dim3(512), 0,
+                         st, b);
     } else {
       hipLaunchKernelGGL((k_bwd_scan<D, C, TILE>), dim3(static_cast<unsigned>(sblocks)),
                          dim3(256), 0, st, b);
