@@ -434,15 +434,9 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
 }
 
 // ---------------------------------------------------------------------------
-// B, part 2 on the matrix cores (d = 128, C = 64): the same step as k_scan,
-//   Delta = U - W S^T            (64 x 32 x 128 per 32-row tile)
-//   S'    = gam S + Dt^T Khat    (32 x 128 x 64),  Dt_p = Delta_p * lam_p,
-// with v_mfma_f32_16x16x4_f32.  Fixed reduction order: Delta starts from U and
-// adds the 32 products of i-steps s = 0..31, lane group g supplying i =
-// 32 g + s; S' starts from gam * S and adds the 16 products of p-steps s =
-// 0..15, group g supplying p = 16 g + s.  Four waves: wave w owns rows
-// p in [16w, 16w + 16) of Delta and columns i in [32w, 32w + 32) of S'.
-// The prefill scan and the decode resync both run this kernel.
+// Matrix-core helpers.  mfma4 is v_mfma_f32_16x16x4_f32 on one 16 x 16 tile:
+// lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], and holds
+// D[4 (l / 16) + r][l % 16] in accumulator register r.
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
@@ -457,29 +451,39 @@ __device__ __forceinline__ int64_t xcd_block(int64_t nb8) {
   return (b % 8) * (nb8 / 8) + b / 8;
 }
 
+// B, part 2 on the matrix cores (d = 128, C = 64): the chunk-state scan
+//   Delta = U - W S^T,   S' = gam_C S + sum_p lam_p Delta_p k_p^T
+// (gam_C = exp(G_C), lam_p = exp(G_C - G_p)), sequential over the chunks of a
+// sequence.  A block of 4 waves owns 64 columns j of d_v of one (sequence,
+// head); wave w holds S^T (rows i of d_k, its 16 columns j) as eight 16 x 16
+// accumulator tiles.  In that layout accumulator register r of lane group g
+// is the B operand of the k-step in which lane group g supplies
+// k = 16 b + 4 g + r, so both contractions take their B operand straight from
+// registers: Delta (k = i) from the state, S' (k = p) from lam * Delta.
+// Summation orders: Delta starts from U and adds the k-steps (ib = 0..7,
+// r = 0..3); S' starts from gam_C S and adds the k-steps (pb = 0..3,
+// r = 0..3).  W (rows p) and K^T (rows i) of a chunk sit in LDS; the next
+// chunk's W, K, U and G are fetched into registers while the current chunk
+// computes.  Decode resync runs this same kernel on the chunk buffers.
 template <int C, int MODE>
 __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, int64_t nb8) {
-  constexpr int D = 128, TILE = 32, NTILE = D / TILE;
-  constexpr int SS = D + 4;  // row stride of sS (floats)
-  constexpr int DS = C + 4;  // row stride of sDt
-  static_assert(C == 64, "tiling assumes C = 64");
+  constexpr int D = 128, WS = D + 4, TS = C + 4, NQ = C * D / 4 / 256;  // float4 per thread
+  static_assert(C == 64 && NQ == 8, "tiling assumes C = 64, D = 128");
   constexpr bool RESYNC = MODE == kResync;
-  __shared__ __attribute__((aligned(16))) float sS[TILE * SS];   // S[j][i] of the tile
-  __shared__ __attribute__((aligned(16))) float sDt[TILE * DS];  // Dt[j][p]
-  __shared__ float sG[C];
+  __shared__ __attribute__((aligned(16))) float sW[C * WS];   // W[p][i]
+  __shared__ __attribute__((aligned(16))) float sKT[D * TS];  // K[p][i] at [i][p]
   __shared__ float sLam[C];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int l16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t vb = xcd_block(nb8);
   if (vb >= nblocks) return;
-  const int tile = static_cast<int>(vb % NTILE);
-  const int h = static_cast<int>((vb / NTILE) % io.H_v);
-  const int n = static_cast<int>(vb / (NTILE * io.H_v));
+  const int half = static_cast<int>(vb % 2);
+  const int h = static_cast<int>((vb / 2) % io.H_v);
+  const int n = static_cast<int>(vb / (2 * io.H_v));
   if (n >= io.N) return;
   const int hq = h / (io.H_v / io.H_qk);
-  const int j0 = tile * TILE;
-  const int64_t DD = static_cast<int64_t>(D) * D;
+  const int j = 64 * half + 16 * w + l16;  // this lane's column of d_v
+  const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
   const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
 
   int64_t tok0 = 0, nsteps = 1, L = 0, slot0 = 0, fslot0 = 0, nchunks = 0;
@@ -496,188 +500,165 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
     fslot0 = MODE == kAll ? slot0 : io.cu_full[n];
     if (slot0 + nchunks > io.max_state_slot || fslot0 + nsteps > io.max_full_slot) return;
   }
+  // buffer offsets (bytes): lane part in a VGPR, wave-uniform part in an SGPR
+  const uint32_t fj = 4u * static_cast<uint32_t>(4 * g * D + j);  // (row 4 g, column j) of [.][D]
+  const int r0 = 8 * (tid >> 5), cq = tid & 31;  // this thread's rows r0 .. r0 + 7, column quad cq
+  const uint32_t fq = 4u * static_cast<uint32_t>(r0 * D + 4 * cq);
+  const uint32_t kst = RESYNC ? static_cast<uint32_t>(io.H_qk) * D * 4u : 2 * D * 4u;  // key row stride
+  const uint32_t fk = static_cast<uint32_t>(r0) * kst + 16u * cq;
 
-  const float* src = RESYNC ? io.S_chunk + nh * DD : (io.h0 ? io.h0 + nh * DD : nullptr);
-  static_assert((TILE * D) % 256 == 0, "whole rounds");
-#pragma unroll
-  for (int e_ = 0; e_ < (TILE * D) / 256; ++e_) {
-    const int e = tid + 256 * e_;
-    const int i = e / TILE, jj = e % TILE;
-    sS[jj * SS + i] = src ? src[static_cast<int64_t>(i) * D + j0 + jj] : 0.0f;
-  }
-  __syncthreads();
-  // this wave's S' tiles in accumulator layout: (j = 16 jb + 4 g + r, i = 32 w + 16 ib + l16)
-  v4f accS[2][2];
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        accS[jb][ib][r] = sS[(jb * 16 + 4 * g + r) * SS + 32 * w + 16 * ib + l16];
-
-  // Operands of one chunk step, loaded one step ahead (VMEM loads complete in
-  // order, so the next step's loads overlap this step's matrix work).
-  // W, U and G of a chunk step are loaded one step ahead (VMEM loads complete
-  // in order, so they overlap the previous step's matrix work); Khat is loaded
-  // at the start of its own step and lands while Delta is computed.
-  struct StepOps {
-    float4 wa[8];      // -W rows 16 w + l16, i = 32 g + 4 s4 + (0..3)
-    float u[2][4];     // U rows 16 w + 4 g + r, columns 16 jb + l16 of the tile
-    float gv;          // G[tid] (tid < C)
+  // one chunk step's operands: W and K rows p = r0 + m, column quad cq; U in
+  // accumulator layout (p = 16 pb + 4 g + r, j); G
+  struct Ops {
+    float4 w[NQ], k[NQ];
+    float u[4][4];
+    float gv, glast;
   };
-  auto load_ops = [&](StepOps& o, int64_t c) {
+  auto load_ops = [&](Ops& o, int64_t c) {
     const int64_t fs = fslot0 + c;
-    const float* Wc = io.W + (fs * io.H_v + h) * static_cast<int64_t>(C) * D;
-    const float* Uc = io.U + (fs * io.H_v + h) * static_cast<int64_t>(C) * D;
-    const float* wrow = Wc + static_cast<int64_t>(16 * w + l16) * D + 32 * g;
-#pragma unroll
-    for (int s4 = 0; s4 < 8; ++s4) o.wa[s4] = *reinterpret_cast<const float4*>(wrow + 4 * s4);
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        o.u[jb][r] = Uc[static_cast<int64_t>(16 * w + 4 * g + r) * D + j0 + 16 * jb + l16];
-    o.gv = tid < C ? io.G[(fs * io.H_v + h) * C + tid] : 0.0f;
-  };
-  auto load_khat = [&](float (&kb)[16][2], int64_t c) {
-    const int64_t ktok0 = RESYNC ? static_cast<int64_t>(n) * C : tok0 + c * C;
-    int64_t kst;
-    const float* krow = key_rows<D, RESYNC>(io.khat, io.T, io.H_qk, hq, ktok0, kst);
+    const int64_t sh = fs * io.H_v + h;
     const int rows = RESYNC ? C : static_cast<int>(L - c * C < C ? L - c * C : C);
+    const float* kb = RESYNC ? io.khat + (static_cast<int64_t>(n) * C * io.H_qk + hq) * D
+                             : io.khat + (static_cast<int64_t>(hq) * io.T + tok0 + c * C) * 2 * D;
+    const brsrc_t rk = make_rsrc(kb, static_cast<uint32_t>(rows) * kst);  // rows past the end read 0
+    const brsrc_t rw = make_rsrc(io.W + sh * CD, C * D * 4u);
+    const brsrc_t ru = make_rsrc(io.U + sh * CD, C * D * 4u);
 #pragma unroll
-    for (int pq = 0; pq < 16; ++pq) {
-      const int p = 16 * g + pq;
-      const int pc = p < rows ? p : rows - 1;  // in bounds; zeroed below
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        const float x = krow[pc * kst + 32 * w + 16 * ib + l16];
-        kb[pq][ib] = p < rows ? x : 0.0f;
-      }
+    for (int m = 0; m < NQ; ++m) {
+      o.w[m] = ldbuf4(rw, fq, static_cast<uint32_t>(m * D * 4));
+      o.k[m] = ldbuf4(rk, fk + static_cast<uint32_t>(m) * kst, 0u);
     }
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        o.u[pb][r] = ldbuf(ru, fj, static_cast<uint32_t>((16 * pb + r) * D * 4), static_cast<const float*>(nullptr));
+    o.gv = tid < C ? io.G[sh * C + tid] : 0.0f;
+    o.glast = io.G[sh * C + C - 1];
   };
-  StepOps cur;
-  if (nsteps > 0) load_ops(cur, 0);
 
+  // S^T tiles (i = 16 ib + 4 g + r, j)
+  v4f st[8];
+  {
+    const float* src = RESYNC ? io.S_chunk + nh * DD : (io.h0 ? io.h0 + nh * DD : nullptr);
+    const brsrc_t rs = make_rsrc(src ? src : io.W, src ? D * D * 4u : 0u);  // no h0: reads 0
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        st[ib][r] = ldbuf(rs, fj, static_cast<uint32_t>((16 * ib + r) * D * 4), static_cast<const float*>(nullptr));
+  }
+  auto store_state = [&](float* dst) {
+    const brsrc_t rd = make_rsrc(dst, D * D * 4u);
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rd, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+  };
+
+  Ops nx;
+  if (nsteps > 0) load_ops(nx, 0);
   for (int64_t c = 0; c < nsteps; ++c) {
-    if (!RESYNC) {  // chunk-start state of chunk c
-      float* dst = io.states + ((slot0 + c) * io.H_v + h) * DD;
-      for (int e = tid; e < TILE * D; e += 256) {
-        const int i = e / TILE, jj = e % TILE;
-        dst[static_cast<int64_t>(i) * D + j0 + jj] = sS[jj * SS + i];
-      }
-    }
     const int64_t fs = fslot0 + c;
-    if (tid < C) sG[tid] = cur.gv;
-    float kb[16][2];
-    load_khat(kb, c);
-    StepOps nxt;
-    if (c + 1 < nsteps) load_ops(nxt, c + 1);
+    __syncthreads();  // the previous step's LDS reads are done
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) *reinterpret_cast<float4*>(sW + (r0 + m) * WS + 4 * cq) = nx.w[m];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {  // K^T: four consecutive rows p per 16-byte store
+      const float4* k4 = nx.k + 4 * hh;
+      float* dst = sKT + (4 * cq) * TS + r0 + 4 * hh;
+      *reinterpret_cast<float4*>(dst) = float4{k4[0].x, k4[1].x, k4[2].x, k4[3].x};
+      *reinterpret_cast<float4*>(dst + TS) = float4{k4[0].y, k4[1].y, k4[2].y, k4[3].y};
+      *reinterpret_cast<float4*>(dst + 2 * TS) = float4{k4[0].z, k4[1].z, k4[2].z, k4[3].z};
+      *reinterpret_cast<float4*>(dst + 3 * TS) = float4{k4[0].w, k4[1].w, k4[2].w, k4[3].w};
+    }
+    const float glast = nx.glast;
+    if (tid < C) sLam[tid] = expf(glast - nx.gv);
+    float u[4][4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[pb][r] = nx.u[pb][r];
+    if (c + 1 < nsteps) load_ops(nx, c + 1);  // lands while this step computes
+    if (!RESYNC) store_state(io.states + ((slot0 + c) * io.H_v + h) * DD);  // chunk-start state
     __syncthreads();
-    const float glast = sG[C - 1];
-    if (tid < C) sLam[tid] = expf(glast - sG[tid]);
-    // ---- Delta rows p = 16 w + 4 g + r, columns j = 16 jb + l16
-    v4f accD[2];
+    // ---- Delta tiles (p = 16 pb + 4 g + r, j) = U - W S^T, k = i
+    // (the four tiles' chains are interleaved; each keeps its own k order)
+    v4f dl[4];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) accD[jb][r] = cur.u[jb][r];
+      for (int r = 0; r < 4; ++r) dl[pb][r] = u[pb][r];
 #pragma unroll
-    for (int s4 = 0; s4 < 8; ++s4) {
-      const float4 wa = cur.wa[s4];
+    for (int ib = 0; ib < 8; ++ib) {
+      float4 a[4];
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const float4 sb = *reinterpret_cast<const float4*>(sS + (16 * jb + l16) * SS + 32 * g + 4 * s4);
-        accD[jb] = mfma4(-wa.x, sb.x, accD[jb]);
-        accD[jb] = mfma4(-wa.y, sb.y, accD[jb]);
-        accD[jb] = mfma4(-wa.z, sb.z, accD[jb]);
-        accD[jb] = mfma4(-wa.w, sb.w, accD[jb]);
-      }
+      for (int pb = 0; pb < 4; ++pb)
+        a[pb] = *reinterpret_cast<const float4*>(sW + (16 * pb + l16) * WS + 16 * ib + 4 * g);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(-a[pb].x, st[ib][0], dl[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(-a[pb].y, st[ib][1], dl[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(-a[pb].z, st[ib][2], dl[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(-a[pb].w, st[ib][3], dl[pb]);
+      __builtin_amdgcn_sched_barrier(0);  // keep operand reads per k block
     }
     if (MODE == kAll) {
+      const brsrc_t rd = make_rsrc(io.Dl + (fs * io.H_v + h) * CD, C * D * 4u);
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+      for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          io.Dl[((fs * io.H_v + h) * C + 16 * w + 4 * g + r) * static_cast<int64_t>(D) + j0 + 16 * jb + l16] =
-              accD[jb][r];
+        for (int r = 0; r < 4; ++r) stbuf(dl[pb][r], rd, fj, static_cast<uint32_t>((16 * pb + r) * D * 4));
     }
-    __syncthreads();  // sLam ready; every wave is done reading sS
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      v4f x;
+    for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = accD[jb][r] * sLam[16 * w + 4 * g + r];
-      *reinterpret_cast<v4f*>(sDt + (16 * jb + l16) * DS + 16 * w + 4 * g) = x;
-    }
-    __syncthreads();
-    // ---- S' = gam S + Dt^T Khat, rows j = 16 jb + 4 g + r, columns i = 32 w + 16 ib + l16
+      for (int r = 0; r < 4; ++r) dl[pb][r] = dl[pb][r] * sLam[16 * pb + 4 * g + r];
+    // ---- S'^T tiles (i, j) = gam_C S^T + K^T (lam Delta), k = p
     const float gam = expf(glast);
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int ib = 0; ib < 8; ++ib) st[ib] = gam * st[ib];
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
+    for (int pb = 0; pb < 4; ++pb) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accS[jb][ib][r] = gam * accS[jb][ib][r];
+      for (int h2 = 0; h2 < 2; ++h2) {  // two groups of four tiles
+        float4 a[4];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      float4 da[2];
+        for (int q = 0; q < 4; ++q)
+          a[q] = *reinterpret_cast<const float4*>(sKT + (16 * (4 * h2 + q) + l16) * TS + 16 * pb + 4 * g);
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-        da[jb] = *reinterpret_cast<const float4*>(sDt + (16 * jb + l16) * DS + 16 * g + 4 * s4);
+        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].x, dl[pb][0], st[4 * h2 + q]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].y, dl[pb][1], st[4 * h2 + q]);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          const float a = q == 0 ? da[jb].x : q == 1 ? da[jb].y : q == 2 ? da[jb].z : da[jb].w;
+        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].z, dl[pb][2], st[4 * h2 + q]);
 #pragma unroll
-          for (int ib = 0; ib < 2; ++ib) accS[jb][ib] = mfma4(a, kb[4 * s4 + q][ib], accS[jb][ib]);
-        }
+        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].w, dl[pb][3], st[4 * h2 + q]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sS[(jb * 16 + 4 * g + r) * SS + 32 * w + 16 * ib + l16] = accS[jb][ib][r];
-    __syncthreads();
-    if (c + 1 < nsteps) cur = nxt;
   }
 
   if (RESYNC) {
-    float* d1 = io.S_chunk + nh * DD;
-    float* d2 = io.S_run + nh * DD;
-    for (int e = tid; e < TILE * D; e += 256) {
-      const int i = e / TILE, jj = e % TILE;
-      const float x = sS[jj * SS + i];
-      d1[static_cast<int64_t>(i) * D + j0 + jj] = x;
-      d2[static_cast<int64_t>(i) * D + j0 + jj] = x;
-    }
+    store_state(io.S_chunk + nh * DD);
+    store_state(io.S_run + nh * DD);
     return;
   }
   const bool tail = (L % C) != 0;
   if (MODE == kAll && tail) return;
-  static_assert((TILE * D) % 256 == 0, "whole rounds");
-#pragma unroll
-  for (int e_ = 0; e_ < (TILE * D) / 256; ++e_) {
-    const int e = tid + 256 * e_;
-    const int i = e / TILE, jj = e % TILE;
-    const int64_t off = static_cast<int64_t>(i) * D + j0 + jj;
-    const float x = sS[jj * SS + i];
-    if (tail) {
-      io.states[((slot0 + nsteps) * io.H_v + h) * DD + off] = x;  // tail chunk start
-      if (io.S_chunk) io.S_chunk[nh * DD + off] = x;
-    } else {
-      if (io.hT) io.hT[nh * DD + off] = x;
-      if (io.S_chunk) {
-        io.S_chunk[nh * DD + off] = x;
-        io.S_run[nh * DD + off] = x;
-      }
+  if (tail) {
+    store_state(io.states + ((slot0 + nsteps) * io.H_v + h) * DD);  // tail chunk start
+    if (io.S_chunk) store_state(io.S_chunk + nh * DD);
+  } else {
+    if (io.hT) store_state(io.hT + nh * DD);
+    if (io.S_chunk) {
+      store_state(io.S_chunk + nh * DD);
+      store_state(io.S_run + nh * DD);
     }
   }
-  if (io.pos && tile == 0 && tid == 0) io.pos[nh] = static_cast<int32_t>(L % C);
+  if (io.pos && half == 0 && tid == 0) io.pos[nh] = static_cast<int32_t>(L % C);
 }
 
 // ---------------------------------------------------------------------------
@@ -1984,11 +1965,12 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
   // SGPR.  Rows past a partial chunk's end are outside the range of the
   // chunk's K/Q and dO resources (range-checked lane offsets) and read 0.
   const uint32_t fj = 4u * static_cast<uint32_t>(4 * g * D + j);   // (p or i = 4 g, j) of [.][D]
-  const uint32_t fq = 4u * static_cast<uint32_t>((tid >> 5) * 2 * D + 4 * (tid & 31));
-  const uint32_t fw = 4u * static_cast<uint32_t>((tid >> 5) * D + 4 * (tid & 31));
+  const int r0 = 4 * (tid >> 5), cq = tid & 31;  // this thread's rows r0 .. r0 + 3, column quad cq
+  const uint32_t fq = 4u * static_cast<uint32_t>(r0 * 2 * D + 4 * cq);
+  const uint32_t fw = 4u * static_cast<uint32_t>(r0 * D + 4 * cq);
   const uint32_t ostride = static_cast<uint32_t>(io.H_v) * D * 4u;  // dO row stride
   const uint32_t fo = 4u * static_cast<uint32_t>(j) + static_cast<uint32_t>(4 * g) * ostride;
-  // chunk operands: this thread's rows p = tid / 32 + 16 m and column quad tid % 32
+  // chunk operands: this thread's rows p = r0 + m and column quad cq
   struct Ops {
     float4 k[NQ], q[NQ], wv[NQ];
     float gv, glast;  // G[tid] (tid < C) and G[C - 1]
@@ -2002,10 +1984,10 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     const brsrc_t rw = make_rsrc(io.W + sh * CD, C * D * 4u);
 #pragma unroll
     for (int m = 0; m < NQ; ++m) {
-      const uint32_t mq = fq + static_cast<uint32_t>(16 * m * 2 * D * 4);
+      const uint32_t mq = fq + static_cast<uint32_t>(m * 2 * D * 4);
       o.k[m] = ldbuf4(rq, mq, 0u);
       o.q[m] = ldbuf4(rq, mq + D * 4u, 0u);
-      o.wv[m] = ldbuf4(rw, fw, static_cast<uint32_t>(16 * m * D * 4));  // padded rows of W are 0
+      o.wv[m] = ldbuf4(rw, fw, static_cast<uint32_t>(m * D * 4));  // padded rows of W are 0
     }
     o.gv = tid < C ? io.G[sh * C + tid] : 0.0f;
     o.glast = io.G[sh * C + C - 1];
@@ -2045,17 +2027,20 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     const int rows = rows_of(c);
     __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-      const int p = (tid >> 5) + 16 * m, i = 4 * (tid & 31);
-      *reinterpret_cast<float4*>(sK + p * KS + i) = nx.k[m];
-      sQT[(i + 0) * TS + p] = nx.q[m].x;
-      sQT[(i + 1) * TS + p] = nx.q[m].y;
-      sQT[(i + 2) * TS + p] = nx.q[m].z;
-      sQT[(i + 3) * TS + p] = nx.q[m].w;
-      sWT[(i + 0) * TS + p] = nx.wv[m].x;
-      sWT[(i + 1) * TS + p] = nx.wv[m].y;
-      sWT[(i + 2) * TS + p] = nx.wv[m].z;
-      sWT[(i + 3) * TS + p] = nx.wv[m].w;
+    for (int m = 0; m < NQ; ++m) *reinterpret_cast<float4*>(sK + (r0 + m) * KS + 4 * cq) = nx.k[m];
+    {  // Q^T, W^T: four consecutive rows p per 16-byte store
+      const float4* q4 = nx.q;
+      const float4* w4 = nx.wv;
+      float* dq = sQT + (4 * cq) * TS + r0;
+      float* dw = sWT + (4 * cq) * TS + r0;
+      *reinterpret_cast<float4*>(dq) = float4{q4[0].x, q4[1].x, q4[2].x, q4[3].x};
+      *reinterpret_cast<float4*>(dq + TS) = float4{q4[0].y, q4[1].y, q4[2].y, q4[3].y};
+      *reinterpret_cast<float4*>(dq + 2 * TS) = float4{q4[0].z, q4[1].z, q4[2].z, q4[3].z};
+      *reinterpret_cast<float4*>(dq + 3 * TS) = float4{q4[0].w, q4[1].w, q4[2].w, q4[3].w};
+      *reinterpret_cast<float4*>(dw) = float4{w4[0].x, w4[1].x, w4[2].x, w4[3].x};
+      *reinterpret_cast<float4*>(dw + TS) = float4{w4[0].y, w4[1].y, w4[2].y, w4[3].y};
+      *reinterpret_cast<float4*>(dw + 2 * TS) = float4{w4[0].z, w4[1].z, w4[2].z, w4[3].z};
+      *reinterpret_cast<float4*>(dw + 3 * TS) = float4{w4[0].w, w4[1].w, w4[2].w, w4[3].w};
     }
     const float gcur = nx.gv, glast = nx.glast;
     float ec[4][4], dc[4][4];  // land while dDelta is computed
@@ -2075,17 +2060,22 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     // dDelta tiles (p = 16 pb + 4 g + r, j): k = i from the state registers
     v4f dd[4];
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      dd[pb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int pb = 0; pb < 4; ++pb) dd[pb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ib = 0; ib < 8; ++ib) {
-        const float4 a = *reinterpret_cast<const float4*>(sK + (16 * pb + l16) * KS + 16 * ib + 4 * g);
-        dd[pb] = mfma4(a.x, st[ib][0], dd[pb]);
-        dd[pb] = mfma4(a.y, st[ib][1], dd[pb]);
-        dd[pb] = mfma4(a.z, st[ib][2], dd[pb]);
-        dd[pb] = mfma4(a.w, st[ib][3], dd[pb]);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep operand reads per tile
+    for (int ib = 0; ib < 8; ++ib) {
+      float4 a[4];
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb)
+        a[pb] = *reinterpret_cast<const float4*>(sK + (16 * pb + l16) * KS + 16 * ib + 4 * g);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(a[pb].x, st[ib][0], dd[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(a[pb].y, st[ib][1], dd[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(a[pb].z, st[ib][2], dd[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(a[pb].w, st[ib][3], dd[pb]);
+      __builtin_amdgcn_sched_barrier(0);  // keep operand reads per k block
     }
     const brsrc_t rd = make_rsrc(io.dD + sh * CD, C * D * 4u);
 #pragma unroll
@@ -2100,34 +2090,45 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
       }
     // dS^T = gam_last dS'^T + Q^T (gam dO) - W^T dDelta: k = p from registers
     const float gl = expf(glast);
+    v4f dcv[4];
 #pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      v4f acc = gl * st[ib];
+    for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const float4 aq = *reinterpret_cast<const float4*>(sQT + (16 * ib + l16) * TS + 16 * pb + 4 * g);
-        acc = mfma4(aq.x, dc[pb][0], acc);
-        acc = mfma4(aq.y, dc[pb][1], acc);
-        acc = mfma4(aq.z, dc[pb][2], acc);
-        acc = mfma4(aq.w, dc[pb][3], acc);
-      }
+      for (int r = 0; r < 4; ++r) dcv[pb][r] = dc[pb][r];
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib) st[ib] = gl * st[ib];
+#pragma unroll
+    for (int op = 0; op < 2; ++op) {  // Q^T (gam dO), then -W^T dDelta
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) {
-        const float4 aw = *reinterpret_cast<const float4*>(sWT + (16 * ib + l16) * TS + 16 * pb + 4 * g);
-        acc = mfma4(-aw.x, dd[pb][0], acc);
-        acc = mfma4(-aw.y, dd[pb][1], acc);
-        acc = mfma4(-aw.z, dd[pb][2], acc);
-        acc = mfma4(-aw.w, dd[pb][3], acc);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {  // two groups of four tiles, chains interleaved
+          float4 a[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float* src = (op == 0 ? sQT : sWT) + (16 * (4 * h2 + q) + l16) * TS + 16 * pb + 4 * g;
+            const float4 x = *reinterpret_cast<const float4*>(src);
+            a[q] = op == 0 ? x : float4{-x.x, -x.y, -x.z, -x.w};
+          }
+          const v4f bv = op == 0 ? dcv[pb] : dd[pb];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].x, bv[0], st[4 * h2 + q]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].y, bv[1], st[4 * h2 + q]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].z, bv[2], st[4 * h2 + q]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].w, bv[3], st[4 * h2 + q]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      st[ib] = acc;
-      __builtin_amdgcn_sched_barrier(0);  // keep operand reads per tile
     }
   }
-  const brsrc_t r0 = make_rsrc(io.dh0 + nh * DD, D * D * 4u);
+  const brsrc_t rh0 = make_rsrc(io.dh0 + nh * DD, D * D * 4u);
 #pragma unroll
   for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) stbuf(st[ib][r], r0, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+    for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rh0, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
 }
 
 // Sum of a value over the 4 lanes of a quad (lanes 4k .. 4k+3 of a wave) as
@@ -2613,10 +2614,11 @@ void launch_scan(const ScanIO& io, int64_t N, int H_v, hipStream_t st) {
   constexpr int TILE = scan_tile<D>();
   const int64_t blocks = N * H_v * (D / TILE);
   if (blocks <= 0) return;
-  if constexpr (D == 128) {
-    const int64_t nb8 = (blocks + 7) / 8 * 8;
+  if constexpr (D == 128) {  // blocks of 64 columns of d_v
+    const int64_t mblocks = N * H_v * 2;
+    const int64_t nb8 = (mblocks + 7) / 8 * 8;
     hipLaunchKernelGGL((k_scan_mfma<C, MODE>), dim3(static_cast<unsigned>(nb8)), dim3(256), 0, st,
-                       io, blocks, nb8);
+                       io, mblocks, nb8);
   } else {
     hipLaunchKernelGGL((k_scan<D, C, TILE, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256),
                        0, st, io);
@@ -2998,8 +3000,8 @@ int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
 }
 
 const char* gdn_contract_id(void) {
-  return "gdn-cpr/v6;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
-         "B=mfma16x16x4-wy-blocked16,mfma16x16x4-scan-tile32;prep=wave-butterfly";
+  return "gdn-cpr/v7;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
+         "B=mfma16x16x4-wy-blocked16,mfma16x16x4-scan-regB;prep=wave-butterfly";
 }
 
 const char* gdn_error_string(int status) {
