@@ -91,6 +91,40 @@ def test_degenerate_inputs():
     inp = make_inputs([0, 0], 1, 2, 128, "bf16", seed=15, h0="normal")
     o, hT, _ = run_prefill(inp)
     assert bit_equal(hT, inp["h0"].cuda())
+    say("case: growing state (g = +0.4 on every token, decay factor 1.49)")
+    inp = make_inputs([100, 64], 1, 2, 128, "bf16", seed=16, h0="normal")
+    inp["g"][:] = 0.4
+    o, hT, _ = run_prefill(inp)
+    ro, rh = oracle_fwd(inp)
+    # The state grows 1.49x per token (~1e16 after 100 tokens), and a rounding
+    # error made at token t grows with it, so the bar is relative: 1e-4 of the
+    # largest value (~100 tokens x fp32 rounding of O(d)-term dot products).
+    for name, got, want in [("o", o, ro), ("hT", hT, rh)]:
+        err, top = maxabs(got, want), float(np.max(np.abs(want)))
+        say(f"  {name}: max err {err:.3e}, max |oracle| {top:.3e}, relative {err / top:.2e}")
+        assert np.isfinite(err) and err <= 1e-4 * top, name
+
+
+@pytest.mark.parametrize("gval", [0.4, -30.0])
+def test_extreme_gates_decode_equals_prefill(gval):
+    """Decode across tokens with a growing (g > 0) or near-reset (g = -30)
+    decay gives the prefill's o and state bit for bit."""
+    say(f"case: g = {gval} on every 3rd token, prefill 40 + decode 60")
+    total, pre = 100, 40
+    inp = make_inputs([total] * 2, 1, 2, 128, "bf16", seed=17, h0="normal")
+    inp["g"][::3] = gval
+    o_full, h_full, _ = run_prefill(inp, cache=True)
+    shape = shape_for(inp)
+    first = dict(inp)
+    idx = torch.cat([torch.arange(n * total, n * total + pre) for n in range(2)])
+    for key in ["q", "k", "v", "beta", "g"]:
+        first[key] = inp[key][idx].contiguous()
+    first["cu_seqlens"] = torch.tensor([0, pre, 2 * pre], dtype=torch.int32)
+    _, _, cache = run_prefill(first, cache=True)
+    od = decode_tokens(inp, cache, shape, pre, total - pre)
+    for n in range(2):
+        assert bit_equal(od[:, n], o_full[n * total + pre:(n + 1) * total]), f"o seq {n}"
+    assert bit_equal(cache.S_run, h_full)
 
 
 # ------------------------------------------------------------------ bit consistency
