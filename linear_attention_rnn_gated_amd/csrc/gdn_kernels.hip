@@ -756,7 +756,10 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vpre[bi][ct][r] = isW ? 0.0f : ldin(sV + (16 * bi + 4 * g + r) * D + cbase + 16 * ct + l16);
+      {  // read unconditionally (in bounds) and select: no per-element branch
+        const float x = ldin(sV + (16 * bi + 4 * g + r) * D + cbase + 16 * ct + l16);
+        vpre[bi][ct][r] = isW ? 0.0f : x;
+      }
   if (tid == 0) {  // running sum of g, p ascending
     float acc = 0.0f;
     for (int p = 0; p < C; ++p) {
@@ -806,7 +809,8 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int p = 16 * bi + 4 * g + r, col = cbase + 16 * ct + l16;
-        acc[ct][r] = isW ? sBG[p] * sK[p * KS + col] : sB[p] * vpre[bi][ct][r];
+        const float wv = sBG[p] * sK[p * KS + col], uv = sB[p] * vpre[bi][ct][r];
+        acc[ct][r] = isW ? wv : uv;
       }
 #pragma unroll
     for (int bj = 0; bj < bi; ++bj)
@@ -2284,8 +2288,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     }
 #pragma unroll
     for (int r = 8 * part; r < 8 * part + 8; ++r) {
-      if (r < pp) zq = fmaf(sZ[pp * CS + r], sQK[pp * CS + r], zq);
-      else if (r > pp) zq = fmaf(-sZ[r * CS + pp], sQK[r * CS + pp], zq);
+      // both candidates read (in bounds), then selected: no divergent branch
+      const bool lo = r < pp;
+      const float z1 = sZ[pp * CS + r], q1 = sQK[pp * CS + r];
+      const float z2 = sZ[r * CS + pp], q2 = sQK[r * CS + pp];
+      const float t = fmaf(lo ? z1 : -z2, lo ? q1 : q2, zq);
+      zq = r != pp ? t : zq;
     }
     qs = oct_sum(qs);
     kd = oct_sum(kd);
@@ -2382,12 +2390,14 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     }
 #pragma unroll
     for (int r = 8 * part; r < 8 * part + 8; ++r) {
-      if (r < pp) {
-        da = fmaf(sZ[pp * CS + r], sKG[pp * CS + r], da);
-        dga = fmaf(sZ[pp * CS + r], sB[pp] * sKG[pp * CS + r], dga);
-      } else if (r > pp) {
-        dga = fmaf(-sZ[r * CS + pp], sB[r] * sKG[r * CS + pp], dga);
-      }
+      // both candidates read (in bounds), then selected: no divergent branch
+      const bool lo = r < pp;
+      const float z1 = sZ[pp * CS + r], k1 = sKG[pp * CS + r];
+      const float z2 = sZ[r * CS + pp], k2 = sKG[r * CS + pp], b2 = sB[r];
+      const float ta = fmaf(z1, k1, da);
+      const float tg = lo ? fmaf(z1, sB[pp] * k1, dga) : fmaf(-z2, b2 * k2, dga);
+      da = lo ? ta : da;
+      dga = r != pp ? tg : dga;
     }
     xk = oct_sum(xk);
     uv = oct_sum(uv);
