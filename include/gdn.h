@@ -175,9 +175,18 @@ int gdn_profile_enable(int on);
 int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches);
 
 /* Identifier of the compiled arithmetic contract (chunk lengths, epsilon,
- * reduction orders, tiling).  Two builds give bit-identical results only if
- * these strings are equal. */
+ * reduction orders, tiling) ending in "src=" and the first 16 hex digits of a
+ * SHA-256 over this header, the library sources and the compile flags.  Two
+ * builds give bit-identical results only if these strings are equal (the
+ * write-up's contract section, identities: the engines that must agree carry
+ * and compare such an identity). */
 const char* gdn_contract_id(void);
+
+/* Compares another build's gdn_contract_id() with this one's: GDN_OK if equal,
+ * GDN_ERR_UNSUPPORTED if not (the two builds are not guaranteed to produce
+ * the same bits, e.g. a trainer and a rollout engine built from different
+ * sources), GDN_ERR_INVALID_ARG for NULL.  Host only. */
+int gdn_contract_check(const char* id);
 
 /* Human-readable text for a gdn_status_t. */
 const char* gdn_error_string(int status);

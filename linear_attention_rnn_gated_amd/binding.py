@@ -24,7 +24,7 @@ OP_PREFILL, OP_DECODE, OP_FWD_BWD = 0, 1, 2
 
 EXPORTS = ["gdn_workspace_bytes", "gdn_cache_init", "gdn_prefill", "gdn_decode_step",
            "gdn_fwd_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_contract_id",
-           "gdn_error_string"]
+           "gdn_contract_check", "gdn_error_string"]
 
 
 class Shape(ctypes.Structure):
@@ -72,6 +72,8 @@ def lib():
         L.gdn_profile_read.restype = ctypes.c_int
         L.gdn_contract_id.argtypes = []
         L.gdn_contract_id.restype = ctypes.c_char_p
+        L.gdn_contract_check.argtypes = [ctypes.c_char_p]
+        L.gdn_contract_check.restype = ctypes.c_int
         L.gdn_error_string.argtypes = [ctypes.c_int]
         L.gdn_error_string.restype = ctypes.c_char_p
         _lib = L
@@ -125,6 +127,11 @@ def profile_read(kernel=""):
 
 def contract_id():
     return lib().gdn_contract_id().decode()
+
+
+def contract_check(other_id):
+    """GDN_OK (0) if another build's contract id equals this build's."""
+    return lib().gdn_contract_check(other_id.encode())
 
 
 def _workspace(shape, n, T, op, device, ws=None):

@@ -6,6 +6,7 @@ FP32 instructions disabled; every kernel is in one translation unit built with
 the same flags.
 """
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -30,9 +31,23 @@ FLAGS = [
 ]
 
 
+def source_digest(extra_flags=()):
+    """SHA-256 (first 16 hex digits) over the header, every source and the
+    compile flags: part of gdn_contract_id(), so two builds that could differ in
+    arithmetic never report the same id."""
+    h = hashlib.sha256()
+    for path in [os.path.join(ROOT, "include", "gdn.h"), os.path.join(CSRC, "gdn_plan.h"),
+                 *[os.path.join(CSRC, s) for s in SOURCES]]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join([*FLAGS, *extra_flags]).encode())
+    return h.hexdigest()[:16]
+
+
 def build(verbose=False, extra_flags=()):
     """Compiles every source into libgdn.so; returns the library path."""
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    digest = f'-DGDN_SOURCE_DIGEST="{source_digest(extra_flags)}"'
+    cmd = [HIPCC, *FLAGS, *extra_flags, digest, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -26,6 +26,9 @@
 #include <string>
 #include <vector>
 
+#ifndef GDN_SOURCE_DIGEST
+#define GDN_SOURCE_DIGEST "unversioned"
+#endif
 #include "gdn.h"
 #include "gdn_plan.h"
 
@@ -3011,7 +3014,12 @@ int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
 
 const char* gdn_contract_id(void) {
   return "gdn-cpr/v7;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
-         "B=mfma16x16x4-wy-blocked16,mfma16x16x4-scan-regB;prep=wave-butterfly";
+         "B=mfma16x16x4-wy-blocked16,mfma16x16x4-scan-regB;prep=wave-butterfly;src=" GDN_SOURCE_DIGEST;
+}
+
+int gdn_contract_check(const char* id) {
+  if (!id) return GDN_ERR_INVALID_ARG;
+  return std::strcmp(id, gdn_contract_id()) == 0 ? GDN_OK : GDN_ERR_UNSUPPORTED;
 }
 
 const char* gdn_error_string(int status) {

@@ -36,6 +36,12 @@ def test_library_exports_every_declared_function():
 def test_contract_id_and_error_strings():
     cid = B.contract_id()
     assert cid.startswith("gdn-cpr/") and "eps=1e-6" in cid
+    # the id ends in a digest of the sources and flags this library was built from
+    from linear_attention_rnn_gated_amd.build import source_digest
+    assert cid.endswith(";src=" + source_digest())
+    assert B.contract_check(cid) == B.GDN_OK
+    assert B.contract_check(cid[:-1] + ("0" if cid[-1] != "0" else "1")) == B.GDN_ERR_UNSUPPORTED
+    assert B.lib().gdn_contract_check(None) == B.GDN_ERR_INVALID_ARG
     L = B.lib()
     for st in [0, -1, -2, -3, -4]:
         assert L.gdn_error_string(st).decode() not in ("", "unknown status")

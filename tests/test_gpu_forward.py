@@ -156,6 +156,75 @@ def test_decode_continues_prefill_bit_exactly(pre, use_pos_host):
     assert torch.equal(cache.pos.cpu(), c_full.pos.cpu())
 
 
+def test_mixed_position_decode_equals_prefill():
+    """Sequences sitting at different offsets inside their chunks decode together
+    (one call per step, each sequence resyncing on its own step); every output
+    and final state equals a prefill of the whole sequence, bit for bit."""
+    pre = [70, 64, 1, 130, 0, 129]
+    steps = 80
+    say(f"case: mixed-position decode, prefixes {pre} + {steps} steps")
+    inp = make_inputs([p + steps for p in pre], 2, 4, 128, "bf16", seed=31, h0="normal")
+    o_full, h_full, _ = run_prefill(inp)
+    cu = inp["cu_seqlens"].tolist()
+    n_seq = len(pre)
+    first = dict(inp)
+    idx = torch.cat([torch.arange(cu[n], cu[n] + pre[n]) for n in range(n_seq)])
+    for key in ["q", "k", "v", "beta", "g"]:
+        first[key] = inp[key][idx].contiguous()
+    first["cu_seqlens"] = torch.tensor([0] + list(np.cumsum(pre)), dtype=torch.int32)
+    _, _, cache = run_prefill(first, cache=True)
+    shape = shape_for(inp)
+    pos = cache.pos.cpu()
+    assert sorted(set(pos[:, 0].tolist())) == sorted({p % 64 for p in pre})
+    for s in range(steps):
+        rows = torch.tensor([cu[n] + pre[n] + s for n in range(n_seq)])
+        o = B.gdn_decode_step(shape, *[inp[k_][rows].cuda().contiguous()
+                                       for k_ in ["q", "k", "v", "beta", "g"]],
+                              cache, pos_host=pos)
+        pos = (pos + 1) % shape.C
+        assert bit_equal(o, o_full[rows.cuda()]), f"step {s}"
+    assert bit_equal(cache.S_run, h_full)
+
+
+def test_decode_step_in_hip_graph_replays_bit_exactly():
+    """One decode step (device-side resync decision, no host pos mirror)
+    captured in a HIP graph and replayed token after token, with eager work and
+    synchronisations between replays, equals eager decode on every replay,
+    including the replays that resync."""
+    n_seq, pre, steps = 3, 60, 10
+    say(f"case: decode step captured in a graph, {n_seq} seqs, prefill {pre}, {steps} replays")
+    inp = make_inputs([pre + steps] * n_seq, 2, 4, 128, "bf16", seed=32, h0="normal")
+    cu = inp["cu_seqlens"].tolist()
+    first = dict(inp)
+    idx = torch.cat([torch.arange(cu[n], cu[n] + pre) for n in range(n_seq)])
+    for key in ["q", "k", "v", "beta", "g"]:
+        first[key] = inp[key][idx].contiguous()
+    first["cu_seqlens"] = torch.tensor([0, pre, 2 * pre, 3 * pre], dtype=torch.int32)
+    _, _, cache_e = run_prefill(first, cache=True)
+    cache_g = cache_e.clone()
+    shape = shape_for(inp)
+    names = ["q", "k", "v", "beta", "g"]
+    static = {k_: inp[k_][idx[:n_seq]].cuda().contiguous() for k_ in names}
+    out = torch.empty(n_seq, 4, 128, dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.workspace_bytes(shape, n_seq, 0, B.OP_DECODE), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.gdn_decode_step(shape, *[static[k_] for k_ in names], cache_g, ws=ws, out=out)
+    for s in range(steps):
+        rows = torch.tensor([cu[n] + pre + s for n in range(n_seq)])
+        for k_ in names:
+            static[k_].copy_(inp[k_][rows])
+        graph.replay()
+        o_e = B.gdn_decode_step(shape, *[inp[k_][rows].cuda().contiguous() for k_ in names],
+                                cache_e)
+        torch.cuda.synchronize()
+        assert bit_equal(out, o_e), f"replay {s}"
+    assert bit_equal(cache_g.S_run, cache_e.S_run) and bit_equal(cache_g.S_chunk, cache_e.S_chunk)
+    assert torch.equal(cache_g.pos, cache_e.pos)
+
+
 def test_split_at_chunk_boundary_equals_one_prefill():
     say("case: two prefills split at a chunk edge == one prefill")
     inp = make_inputs([192, 256], 2, 4, 128, "bf16", seed=22, h0="normal")
