@@ -131,6 +131,44 @@ def bench_prefill(args, B, torch, make_inputs):
                 inputs=inp, shape=shape)
 
 
+def bench_native_mixed(args, B, torch, pf):
+    """The same prefill workload through gdn_prefill_chunked: chunk-form outputs
+    (what a chunked prefill paired with a recurrent decode computes), i.e. the
+    native-mixed baseline without the bitwise prefill/decode guarantee."""
+    c = PREFILL
+    dev = "cuda"
+    inp, shape = pf["inputs"], pf["shape"]
+    T = inp["T"]
+    ws = torch.empty(B.workspace_bytes(shape, c["N"], T, B.OP_PREFILL_CHUNKED),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty(T, c["H_v"], c["d"], dtype=torch.float32, device=dev)
+    cu = inp["cu_seqlens"].to(dev)
+
+    def step():
+        B.gdn_prefill_chunked(shape, inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], cu,
+                              h0=inp["h0"], ws=ws, out=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.profile_read("")
+    B.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.profile_enable(False)
+    per_kernel = {}
+    for name in ["k_plan", "k_prep", "k_wy", "k_scan", "k_chunk_o"]:
+        ms, n = B.profile_read(name)
+        per_kernel[name] = round(1e3 * ms / max(n, 1), 2)
+    ms_step = 1e3 * (t1 - t0) / args.steps
+    return dict(ms_per_step=round(ms_step, 4), tokens_per_s=round(T / (ms_step * 1e-3), 1),
+                cpr_over_native=round(pf["ms_per_step"] / ms_step, 3),
+                per_kernel_us=per_kernel)
+
+
 def bench_decode(args, B, torch, make_inputs):
     c = DECODE
     dev = "cuda"
@@ -316,6 +354,7 @@ def main():
         "per_kernel_us": {k: round(v["avg_us"], 2) for k, v in pf["per_kernel"].items()},
         "contract": B.contract_id(),
     }
+    line["native_mixed_prefill"] = bench_native_mixed(args, B, torch, pf)
     if not args.no_decode:
         dc = bench_decode(args, B, torch, make_inputs)
         line["decode"] = dc

@@ -75,7 +75,12 @@ typedef enum {
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
 
-typedef enum { GDN_OP_PREFILL = 0, GDN_OP_DECODE = 1, GDN_OP_FWD_BWD = 2 } gdn_op_t;
+typedef enum {
+  GDN_OP_PREFILL = 0,
+  GDN_OP_DECODE = 1,
+  GDN_OP_FWD_BWD = 2,
+  GDN_OP_PREFILL_CHUNKED = 3
+} gdn_op_t;
 
 /* Problem shape.  beta, g, states, o and gradients are always fp32. */
 typedef struct {
@@ -161,13 +166,34 @@ int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs,
                 size_t ws_bytes, void* stream);
 
 /*
+ * Native-mixed baseline (not the CPR contract): prefill whose outputs come
+ * from the chunk form instead of the token recurrence,
+ *     o_p = exp(G_p) S_c q_p + sum_{r<=p} (q_p . k_r) exp(G_p - G_r) Delta_r
+ * for each chunk with start state S_c (the same chunk-state scan as
+ * gdn_prefill, run over every chunk including a partial last one).  This is
+ * the "native mixed" prefill of the write-up's stage table (CPR section):
+ * the same function as gdn_prefill within the parity tolerance, but its bits
+ * are NOT those of gdn_prefill / gdn_decode_step.  It exists to measure what
+ * the bitwise guarantee costs.  hT (nullable) gets each sequence's final
+ * state from the chunk form.  Same argument conventions as gdn_prefill, no
+ * cache; workspace from gdn_workspace_bytes(..., GDN_OP_PREFILL_CHUNKED).
+ * Supported at d_k = d_v = 128 only (GDN_ERR_UNSUPPORTED otherwise).
+ */
+int gdn_prefill_chunked(const gdn_shape_t* shape, int32_t n_seqs,
+                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                        const void* q, const void* k, const void* v, const float* beta,
+                        const float* g, const float* h0, float* o, float* hT, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing (instrumentation).  While enabled, every launch the entry
  * points make is bracketed by HIP events recorded on the call's stream.
  * gdn_profile_read waits for the recorded events, returns the summed
  * duration (ms) and launch count of the kernels whose name contains `kernel`
  * (e.g. "k_rec"; NULL or "" = all), and forgets them.  Kernel names:
  * k_plan, k_prep, k_wy, k_scan, k_rec, k_decode, k_wy_resync, k_scan_resync,
- * k_cache_init and the k_bwd_* kernels of gdn_fwd_bwd.  Events are created
+ * k_cache_init, k_chunk_o (gdn_prefill_chunked) and the k_bwd_* kernels of
+ * gdn_fwd_bwd.  Events are created
  * by the library on first use and reused; no device memory is allocated.
  * Thread-safe; records from concurrent calls are merged.
  */

@@ -20,11 +20,11 @@ GDN_ERR_WORKSPACE = -3
 GDN_ERR_HIP = -4
 GDN_F32 = 0
 GDN_BF16 = 1
-OP_PREFILL, OP_DECODE, OP_FWD_BWD = 0, 1, 2
+OP_PREFILL, OP_DECODE, OP_FWD_BWD, OP_PREFILL_CHUNKED = 0, 1, 2, 3
 
 EXPORTS = ["gdn_workspace_bytes", "gdn_cache_init", "gdn_prefill", "gdn_decode_step",
            "gdn_fwd_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_contract_id",
-           "gdn_contract_check", "gdn_error_string"]
+           "gdn_contract_check", "gdn_error_string", "gdn_prefill_chunked"]
 
 
 class Shape(ctypes.Structure):
@@ -59,6 +59,9 @@ def lib():
         L.gdn_cache_init.argtypes = [sp, i32, vp, cp, vp]
         L.gdn_cache_init.restype = ctypes.c_int
         L.gdn_prefill.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cp, vp, sz, vp]
+        L.gdn_prefill_chunked.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                          vp]
+        L.gdn_prefill_chunked.restype = ctypes.c_int
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_decode_step.argtypes = [sp, i32, vp, vp, vp, vp, vp, cp, vp, vp, vp, sz, vp]
         L.gdn_decode_step.restype = ctypes.c_int
@@ -214,6 +217,35 @@ def gdn_prefill(shape, q, k, v, beta, g, cu_seqlens, h0=None, cache=None, want_h
                            ctypes.byref(cs) if cs is not None else None, _ptr(ws),
                            ws.numel(), _stream(dev))
     _check(st, "gdn_prefill")
+    return o, hT
+
+
+def gdn_prefill_chunked(shape, q, k, v, beta, g, cu_seqlens, h0=None, want_hT=True, ws=None,
+                        out=None):
+    """Native-mixed baseline prefill (chunk-form outputs; not bit-identical to
+    gdn_prefill / decode).  Returns (o, hT)."""
+    dev = q.device
+    T = q.shape[0]
+    n = cu_seqlens.numel() - 1
+    d, Hq, Hv = shape.d_k, shape.H_qk, shape.H_v
+    idt = q.dtype
+    _req(q, idt, (T, Hq, d), "q")
+    _req(k, idt, (T, Hq, d), "k")
+    _req(v, idt, (T, Hv, d), "v")
+    _req(beta, torch.float32, (T, Hv), "beta")
+    _req(g, torch.float32, (T, Hv), "g")
+    if h0 is not None:
+        _req(h0, torch.float32, (n, Hv, d, d), "h0")
+    cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
+    cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    o = torch.empty(T, Hv, d, dtype=torch.float32, device=dev) if out is None else out
+    hT = torch.empty(n, Hv, d, d, dtype=torch.float32, device=dev) if want_hT else None
+    ws = _workspace(shape, n, T, OP_PREFILL_CHUNKED, dev, ws)
+    st = lib().gdn_prefill_chunked(ctypes.byref(shape), n, _ptr(cu_dev),
+                                   ctypes.c_void_p(cu_host.data_ptr()), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(beta), _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws),
+                                   ws.numel(), _stream(dev))
+    _check(st, "gdn_prefill_chunked")
     return o, hT
 
 

@@ -308,6 +308,8 @@ struct ScanIO {
   float* states;         // prefill chunk-start states
   float* hT;             // nullable
   float* Dl;             // kAll: Delta of every chunk [slot][H_v][C][D]
+  float* hT_tail;        // kAll, nullable: the chunk-form final state of a
+                         // sequence whose last chunk is partial
   // cache (nullable in prefill)
   float* S_run;
   float* S_chunk;
@@ -650,7 +652,10 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
     return;
   }
   const bool tail = (L % C) != 0;
-  if (MODE == kAll && tail) return;
+  if (MODE == kAll && tail) {
+    if (io.hT_tail) store_state(io.hT_tail + nh * DD);
+    return;
+  }
   if (tail) {
     store_state(io.states + ((slot0 + nsteps) * io.H_v + h) * DD);  // tail chunk start
     if (io.S_chunk) store_state(io.S_chunk + nh * DD);
@@ -1786,6 +1791,113 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
   }
 }
 
+// Native-mixed baseline (not the CPR contract): the outputs of one chunk and
+// value head in chunk form on the matrix cores,
+//   O = diag(gam) Q S_c^T + P Delta,   P_pr = (q_p . k_r) exp(G_p - G_r), r <= p,
+// from the chunk-start state S_c (stored [d_k][d_v]) and Delta = U - W S_c^T
+// of the chunk scan.  P is built in LDS by pairs of waves; wave w then owns
+// the 16 output columns j = 16 w + l16 for all 64 rows, with S_c and Delta
+// streamed as B operands (k = i, then k = r).
+template <int C>
+__global__ __launch_bounds__(512) void k_chunk_o_m(BwdIO io) {
+  constexpr int D = 128, S1 = D + 4, S2 = C + 4;
+  static_assert(C == 64, "tiling assumes C = 64");
+  __shared__ __attribute__((aligned(16))) float sQ[C * S1];
+  __shared__ __attribute__((aligned(16))) float sK[C * S1];
+  __shared__ __attribute__((aligned(16))) float sP[C * S2];
+  __shared__ float sG[C], sGam[C];
+  int64_t slot, tok0;
+  int L;
+  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  const int64_t sh = slot * io.H_v + h;
+  const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
+  const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
+  const float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  static_assert((C * (D / 4)) % 512 == 0, "whole rounds");
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
+    const int e = tid + 512 * e_;
+    const int p = e / (D / 4), i4 = e % (D / 4);
+    const int pc = p < L ? p : L - 1;
+    const float4 k4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
+    const float4 q4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
+    *reinterpret_cast<float4*>(sK + p * S1 + 4 * i4) = sel4(p < L, k4, z4);
+    *reinterpret_cast<float4*>(sQ + p * S1 + 4 * i4) = sel4(p < L, q4, z4);
+  }
+  if (tid < C) {
+    const float gv = io.G[sh * C + tid];
+    sG[tid] = gv;
+    sGam[tid] = expf(gv);
+  }
+  __syncthreads();
+  // P tiles (row block tmb, column blocks tnb0 and tnb0 + 2), r <= p
+  const int tmb = w >> 1, tnb0 = w & 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int nb = tnb0 + 2 * t;
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (nb <= tmb) acc = mma_nt<D>(acc, sQ + (16 * tmb + l16) * S1, sK + (16 * nb + l16) * S1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * tmb + 4 * g + r, qq = 16 * nb + l16;
+      const float x = acc[r] * expf(sG[pp] - sG[qq]);
+      sP[pp * S2 + qq] = (nb <= tmb && qq <= pp && pp < L) ? x : 0.0f;
+    }
+  }
+  __syncthreads();
+  // O tiles (p = 16 pb + 4 g + r, j): Q S_c^T (k = i = g D/4 + s), scaled by
+  // gam_p, then + P Delta (k = r = g C/4 + s)
+  const int j = 16 * w + l16;
+  const float* Sc = io.states + sh * DD + j;
+  const float* Dc = io.Dl + sh * CD + j;
+  v4f acc[4];
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb) acc[pb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s4 = 0; s4 < D / 16; ++s4) {
+    float b[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b[c] = Sc[static_cast<int64_t>(g * (D / 4) + 4 * s4 + c) * D];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      const float4 a = *reinterpret_cast<const float4*>(sQ + (16 * pb + l16) * S1 + g * (D / 4) + 4 * s4);
+      acc[pb] = mfma4(a.x, b[0], acc[pb]);
+      acc[pb] = mfma4(a.y, b[1], acc[pb]);
+      acc[pb] = mfma4(a.z, b[2], acc[pb]);
+      acc[pb] = mfma4(a.w, b[3], acc[pb]);
+    }
+  }
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[pb][r] = sGam[16 * pb + 4 * g + r] * acc[pb][r];
+#pragma unroll
+  for (int s4 = 0; s4 < C / 16; ++s4) {
+    float b[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b[c] = Dc[static_cast<int64_t>(g * (C / 4) + 4 * s4 + c) * D];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      const float4 a = *reinterpret_cast<const float4*>(sP + (16 * pb + l16) * S2 + g * (C / 4) + 4 * s4);
+      acc[pb] = mfma4(a.x, b[0], acc[pb]);
+      acc[pb] = mfma4(a.y, b[1], acc[pb]);
+      acc[pb] = mfma4(a.z, b[2], acc[pb]);
+      acc[pb] = mfma4(a.w, b[3], acc[pb]);
+    }
+  }
+  const int64_t vs = static_cast<int64_t>(io.H_v) * D;
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int p = 16 * pb + 4 * g + r;
+      if (p < L) io.dqv[(tok0 + p) * vs + static_cast<int64_t>(h) * D + j] = acc[pb][r];
+    }
+}
+
 // Chunk item `it` of the persistent backward kernels: items are (chunk slot,
 // value head) pairs, head fastest.  False if the item has no tokens.
 template <int C>
@@ -2853,6 +2965,66 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// Native-mixed baseline prefill: the trainer forward's chunk kernels over every
+// chunk, then chunk-form outputs.  d = 128 only.
+template <int D, int C, typename TIn>
+int launch_prefill_chunked(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt,
+                           const gdn::Layout& L, const int32_t* cu, const void* q, const void* k,
+                           const void* v, const float* beta, const float* g, const float* h0,
+                           float* o, float* hT, char* ws, hipStream_t st) {
+  if constexpr (D != 128) {
+    return GDN_ERR_UNSUPPORTED;
+  } else {
+    int32_t* cu_chunks = reinterpret_cast<int32_t*>(ws + L.cu_chunks);
+    int32_t* cu_full = reinterpret_cast<int32_t*>(ws + L.cu_full);
+    float* qk = reinterpret_cast<float*>(ws + L.qk);
+    float* W = reinterpret_cast<float*>(ws + L.W);
+    float* U = reinterpret_cast<float*>(ws + L.U);
+    float* Gs = reinterpret_cast<float*>(ws + L.G);
+    float* states = reinterpret_cast<float*>(ws + L.states);
+    float* Dl = reinterpret_cast<float*>(ws + L.Dl);
+    {
+      Timed t_("k_plan", st);
+      hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, st, cu, N, C, cu_chunks, cu_full);
+    }
+    const int64_t nvec = cnt.T * s->H_qk;
+    if (nvec > 0) {
+      Timed t_("k_prep", st);
+      hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)), dim3(256),
+                         0, st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
+                         s->H_qk, s->scale, s->qk_l2norm);
+    }
+    if (cnt.chunks > 0) {
+      ChunkIO io{};
+      io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_chunks;
+      io.W = W; io.U = U; io.G = Gs;
+      io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_slot = L.state_slots;
+      Timed t_("k_wy", st);
+      launch_wy<D, C, TIn, kAll>(io, cnt.chunks, s->H_v, st);
+    }
+    if (N > 0) {
+      ScanIO io{};
+      io.khat = qk; io.W = W; io.U = U; io.G = Gs; io.cu = cu; io.cu_chunks = cu_chunks;
+      io.cu_full = cu_full; io.h0 = h0; io.states = states; io.hT = hT; io.hT_tail = hT;
+      io.Dl = Dl;
+      io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
+      io.max_state_slot = L.state_slots; io.max_full_slot = L.state_slots;
+      Timed t_("k_scan", st);
+      launch_scan<D, C, kAll>(io, N, s->H_v, st);
+    }
+    if (cnt.chunks > 0) {
+      BwdIO b{};
+      b.qk = qk; b.cu = cu; b.cu_chunks = cu_chunks; b.G = Gs; b.states = states; b.Dl = Dl;
+      b.dqv = o;
+      b.N = N; b.H_qk = s->H_qk; b.H_v = s->H_v; b.T = cnt.T; b.max_state_slot = L.state_slots;
+      Timed t_("k_chunk_o", st);
+      hipLaunchKernelGGL((k_chunk_o_m<C>), dim3(static_cast<unsigned>(cnt.chunks), s->H_v),
+                         dim3(512), 0, st, b);
+    }
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
+}
+
 // Calls f.template operator()<D, C, TIn>() for the shape's compiled variant.
 template <typename F>
 int dispatch(const gdn_shape_t* s, F&& f) {
@@ -2974,6 +3146,29 @@ int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seql
   return dispatch(shape, [&]<int D, int C, typename TIn>() {
     return launch_fwd_bwd<D, C, TIn>(shape, n_seqs, cnt, L, cu_seqlens_dev, q, k, v, beta, g, h0,
                                      dO, dhT, o, hT, dq, dk, dv, dbeta, dg, dh0, w, st);
+  });
+}
+
+int gdn_prefill_chunked(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                        const int32_t* cu_seqlens_host, const void* q, const void* k,
+                        const void* v, const float* beta, const float* g, const float* h0,
+                        float* o, float* hT, void* ws, size_t ws_bytes, void* stream) {
+  int rc = gdn::check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (shape->d_k != 128) return GDN_ERR_UNSUPPORTED;
+  if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host) return GDN_ERR_INVALID_ARG;
+  gdn::Counts cnt;
+  if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
+  if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, h0, o, hT})) return GDN_ERR_INVALID_ARG;
+  const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_PREFILL_CHUNKED);
+  if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (n_seqs == 0) return GDN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  return dispatch(shape, [&]<int D, int C, typename TIn>() {
+    return launch_prefill_chunked<D, C, TIn>(shape, n_seqs, cnt, L, cu_seqlens_dev, q, k, v, beta,
+                                             g, h0, o, hT, w, st);
   });
 }
 

@@ -60,7 +60,8 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
     L.total = cur;
     return L;
   }
-  if (op != GDN_OP_PREFILL && op != GDN_OP_FWD_BWD) return Layout{};
+  if (op != GDN_OP_PREFILL && op != GDN_OP_FWD_BWD && op != GDN_OP_PREFILL_CHUNKED) return Layout{};
+  const bool all_chunks = op != GDN_OP_PREFILL;  // W, U, G, Delta for every chunk
   L.full_slots = T / static_cast<int64_t>(C);
   L.state_slots = T / static_cast<int64_t>(C) + N;
   L.cu_chunks = take(&cur, (N + 1) * sizeof(int32_t));
@@ -68,11 +69,12 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
   // two spare token rows: the token step reads (prefetches) up to two tokens
   // past the end of a chunk; those values are never used
   L.qk = take(&cur, (T * Hq + 2) * 2 * d * f);
-  const int64_t wu_slots = op == GDN_OP_FWD_BWD ? L.state_slots : L.full_slots;
+  const int64_t wu_slots = all_chunks ? L.state_slots : L.full_slots;
   L.W = take(&cur, wu_slots * Hv * C * d * f);
   L.U = take(&cur, wu_slots * Hv * C * d * f);
   L.G = take(&cur, wu_slots * Hv * C * f);
   L.states = take(&cur, L.state_slots * Hv * d * d * f);
+  if (op == GDN_OP_PREFILL_CHUNKED) L.Dl = take(&cur, L.state_slots * Hv * C * d * f);
   if (op == GDN_OP_FWD_BWD) {
     const size_t cd = L.state_slots * Hv * C * d * f;
     L.Dl = take(&cur, cd);

@@ -159,3 +159,17 @@ def test_misaligned_pointers_rejected():
     cache = B.CacheStruct(16, 16, 16, 20, 16, 16, 16)
     assert L.gdn_cache_init(ctypes.byref(s), 2, None, ctypes.byref(cache), None) == \
         B.GDN_ERR_INVALID_ARG
+
+
+def test_chunked_baseline_claims():
+    """The native-mixed baseline prefill runs at d = 128 only."""
+    L = B.lib()
+    cu = (ctypes.c_int32 * 2)(0, 10)
+    a = ctypes.c_void_p(16)
+    s16 = good_shape(d_k=16, d_v=16, C=16)
+    assert L.gdn_prefill_chunked(ctypes.byref(s16), 1, a, cu, a, a, a, a, a, None, a, None, a,
+                                 1 << 40, None) == B.GDN_ERR_UNSUPPORTED
+    s = good_shape()
+    assert L.gdn_workspace_bytes(ctypes.byref(s), 4, 1000, B.OP_PREFILL_CHUNKED) > 0
+    assert L.gdn_prefill_chunked(ctypes.byref(s), 1, a, cu, a, a, a, a, a, None, a, None, None,
+                                 1 << 40, None) == B.GDN_ERR_WORKSPACE

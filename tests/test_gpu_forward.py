@@ -369,3 +369,23 @@ def test_varlen_32_seqs_packed_alone_reshuffled():
     e = maxabs(o.cpu()[rows][:, hv], ro[rows])
     say(f"  shortest seq {short} (len {inp['lens'][short]}): max|o-oracle|={e:.3e}")
     assert e <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ native-mixed baseline
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunked_baseline_prefill_parity(dtype):
+    """gdn_prefill_chunked (chunk-form outputs, the native-mixed baseline)
+    computes the same function: parity with the oracle on ragged lengths,
+    including partial last chunks and an empty sequence."""
+    lens = [200, 64, 1, 130, 0, 129]
+    say(f"case: chunk-form baseline prefill {dtype} lens={lens}")
+    inp = make_inputs(lens, 2, 4, 128, dtype, seed=41, h0="normal")
+    shape = shape_for(inp)
+    d = to_dev(inp)
+    o, hT = B.gdn_prefill_chunked(shape, d["q"], d["k"], d["v"], d["beta"], d["g"],
+                                  d["cu_seqlens"], h0=d["h0"])
+    check_parity(inp, o, hT, TOL[dtype])
+    # the CPR prefill agrees within the same bar (not bit for bit)
+    o_c, h_c, _ = run_prefill(inp)
+    assert maxabs(o, o_c) <= 2 * TOL[dtype] and maxabs(hT, h_c) <= 2 * TOL[dtype]
