@@ -30,7 +30,7 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3
 # taken on (sha256 prefix of gdn_kernels.hip); for any other source the
 # traffic field is reported as null.
 MEASURED_TRAFFIC = {
-    "76c6c3866553df82": {"k_rec": 613.3e6 + 134.2e6, "k_decode": 135.9e6 + 136.4e6},
+    "51fabe62a7abc541": {"k_rec": 617.6e6 + 142.6e6, "k_decode": 135.9e6 + 136.4e6},
 }
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_rnn_gated_amd", "csrc", "gdn_kernels.hip")
 
