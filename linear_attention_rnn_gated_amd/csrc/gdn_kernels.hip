@@ -1670,8 +1670,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdIO io) {
 //           ldb; rows of B at or past `brows` read row brows - 1 (in bounds)
 //   mma_tn: a -> At[0][m0 + l16] (A given transposed, row stride lda); b as nn
 template <int K>
-__device__ __forceinline__ v4f mma_nt(v4f acc, const float* a, const float* b) {
-  const int g = (threadIdx.x & 63) >> 4;
+__device__ __forceinline__ v4f mma_nt(v4f acc, const float* a, const float* b, int g) {
   a += g * (K / 4);
   b += g * (K / 4);
 #pragma unroll
@@ -1685,9 +1684,24 @@ __device__ __forceinline__ v4f mma_nt(v4f acc, const float* a, const float* b) {
   }
   return acc;
 }
+// mma_nt with the B operand already in registers: b[s4] holds what mma_nt
+// would read at b + g K/4 + 4 s4
 template <int K>
-__device__ __forceinline__ v4f mma_nn(v4f acc, const float* a, const float* b, int ldb, int brows) {
-  const int g = (threadIdx.x & 63) >> 4;
+__device__ __forceinline__ v4f mma_nt_rb(v4f acc, const float* a, const float4* b, int g) {
+  a += g * (K / 4);
+#pragma unroll
+  for (int s4 = 0; s4 < K / 16; ++s4) {
+    const float4 x = *reinterpret_cast<const float4*>(a + 4 * s4);
+    acc = mfma4(x.x, b[s4].x, acc);
+    acc = mfma4(x.y, b[s4].y, acc);
+    acc = mfma4(x.z, b[s4].z, acc);
+    acc = mfma4(x.w, b[s4].w, acc);
+  }
+  return acc;
+}
+template <int K>
+__device__ __forceinline__ v4f mma_nn(v4f acc, const float* a, const float* b, int ldb, int brows,
+                                      int g) {
   a += g * (K / 4);
 #pragma unroll
   for (int s4 = 0; s4 < K / 16; ++s4) {
@@ -1708,8 +1722,7 @@ __device__ __forceinline__ v4f mma_nn(v4f acc, const float* a, const float* b, i
 }
 template <int K>
 __device__ __forceinline__ v4f mma_tn(v4f acc, const float* a, int lda, const float* b, int ldb,
-                                      int brows) {
-  const int g = (threadIdx.x & 63) >> 4;
+                                      int brows, int g) {
 #pragma unroll
   for (int s = 0; s < K / 4; ++s) {
     const int k = g * (K / 4) + s;
@@ -1757,7 +1770,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (nb <= w) acc = mma_nt<D>(acc, sQ + (16 * w + l16) * S1, sK + (16 * nb + l16) * S1);
+    if (nb <= w) acc = mma_nt<D>(acc, sQ + (16 * w + l16) * S1, sK + (16 * nb + l16) * S1, g);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * w + 4 * g + r, qq = 16 * nb + l16;
@@ -1785,7 +1798,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = mma_nn<C>(acc, PT + (16 * w + l16) * S2, sO + 16 * nb + l16, S1, C);
+    acc = mma_nn<C>(acc, PT + (16 * w + l16) * S2, sO + 16 * nb + l16, S1, C, g);
 #pragma unroll
     for (int r = 0; r < 4; ++r) E[(16 * w + 4 * g + r) * D + 16 * nb + l16] = acc[r];
   }
@@ -1839,7 +1852,7 @@ __global__ __launch_bounds__(512) void k_chunk_o_m(BwdIO io) {
   for (int t = 0; t < 2; ++t) {
     const int nb = tnb0 + 2 * t;
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (nb <= tmb) acc = mma_nt<D>(acc, sQ + (16 * tmb + l16) * S1, sK + (16 * nb + l16) * S1);
+    if (nb <= tmb) acc = mma_nt<D>(acc, sQ + (16 * tmb + l16) * S1, sK + (16 * nb + l16) * S1, g);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * tmb + 4 * g + r, qq = 16 * nb + l16;
@@ -2303,15 +2316,17 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   auto crow = [&](int p) { return p < L ? p : L - 1; };
   // C x C tiles of wave w: row block mb = w / 2, column blocks nb = w % 2 and w % 2 + 2
   const int tmb = w >> 1, tnb0 = w & 1;
-
+  const int col = 16 * w + l16;
   if (tid < C) {
     sG[tid] = io.G[sh * C + tid];
     const float bx = io.beta[(tok0 + crow(tid)) * io.H_v + h];
     sB[tid] = tid < L ? bx : 0.0f;
   }
   static_assert((C * (D / 4)) % 512 == 0, "whole rounds");
+  constexpr int NR = (C * (D / 4)) / 512;  // float4 of a C x D tile per thread
+  float4 pq[NR];
 #pragma unroll
-  for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
+  for (int e_ = 0; e_ < NR; ++e_) {
     const int e = tid + 512 * e_;
     const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
     const float4 k4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
@@ -2322,6 +2337,23 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     *reinterpret_cast<float4*>(sD + p * KS + 4 * i4) = sel4(p < L, d4, z4);
   }
   __syncthreads();
+  // Operands of later phases are fetched ahead of their use, after the loads
+  // that the current phase waits for (memory counters retire in order): Q
+  // and, in accumulator layout (rows 16 mb + 4 g + r, column col), SdO and DsD.
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
+    const int e = tid + 512 * e_;
+    const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
+    pq[e_] = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
+  }
+  float pS[4][4], pD[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pS[mb][r] = SdO[(16 * mb + 4 * g + r) * D + col];
+      pD[mb][r] = DsD[(16 * mb + 4 * g + r) * D + col];
+    }
   const float glast = sG[C - 1];
   if (tid < C) {
     sGam[tid] = expf(sG[tid]);
@@ -2333,7 +2365,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   for (int t = 0; t < 2; ++t) {
     const int nb = tnb0 + 2 * t;
     v4f dp = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (nb <= tmb) dp = mma_nt<D>(dp, sO + (16 * tmb + l16) * KS, sD + (16 * nb + l16) * KS);
+    if (nb <= tmb) dp = mma_nt<D>(dp, sO + (16 * tmb + l16) * KS, sD + (16 * nb + l16) * KS, g);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * tmb + 4 * g + r, qq = 16 * nb + l16;
@@ -2342,13 +2374,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     }
   }
   __syncthreads();  // dO and Delta are dead
-  static_assert((C * (D / 4)) % 512 == 0, "whole rounds");
 #pragma unroll
   for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
     const int e = tid + 512 * e_;
-    const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
-    const float4 q4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
-    *reinterpret_cast<float4*>(sQ + p * KS + 4 * i4) = sel4(p < L, q4, z4);
+    const int p = e / (D / 4), i4 = e % (D / 4);
+    *reinterpret_cast<float4*>(sQ + p * KS + 4 * i4) = sel4(p < L, pq[e_], z4);
   }
   __syncthreads();
   // ---- QK (r <= p) and KK Gam (r < p)
@@ -2357,8 +2387,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     const int nb = tnb0 + 2 * t;
     v4f qk = {0.0f, 0.0f, 0.0f, 0.0f}, kk = qk;
     if (nb <= tmb) {
-      qk = mma_nt<D>(qk, sQ + (16 * tmb + l16) * KS, sK + (16 * nb + l16) * KS);
-      kk = mma_nt<D>(kk, sK + (16 * tmb + l16) * KS, sK + (16 * nb + l16) * KS);
+      qk = mma_nt<D>(qk, sQ + (16 * tmb + l16) * KS, sK + (16 * nb + l16) * KS, g);
+      kk = mma_nt<D>(kk, sK + (16 * tmb + l16) * KS, sK + (16 * nb + l16) * KS, g);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -2370,9 +2400,31 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     }
   }
   __syncthreads();
+  // fetched ahead: SdO and DsD as row segments (row tid / 8, 16 elements) for
+  // the dG terms, and the right-hand side of the back substitution (wave w:
+  // columns 32 w .. 32 w + 31 of [SdD | dDelta]); all inside the chunk's slabs
+  float4 rS[4], rD[4];
+  {
+    const int pp = tid >> 3, part = tid & 7;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      rS[m] = *reinterpret_cast<const float4*>(SdO + pp * D + 16 * part + 4 * m);
+      rD[m] = *reinterpret_cast<const float4*>(DsD + pp * D + 16 * part + 4 * m);
+    }
+  }
+  float rh[4][2][4];
+  {
+    const int col0 = 32 * w;
+    const float* rhs = w < 4 ? io.SdD + sh * CD + col0 : io.dD + sh * CD + (col0 - D);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rh[bi][ct][r] = rhs[(16 * bi + 4 * g + r) * D + 16 * ct + l16];
+  }
   // ---- dq-hat = gam SdO + Z K  and  dk-hat (partial) = lam DsD + Z^T Q; wave w
   // owns columns i = 16 w + l16, all four row blocks
-  const int col = 16 * w + l16;
   v4f dk[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -2380,11 +2432,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * mb + 4 * g + r;
-      aq[r] = sGam[pp] * SdO[pp * D + col];
-      ak[r] = sLam[pp] * DsD[pp * D + col];
+      aq[r] = sGam[pp] * pS[mb][r];
+      ak[r] = sLam[pp] * pD[mb][r];
     }
-    aq = mma_nn<C>(aq, sZ + (16 * mb + l16) * CS, sK + col, KS, C);
-    ak = mma_tn<C>(ak, sZ + 16 * mb + l16, CS, sQ + col, KS, C);
+    aq = mma_nn<C>(aq, sZ + (16 * mb + l16) * CS, sK + col, KS, C, g);
+    ak = mma_tn<C>(ak, sZ + 16 * mb + l16, CS, sQ + col, KS, C, g);
     dk[mb] = ak;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -2397,9 +2449,16 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     const int pp = tid >> 3, part = tid & 7;
     float qs = 0.0f, kd = 0.0f, zq = 0.0f;
 #pragma unroll
-    for (int i = 16 * part; i < 16 * part + 16; ++i) {
-      qs = fmaf(sQ[pp * KS + i], SdO[pp * D + i], qs);
-      kd = fmaf(sK[pp * KS + i], DsD[pp * D + i], kd);
+    for (int m = 0; m < 4; ++m) {
+      const int i = 16 * part + 4 * m;
+      qs = fmaf(sQ[pp * KS + i], rS[m].x, qs);
+      kd = fmaf(sK[pp * KS + i], rD[m].x, kd);
+      qs = fmaf(sQ[pp * KS + i + 1], rS[m].y, qs);
+      kd = fmaf(sK[pp * KS + i + 1], rD[m].y, kd);
+      qs = fmaf(sQ[pp * KS + i + 2], rS[m].z, qs);
+      kd = fmaf(sK[pp * KS + i + 2], rD[m].z, kd);
+      qs = fmaf(sQ[pp * KS + i + 3], rS[m].w, qs);
+      kd = fmaf(sK[pp * KS + i + 3], rD[m].w, kd);
     }
 #pragma unroll
     for (int r = 8 * part; r < 8 * part + 8; ++r) {
@@ -2426,9 +2485,30 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   }
   // ---- back substitution (I + A)^T Y = [-SdD | dDelta], A_pr = beta_p KG_pr,
   // blocked by 16 rows from the bottom; wave w owns columns 32 w .. 32 w + 31
+  // W and U rows of this wave's first dA tile, fetched while the back
+  // substitution runs (the wave with no first tile fetches a valid row block)
+  float4 pw[D / 16], pu[D / 16];
+  {
+    const int nb = tnb0 <= tmb ? tnb0 : 0;
+    const float* wr = Wc + (16 * nb + l16) * D + g * (D / 4);
+    const float* ur = Uc + (16 * nb + l16) * D + g * (D / 4);
+#pragma unroll
+    for (int s4 = 0; s4 < D / 16; ++s4) {
+      pw[s4] = *reinterpret_cast<const float4*>(wr + 4 * s4);
+      pu[s4] = *reinterpret_cast<const float4*>(ur + 4 * s4);
+    }
+  }
+  // and this thread's v segment for dbeta (row tid / 8, 16 elements)
+  float pv[16];
+  {
+    const int pp = tid >> 3, part = tid & 7;
+    const TIn* vin = static_cast<const TIn*>(io.v) + (tok0 + crow(pp)) * vs +
+                     static_cast<int64_t>(h) * D + 16 * part;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pv[i] = ldin(vin + i);
+  }
   {
     const int col0 = 32 * w;
-    const float* rhs = w < 4 ? io.SdD + sh * CD + col0 : io.dD + sh * CD + (col0 - D);
     const float sgn = w < 4 ? -1.0f : 1.0f;
     v4f Y[4][2];
 #pragma unroll
@@ -2439,7 +2519,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int pp = 16 * bi + 4 * g + r;
-          const float x = sgn * rhs[pp * D + 16 * ct + l16];
+          const float x = sgn * rh[bi][ct][r];
           acc[ct][r] = pp < L ? x : 0.0f;
         }
 #pragma unroll
@@ -2483,8 +2563,21 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     const int nb = tnb0 + 2 * t;
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (nb <= tmb) {
-      acc = mma_nt<D>(acc, sY + (16 * tmb + l16) * YS, Wc + (16 * nb + l16) * D);
-      acc = mma_nt<D>(acc, sY + (16 * tmb + l16) * YS + D, Uc + (16 * nb + l16) * D);
+      // each half's registers are refilled with the next tile's rows as soon
+      // as its products are issued
+      const bool next = t == 0 && nb + 2 <= tmb;
+      acc = mma_nt_rb<D>(acc, sY + (16 * tmb + l16) * YS, pw, g);
+      if (next) {
+#pragma unroll
+        for (int s4 = 0; s4 < D / 16; ++s4)
+          pw[s4] = *reinterpret_cast<const float4*>(Wc + (16 * (nb + 2) + l16) * D + g * (D / 4) + 4 * s4);
+      }
+      acc = mma_nt_rb<D>(acc, sY + (16 * tmb + l16) * YS + D, pu, g);
+      if (next) {
+#pragma unroll
+        for (int s4 = 0; s4 < D / 16; ++s4)
+          pu[s4] = *reinterpret_cast<const float4*>(Uc + (16 * (nb + 2) + l16) * D + g * (D / 4) + 4 * s4);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -2495,13 +2588,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   __syncthreads();
   // ---- dbeta and the remaining dG terms (8 lanes per row); F = E2 + E2^T
   {
-    const int pp = tid >> 3, part = tid & 7, pc = crow(pp);
-    const TIn* vin = static_cast<const TIn*>(io.v) + (tok0 + pc) * vs + static_cast<int64_t>(h) * D;
+    const int pp = tid >> 3, part = tid & 7;
     float xk = 0.0f, uv = 0.0f, da = 0.0f, dga = 0.0f;
 #pragma unroll
     for (int i = 16 * part; i < 16 * part + 16; ++i) {
       xk = fmaf(sY[pp * YS + i], sK[pp * KS + i], xk);
-      uv = fmaf(sY[pp * YS + D + i], ldin(vin + i), uv);
+      uv = fmaf(sY[pp * YS + D + i], pv[i - 16 * part], uv);
     }
 #pragma unroll
     for (int r = 8 * part; r < 8 * part + 8; ++r) {
@@ -2544,7 +2636,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
       const int pp = 16 * mb + 4 * g + r;
       ak[r] = fmaf(sB[pp] * sGam[pp], sY[pp * YS + col], ak[r]);
     }
-    ak = mma_nn<C>(ak, sQK + (16 * mb + l16) * CS, sK + col, KS, C);
+    ak = mma_nn<C>(ak, sQK + (16 * mb + l16) * CS, sK + col, KS, C, g);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * mb + 4 * g + r;
