@@ -95,14 +95,12 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ arr, int N, 
 // L2 normalisation of one d-vector (d <= 128) by one full wave of 64 lanes.
 // Lane l holds elements l and l + 64.  The sum of squares is combined by a
 // butterfly, after which every lane holds the same value.  Every kernel that
-// needs a normalised q or k goes through this function, so all of them see
-// the same bits.
-template <int D, typename TIn>
-__device__ __forceinline__ void l2norm_wave(const TIn* __restrict__ x, float mul, int do_norm,
-                                            float& y0, float& y1) {
-  const int l = threadIdx.x & 63;
-  float x0 = (l < D) ? ldin(x + l) : 0.0f;
-  float x1 = (D > 64) ? ldin(x + l + 64) : 0.0f;
+// needs a normalised q or k goes through l2norm_vals (directly or through
+// l2norm_wave), so all of them see the same bits.
+// The arithmetic on already loaded elements x0 = x[l], x1 = x[l + 64]:
+template <int D>
+__device__ __forceinline__ void l2norm_vals(float x0, float x1, float mul, int do_norm, float& y0,
+                                            float& y1) {
   if (do_norm) {
     float ss = fmaf(x1, x1, x0 * x0);
 #pragma unroll
@@ -113,6 +111,14 @@ __device__ __forceinline__ void l2norm_wave(const TIn* __restrict__ x, float mul
   }
   y0 = x0 * mul;
   y1 = x1 * mul;
+}
+template <int D, typename TIn>
+__device__ __forceinline__ void l2norm_wave(const TIn* __restrict__ x, float mul, int do_norm,
+                                            float& y0, float& y1) {
+  const int l = threadIdx.x & 63;
+  const float x0 = (l < D) ? ldin(x + l) : 0.0f;
+  const float x1 = (D > 64) ? ldin(x + l + 64) : 0.0f;
+  l2norm_vals<D>(x0, x1, mul, do_norm, y0, y1);
 }
 
 // ---------------------------------------------------------------------------
@@ -135,27 +141,48 @@ __global__ void k_plan(const int32_t* __restrict__ cu, int N, int C, int32_t* __
 }
 
 // ---------------------------------------------------------------------------
-// Prep: normalised k and q (times scale) in fp32, one wave per (token, q/k
-// head), written head-major and interleaved: qk[hq][t][0][:] = k-hat,
-// qk[hq][t][1][:] = q-hat.  A chunk's key/query stream for one head is then a
-// single contiguous run, read by k_rec as wave-uniform scalar loads.
+// Prep: normalised k and q (times scale) in fp32, written head-major and
+// interleaved: qk[hq][t][0][:] = k-hat, qk[hq][t][1][:] = q-hat.  A chunk's
+// key/query stream for one head is then a single contiguous run, read by
+// k_rec as wave-uniform scalar loads.  Each wave normalises kPrepVecs
+// consecutive (token, q/k head) vectors, one at a time with the lanes and
+// arithmetic of l2norm_wave, after loading all of them.
+constexpr int kPrepVecs = 4;
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void k_prep(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                               float* __restrict__ qk, int64_t T, int H_qk,
                                               float scale, int l2) {
-  const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // t * H_qk + hq
-  if (vec >= T * H_qk) return;
-  const int64_t t = vec / H_qk;
-  const int hq = static_cast<int>(vec - t * H_qk);
-  float* out = qk + (static_cast<int64_t>(hq) * T + t) * 2 * D;
+  const int64_t nvec = T * H_qk;
+  const int64_t vec0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepVecs;
+  if (vec0 >= nvec) return;
   const int l = threadIdx.x & 63;
-  float y0, y1;
-  l2norm_wave<D>(k + vec * D, 1.0f, l2, y0, y1);
-  if (l < D) out[l] = y0;
-  if (D > 64) out[l + 64] = y1;
-  l2norm_wave<D>(q + vec * D, scale, l2, y0, y1);
-  if (l < D) out[D + l] = y0;
-  if (D > 64) out[D + l + 64] = y1;
+  float k0[kPrepVecs], k1[kPrepVecs], q0[kPrepVecs], q1[kPrepVecs];
+#pragma unroll
+  for (int v = 0; v < kPrepVecs; ++v) {
+    const int64_t vec = vec0 + v < nvec ? vec0 + v : nvec - 1;  // t * H_qk + hq
+    k0[v] = (l < D) ? ldin(k + vec * D + l) : 0.0f;
+    k1[v] = (D > 64) ? ldin(k + vec * D + l + 64) : 0.0f;
+    q0[v] = (l < D) ? ldin(q + vec * D + l) : 0.0f;
+    q1[v] = (D > 64) ? ldin(q + vec * D + l + 64) : 0.0f;
+  }
+#pragma unroll
+  for (int v = 0; v < kPrepVecs; ++v) {
+    const int64_t vec = vec0 + v;
+    if (vec >= nvec) break;  // uniform over the wave
+    const int64_t t = vec / H_qk;
+    const int hq = static_cast<int>(vec - t * H_qk);
+    float* out = qk + (static_cast<int64_t>(hq) * T + t) * 2 * D;
+    float y0, y1;
+    l2norm_vals<D>(k0[v], k1[v], 1.0f, l2, y0, y1);
+    if (l < D) out[l] = y0;
+    if (D > 64) out[l + 64] = y1;
+    l2norm_vals<D>(q0[v], q1[v], scale, l2, y0, y1);
+    if (l < D) out[D + l] = y0;
+    if (D > 64) out[D + l + 64] = y1;
+  }
+}
+__host__ __device__ constexpr int64_t prep_blocks(int64_t nvec) {
+  return (nvec + 4 * kPrepVecs - 1) / (4 * kPrepVecs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1146,7 +1173,7 @@ struct DecIO {
 template <int D, int C, typename TIn>
 __global__ __launch_bounds__(256) void k_decode(DecIO io) {
   using RS = RowSplit<D>;
-  constexpr int DK = RS::DK, KS = RS::KS, NH = RS::NH;
+  constexpr int DK = RS::DK, KS = RS::KS;
   static_assert(RS::WPH <= 4, "one block of at most 4 waves per head");
   __shared__ float sq[D < 64 ? 64 : D];
   __shared__ float sk[D < 64 ? 64 : D];
@@ -2091,7 +2118,6 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
   const int64_t slot0 = io.cu_chunks[n];
   if (slot0 + nchunks > io.max_state_slot) return;
   const int j = 16 * w + l16;  // this lane's column of d_v
-  const float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
   // Buffer offsets (bytes): a lane part in a VGPR, a wave-uniform part in an
   // SGPR.  Rows past a partial chunk's end are outside the range of the
@@ -2862,7 +2888,7 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   const int64_t nvec = cnt.T * s->H_qk;
   if (nvec > 0) {
     Timed t_("k_prep", st);
-    hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)), dim3(256), 0,
+    hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256), 0,
                        st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
                        s->H_qk, s->scale, s->qk_l2norm);
   }
@@ -2961,7 +2987,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   const int64_t nvec = cnt.T * s->H_qk;
   if (nvec > 0) {
     Timed t_("k_prep", st);
-    hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)), dim3(256), 0,
+    hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256), 0,
                        st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
                        s->H_qk, s->scale, s->qk_l2norm);
   }
@@ -3082,7 +3108,7 @@ int launch_prefill_chunked(const gdn_shape_t* s, int32_t N, const gdn::Counts& c
     const int64_t nvec = cnt.T * s->H_qk;
     if (nvec > 0) {
       Timed t_("k_prep", st);
-      hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)), dim3(256),
+      hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256),
                          0, st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
                          s->H_qk, s->scale, s->qk_l2norm);
     }
