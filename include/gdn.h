@@ -79,7 +79,8 @@ typedef enum {
   GDN_OP_PREFILL = 0,
   GDN_OP_DECODE = 1,
   GDN_OP_FWD_BWD = 2,
-  GDN_OP_PREFILL_CHUNKED = 3
+  GDN_OP_PREFILL_CHUNKED = 3,
+  GDN_OP_PREFILL_CONTINUE = 4
 } gdn_op_t;
 
 /* Problem shape.  beta, g, states, o and gradients are always fp32. */
@@ -149,6 +150,32 @@ int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q,
                     float* o, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Chunked-prefill continuation: n_seqs sequences whose decode cache stands
+ * anywhere inside a chunk (cache->pos = p, the same for every head of a
+ * sequence) take their next tokens q, k, v, beta, g (packed by cu_seqlens, as
+ * in gdn_prefill) in one call.  The result is bit-identical to having run
+ * the whole history and these tokens through one gdn_prefill, or token by
+ * token through gdn_decode_step (chunk grid anchored at each sequence's
+ * first token, as everywhere): the current chunk is prefilled again from
+ * its start state cache->S_chunk, its p buffered tokens (cache->kbuf, vbuf,
+ * bbuf, gbuf) followed by the new ones, and the outputs of the new tokens
+ * only are written to o [T, H_v, d_v].  hT (nullable) receives each
+ * sequence's final state; the cache is left where the sequence now stands.
+ * pos_host [n_seqs] (host memory) must hold each sequence's cache->pos; it
+ * sizes the launches (a value that disagrees with the device gives wrong
+ * results for that sequence, never an access outside the buffers).
+ * GDN_ERR_INVALID_ARG if some pos_host value is outside [0, C).  Workspace
+ * from gdn_workspace_bytes(..., T, GDN_OP_PREFILL_CONTINUE); it covers the
+ * up to n_seqs * (C - 1) buffered tokens.
+ */
+int gdn_prefill_continue(const gdn_shape_t* shape, int32_t n_seqs,
+                         const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                         const int32_t* pos_host, const void* q, const void* k,
+                         const void* v, const float* beta, const float* g,
+                         gdn_cache_t* cache, float* o, float* hT, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
  * Trainer forward + backward (case "trainer_fwd" and its gradient).  The
  * forward runs exactly the prefill launches, so o and hT are bit-identical to
  * gdn_prefill's.  dO [T, H_v, d_v] fp32; dhT [N, H_v, d_k, d_v] nullable
@@ -192,7 +219,8 @@ int gdn_prefill_chunked(const gdn_shape_t* shape, int32_t n_seqs,
  * duration (ms) and launch count of the kernels whose name contains `kernel`
  * (e.g. "k_rec"; NULL or "" = all), and forgets them.  Kernel names:
  * k_plan, k_prep, k_wy, k_scan, k_rec, k_decode, k_wy_resync, k_scan_resync,
- * k_cache_init, k_chunk_o (gdn_prefill_chunked) and the k_bwd_* kernels of
+ * k_cache_init, k_chunk_o (gdn_prefill_chunked), k_cont_plan, k_cont_gather,
+ * k_cont_scatter (gdn_prefill_continue) and the k_bwd_* kernels of
  * gdn_fwd_bwd.  Events are created
  * by the library on first use and reused; no device memory is allocated.
  * Thread-safe; records from concurrent calls are merged.

@@ -20,11 +20,12 @@ GDN_ERR_WORKSPACE = -3
 GDN_ERR_HIP = -4
 GDN_F32 = 0
 GDN_BF16 = 1
-OP_PREFILL, OP_DECODE, OP_FWD_BWD, OP_PREFILL_CHUNKED = 0, 1, 2, 3
+OP_PREFILL, OP_DECODE, OP_FWD_BWD, OP_PREFILL_CHUNKED, OP_PREFILL_CONTINUE = 0, 1, 2, 3, 4
 
 EXPORTS = ["gdn_workspace_bytes", "gdn_cache_init", "gdn_prefill", "gdn_decode_step",
            "gdn_fwd_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_contract_id",
-           "gdn_contract_check", "gdn_error_string", "gdn_prefill_chunked"]
+           "gdn_contract_check", "gdn_error_string", "gdn_prefill_chunked",
+           "gdn_prefill_continue"]
 
 
 class Shape(ctypes.Structure):
@@ -62,6 +63,9 @@ def lib():
         L.gdn_prefill_chunked.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                           vp]
         L.gdn_prefill_chunked.restype = ctypes.c_int
+        L.gdn_prefill_continue.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, cp, vp, vp,
+                                           vp, sz, vp]
+        L.gdn_prefill_continue.restype = ctypes.c_int
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_decode_step.argtypes = [sp, i32, vp, vp, vp, vp, vp, cp, vp, vp, vp, sz, vp]
         L.gdn_decode_step.restype = ctypes.c_int
@@ -217,6 +221,39 @@ def gdn_prefill(shape, q, k, v, beta, g, cu_seqlens, h0=None, cache=None, want_h
                            ctypes.byref(cs) if cs is not None else None, _ptr(ws),
                            ws.numel(), _stream(dev))
     _check(st, "gdn_prefill")
+    return o, hT
+
+
+def gdn_prefill_continue(shape, q, k, v, beta, g, cu_seqlens, cache, pos_host, want_hT=True,
+                         ws=None, out=None):
+    """Next tokens of sequences whose cache stands anywhere inside a chunk.
+    pos_host: each sequence's position in its current chunk (host int32 [N],
+    the value of cache.pos).  Returns (o, hT) of the new tokens."""
+    dev = q.device
+    T = q.shape[0]
+    n = cu_seqlens.numel() - 1
+    d, Hq, Hv = shape.d_k, shape.H_qk, shape.H_v
+    idt = q.dtype
+    _req(q, idt, (T, Hq, d), "q")
+    _req(k, idt, (T, Hq, d), "k")
+    _req(v, idt, (T, Hv, d), "v")
+    _req(beta, torch.float32, (T, Hv), "beta")
+    _req(g, torch.float32, (T, Hv), "g")
+    cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
+    cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    pos = torch.as_tensor(pos_host, dtype=torch.int32).to("cpu").contiguous()
+    if pos.numel() != n:
+        raise ValueError(f"pos_host: expected {n} values, got {pos.numel()}")
+    o = torch.empty(T, Hv, d, dtype=torch.float32, device=dev) if out is None else out
+    hT = torch.empty(n, Hv, d, d, dtype=torch.float32, device=dev) if want_hT else None
+    ws = _workspace(shape, n, T, OP_PREFILL_CONTINUE, dev, ws)
+    cs = cache.struct()
+    st = lib().gdn_prefill_continue(ctypes.byref(shape), n, _ptr(cu_dev),
+                                    ctypes.c_void_p(cu_host.data_ptr()),
+                                    ctypes.c_void_p(pos.data_ptr()), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(beta), _ptr(g), ctypes.byref(cs), _ptr(o), _ptr(hT),
+                                    _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "gdn_prefill_continue")
     return o, hT
 
 

@@ -2747,6 +2747,139 @@ __global__ __launch_bounds__(256) void k_bwd_qk(BwdIO io) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefill continuation.  Sequence n of the extended batch is the p_n tokens
+// already in its cache's chunk buffers (p_n = pos of head 0, clamped into
+// [0, C) as the decode step clamps it) followed by its new tokens.  The
+// extended batch then goes through the prefill kernels from the chunk-start
+// state S_chunk, which makes every new token's output and the final state
+// those of one prefill over the whole history.
+__global__ void k_cont_plan(const int32_t* __restrict__ cu, const int32_t* __restrict__ pos,
+                            int N, int H_v, int C, int32_t* __restrict__ cu_ext,
+                            int32_t* __restrict__ cu_chunks, int32_t* __restrict__ cu_full) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  int32_t e = 0, a = 0, b = 0;
+  cu_ext[0] = 0;
+  cu_chunks[0] = 0;
+  cu_full[0] = 0;
+  for (int n = 0; n < N; ++n) {
+    int32_t p = pos[static_cast<int64_t>(n) * H_v];
+    p = p < 0 ? 0 : (p >= C ? C - 1 : p);
+    int32_t L = cu[n + 1] - cu[n];
+    L = (L < 0 ? 0 : L) + p;
+    e += L;
+    a += (L + C - 1) / C;
+    b += L / C;
+    cu_ext[n + 1] = e;
+    cu_chunks[n + 1] = a;
+    cu_full[n + 1] = b;
+  }
+}
+
+struct ContIO {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  const int32_t* cu;      // new tokens
+  const int32_t* cu_ext;  // buffered + new tokens
+  const float* kbuf;
+  const void* vbuf;
+  const float* bbuf;
+  const float* gbuf;
+  float* qk;              // prep layout of the extended batch
+  void* v_ext;
+  float* b_ext;
+  float* g_ext;
+  const float* o_ext;
+  float* o;
+  int N, H_qk, H_v, C, l2;
+  float scale;
+  int64_t T, T_ext;       // rows of the new and of the extended batch (bounds)
+};
+
+// Extended-batch inputs, one wave per (extended row, q/k head): buffered rows
+// copy the cache's normalised key (the query of a buffered row only feeds an
+// output that is discarded: 0), value, beta and g; new rows normalise q and k
+// with the lanes and arithmetic of k_prep and copy v, beta and g.
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void k_cont_gather(ContIO io) {
+  const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (vec >= io.T_ext * io.H_qk) return;
+  const int64_t e = vec / io.H_qk;
+  const int hq = static_cast<int>(vec - e * io.H_qk);
+  if (e >= io.cu_ext[io.N]) return;  // uniform over the wave
+  const int n = find_seq(io.cu_ext, io.N, e);
+  const int64_t r = e - io.cu_ext[n];
+  const int64_t p = static_cast<int64_t>(io.cu_ext[n + 1] - io.cu_ext[n]) - (io.cu[n + 1] - io.cu[n]);
+  const int l = threadIdx.x & 63;
+  const int G = io.H_v / io.H_qk;
+  float* out = io.qk + (static_cast<int64_t>(hq) * io.T_ext + e) * 2 * D;
+  const TIn* vin;
+  const float *bin, *gin;
+  int64_t vrow, brow;  // row index of v (x H_v) and of beta / g (x H_v) in their source
+  if (r < p) {
+    const int64_t bt = static_cast<int64_t>(n) * io.C + r;
+    const float* kb = io.kbuf + (bt * io.H_qk + hq) * D;
+    if (l < D) {
+      out[l] = kb[l];
+      out[D + l] = 0.0f;
+    }
+    if (D > 64) {
+      out[l + 64] = kb[l + 64];
+      out[D + l + 64] = 0.0f;
+    }
+    vin = static_cast<const TIn*>(io.vbuf);
+    bin = io.bbuf;
+    gin = io.gbuf;
+    vrow = brow = bt;
+  } else {
+    const int64_t src = io.cu[n] + (r - p);
+    const TIn* kx = static_cast<const TIn*>(io.k) + (src * io.H_qk + hq) * D;
+    const TIn* qx = static_cast<const TIn*>(io.q) + (src * io.H_qk + hq) * D;
+    const float k0 = (l < D) ? ldin(kx + l) : 0.0f, k1 = (D > 64) ? ldin(kx + l + 64) : 0.0f;
+    const float q0 = (l < D) ? ldin(qx + l) : 0.0f, q1 = (D > 64) ? ldin(qx + l + 64) : 0.0f;
+    float y0, y1;
+    l2norm_vals<D>(k0, k1, 1.0f, io.l2, y0, y1);
+    if (l < D) out[l] = y0;
+    if (D > 64) out[l + 64] = y1;
+    l2norm_vals<D>(q0, q1, io.scale, io.l2, y0, y1);
+    if (l < D) out[D + l] = y0;
+    if (D > 64) out[D + l + 64] = y1;
+    vin = static_cast<const TIn*>(io.v);
+    bin = io.beta;
+    gin = io.g;
+    vrow = brow = src;
+  }
+  TIn* vo = static_cast<TIn*>(io.v_ext);
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = hq * G + hh;
+    const TIn* vs = vin + (vrow * io.H_v + h) * D;
+    TIn* vd = vo + (e * io.H_v + h) * D;
+    if (l < D) vd[l] = vs[l];
+    if (D > 64) vd[l + 64] = vs[l + 64];
+    if (l == 0) {
+      io.b_ext[e * io.H_v + h] = bin[brow * io.H_v + h];
+      io.g_ext[e * io.H_v + h] = gin[brow * io.H_v + h];
+    }
+  }
+}
+
+// The new tokens' outputs from the extended batch's, one float4 per thread.
+template <int D>
+__global__ __launch_bounds__(256) void k_cont_scatter(ContIO io) {
+  const int64_t per = static_cast<int64_t>(io.H_v) * D / 4;
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (x >= io.T * per) return;
+  const int64_t s = x / per, rem = x - s * per;
+  const int n = find_seq(io.cu, io.N, s);
+  const int64_t p = static_cast<int64_t>(io.cu_ext[n + 1] - io.cu_ext[n]) - (io.cu[n + 1] - io.cu[n]);
+  const int64_t e = io.cu_ext[n] + p + (s - io.cu[n]);
+  if (e < 0 || e >= io.T_ext) return;
+  reinterpret_cast<float4*>(io.o)[s * per + rem] = reinterpret_cast<const float4*>(io.o_ext)[e * per + rem];
+}
+
+// ---------------------------------------------------------------------------
 // Cache init: S_run = S_chunk = h0 (or 0), pos = 0.  Plain fill kernel (no
 // memset nodes, so the call is safe to capture in a graph).
 __global__ void k_cache_init(const float* __restrict__ h0, float* __restrict__ S_run,
@@ -2872,7 +3005,9 @@ template <int D, int C, typename TIn>
 int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const gdn::Layout& L,
                    const int32_t* cu, const void* q, const void* k, const void* v,
                    const float* beta, const float* g, const float* h0, float* o, float* hT,
-                   const gdn_cache_t* cache, char* ws, hipStream_t st) {
+                   const gdn_cache_t* cache, char* ws, hipStream_t st, bool gathered = false) {
+  // gathered: the chunk plan and the prep layout are already in ws (prefill
+  // continuation); q and k are then not read
   int32_t* cu_chunks = reinterpret_cast<int32_t*>(ws + L.cu_chunks);
   int32_t* cu_full = reinterpret_cast<int32_t*>(ws + L.cu_full);
   float* qk = reinterpret_cast<float*>(ws + L.qk);
@@ -2881,12 +3016,12 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   float* Gs = reinterpret_cast<float*>(ws + L.G);
   float* states = reinterpret_cast<float*>(ws + L.states);
 
-  {
+  if (!gathered) {
     Timed t_("k_plan", st);
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, st, cu, N, C, cu_chunks, cu_full);
   }
   const int64_t nvec = cnt.T * s->H_qk;
-  if (nvec > 0) {
+  if (nvec > 0 && !gathered) {
     Timed t_("k_prep", st);
     hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256), 0,
                        st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
@@ -2926,6 +3061,50 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     const int hpb = rec_heads_per_block<D>(G);
     hipLaunchKernelGGL((k_rec<D, C, TIn>), dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb),
                        dim3(64 * RowSplit<D>::WPH * hpb), 0, st, io, hpb);
+  }
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+template <int D, int C, typename TIn>
+int launch_prefill_continue(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt,
+                            const gdn::Counts& cntx, const gdn::Layout& L, const int32_t* cu,
+                            const void* q, const void* k, const void* v, const float* beta,
+                            const float* g, const gdn_cache_t* cache, float* o, float* hT,
+                            char* ws, hipStream_t st) {
+  int32_t* cu_ext = reinterpret_cast<int32_t*>(ws + L.cu_ext);
+  ContIO io{};
+  io.q = q; io.k = k; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_ext = cu_ext;
+  io.kbuf = cache->kbuf; io.vbuf = cache->vbuf; io.bbuf = cache->bbuf; io.gbuf = cache->gbuf;
+  io.qk = reinterpret_cast<float*>(ws + L.qk);
+  io.v_ext = ws + L.v_ext;
+  io.b_ext = reinterpret_cast<float*>(ws + L.b_ext);
+  io.g_ext = reinterpret_cast<float*>(ws + L.g_ext);
+  io.o_ext = reinterpret_cast<float*>(ws + L.o_ext);
+  io.o = o;
+  io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.C = C; io.l2 = s->qk_l2norm;
+  io.scale = s->scale; io.T = cnt.T; io.T_ext = cntx.T;
+  {
+    Timed t_("k_cont_plan", st);
+    hipLaunchKernelGGL(k_cont_plan, dim3(1), dim3(64), 0, st, cu, cache->pos, N, s->H_v, C, cu_ext,
+                       reinterpret_cast<int32_t*>(ws + L.cu_chunks),
+                       reinterpret_cast<int32_t*>(ws + L.cu_full));
+  }
+  const int64_t nvec = cntx.T * s->H_qk;
+  if (nvec > 0) {
+    Timed t_("k_cont_gather", st);
+    hipLaunchKernelGGL((k_cont_gather<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)),
+                       dim3(256), 0, st, io);
+  }
+  const int rc = launch_prefill<D, C, TIn>(s, N, cntx, L, cu_ext, nullptr, nullptr, io.v_ext,
+                                           io.b_ext, io.g_ext, cache->S_chunk,
+                                           reinterpret_cast<float*>(ws + L.o_ext), hT, cache, ws, st,
+                                           true);
+  if (rc != GDN_OK) return rc;
+  const int64_t n4 = cnt.T * s->H_v * (D / 4);
+  if (n4 > 0) {
+    Timed t_("k_cont_scatter", st);
+    hipLaunchKernelGGL((k_cont_scatter<D>), dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256),
+                       0, st, io);
   }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -3208,6 +3387,42 @@ int gdn_prefill(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seql
   return dispatch(shape, [&]<int D, int C, typename TIn>() {
     return launch_prefill<D, C, TIn>(shape, n_seqs, cnt, L, cu_seqlens_dev, q, k, v, beta, g, h0,
                                      o, hT, cache, w, st);
+  });
+}
+
+int gdn_prefill_continue(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                         const int32_t* cu_seqlens_host, const int32_t* pos_host, const void* q,
+                         const void* k, const void* v, const float* beta, const float* g,
+                         gdn_cache_t* cache, float* o, float* hT, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int rc = gdn::check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host || (n_seqs > 0 && !pos_host))
+    return GDN_ERR_INVALID_ARG;
+  if ((rc = gdn::check_cache(cache)) != GDN_OK) return rc;
+  gdn::Counts cnt;
+  if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
+  if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, o, hT})) return GDN_ERR_INVALID_ARG;
+  // the extended batch: each sequence's buffered tokens, then its new ones
+  std::vector<int32_t> cux(static_cast<size_t>(n_seqs) + 1, 0);
+  for (int32_t n = 0; n < n_seqs; ++n) {
+    const int32_t p = pos_host[n];
+    if (p < 0 || p >= shape->C) return GDN_ERR_INVALID_ARG;
+    const int64_t e = static_cast<int64_t>(cux[n]) + p + (cu_seqlens_host[n + 1] - cu_seqlens_host[n]);
+    if (e > INT32_MAX) return GDN_ERR_INVALID_ARG;
+    cux[n + 1] = static_cast<int32_t>(e);
+  }
+  gdn::Counts cntx;
+  if ((rc = gdn::count_chunks(cux.data(), n_seqs, shape->C, &cntx)) != GDN_OK) return rc;
+  const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_PREFILL_CONTINUE);
+  if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (n_seqs == 0) return GDN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  return dispatch(shape, [&]<int D, int C, typename TIn>() {
+    return launch_prefill_continue<D, C, TIn>(shape, n_seqs, cnt, cntx, L, cu_seqlens_dev, q, k, v,
+                                              beta, g, cache, o, hT, w, st);
   });
 }
 

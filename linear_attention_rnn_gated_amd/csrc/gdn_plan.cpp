@@ -60,8 +60,12 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
     L.total = cur;
     return L;
   }
-  if (op != GDN_OP_PREFILL && op != GDN_OP_FWD_BWD && op != GDN_OP_PREFILL_CHUNKED) return Layout{};
-  const bool all_chunks = op != GDN_OP_PREFILL;  // W, U, G, Delta for every chunk
+  if (op != GDN_OP_PREFILL && op != GDN_OP_FWD_BWD && op != GDN_OP_PREFILL_CHUNKED &&
+      op != GDN_OP_PREFILL_CONTINUE)
+    return Layout{};
+  // the continuation re-runs each sequence's up to C - 1 buffered tokens
+  if (op == GDN_OP_PREFILL_CONTINUE) T += static_cast<int64_t>(N) * (static_cast<int64_t>(C) - 1);
+  const bool all_chunks = op != GDN_OP_PREFILL && op != GDN_OP_PREFILL_CONTINUE;
   L.full_slots = T / static_cast<int64_t>(C);
   L.state_slots = T / static_cast<int64_t>(C) + N;
   L.cu_chunks = take(&cur, (N + 1) * sizeof(int32_t));
@@ -87,6 +91,14 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
     L.MdM = take(&cur, L.state_slots * Hv * f);
     L.dqv = take(&cur, T * Hv * d * f);
     L.dkv = take(&cur, T * Hv * d * f);
+  }
+  if (op == GDN_OP_PREFILL_CONTINUE) {
+    const size_t in = s->in_dtype == GDN_BF16 ? 2 : 4;
+    L.cu_ext = take(&cur, (N + 1) * sizeof(int32_t));
+    L.v_ext = take(&cur, T * Hv * d * in);
+    L.b_ext = take(&cur, T * Hv * f);
+    L.g_ext = take(&cur, T * Hv * f);
+    L.o_ext = take(&cur, T * Hv * d * f);
   }
   L.total = cur;
   return L;

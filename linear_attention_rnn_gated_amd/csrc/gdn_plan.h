@@ -49,6 +49,13 @@ struct Layout {
   size_t MdM = 0;        // f32 [state_slots, H_v]  <S, dS'> per chunk
   size_t dqv = 0;        // f32 [T, H_v, d]  per value head dq-hat
   size_t dkv = 0;        // f32 [T, H_v, d]  per value head dk-hat
+  // prefill continuation only: the extended batch (buffered + new tokens of
+  // every sequence, T' <= T + N (C - 1) rows) and its outputs
+  size_t cu_ext = 0;     // int32 [N+1]  prefix of buffered + new tokens
+  size_t v_ext = 0;      // in_dtype [T', H_v, d]
+  size_t b_ext = 0;      // f32 [T', H_v]
+  size_t g_ext = 0;      // f32 [T', H_v]
+  size_t o_ext = 0;      // f32 [T', H_v, d]
   size_t total = 0;
   int64_t full_slots = 0, state_slots = 0;
 };

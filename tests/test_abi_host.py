@@ -173,3 +173,25 @@ def test_chunked_baseline_claims():
     assert L.gdn_workspace_bytes(ctypes.byref(s), 4, 1000, B.OP_PREFILL_CHUNKED) > 0
     assert L.gdn_prefill_chunked(ctypes.byref(s), 1, a, cu, a, a, a, a, a, None, a, None, None,
                                  1 << 40, None) == B.GDN_ERR_WORKSPACE
+
+
+def test_prefill_continue_argument_checks():
+    """Continuation: pos_host is required and must lie in [0, C); the
+    workspace covers the buffered tokens."""
+    L = B.lib()
+    s = good_shape()
+    cu = (ctypes.c_int32 * 3)(0, 10, 20)
+    a = ctypes.c_void_p(16)
+    cache = B.CacheStruct(*([16] * 7))
+    big = 1 << 40
+    args = lambda pos: (ctypes.byref(s), 2, a, cu, pos, a, a, a, a, a, ctypes.byref(cache), a,
+                        None, a, big, None)
+    assert L.gdn_prefill_continue(*args(None)) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_prefill_continue(*args((ctypes.c_int32 * 2)(0, 64))) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_prefill_continue(*args((ctypes.c_int32 * 2)(-1, 3))) == B.GDN_ERR_INVALID_ARG
+    w_pre = L.gdn_workspace_bytes(ctypes.byref(s), 2, 20, B.OP_PREFILL)
+    w_con = L.gdn_workspace_bytes(ctypes.byref(s), 2, 20, B.OP_PREFILL_CONTINUE)
+    assert w_con > w_pre
+    small = (ctypes.byref(s), 2, a, cu, (ctypes.c_int32 * 2)(3, 63), a, a, a, a, a,
+             ctypes.byref(cache), a, None, a, w_pre, None)
+    assert L.gdn_prefill_continue(*small) == B.GDN_ERR_WORKSPACE

@@ -389,3 +389,104 @@ def test_chunked_baseline_prefill_parity(dtype):
     # the CPR prefill agrees within the same bar (not bit for bit)
     o_c, h_c, _ = run_prefill(inp)
     assert maxabs(o, o_c) <= 2 * TOL[dtype] and maxabs(hT, h_c) <= 2 * TOL[dtype]
+
+
+# ------------------------------------------------------------------ prefill continuation
+
+def _token_range(inp, starts, lens):
+    """Packed sub-batch holding tokens starts[n] .. starts[n] + lens[n] - 1 of
+    each sequence n."""
+    cu = inp["cu_seqlens"].tolist()
+    idx = [torch.arange(cu[n] + s, cu[n] + s + m) for n, (s, m) in enumerate(zip(starts, lens))]
+    idx = torch.cat(idx) if idx else torch.zeros(0, dtype=torch.int64)
+    out = dict(inp)
+    for key in ["q", "k", "v", "beta", "g"]:
+        out[key] = inp[key][idx].contiguous()
+    c = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    c[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int32), 0)
+    out["cu_seqlens"] = c
+    out["T"] = int(sum(lens))
+    return out, idx
+
+
+def _continue(inp_part, cache, shape, pos):
+    d = to_dev(inp_part)
+    return B.gdn_prefill_continue(shape, d["q"], d["k"], d["v"], d["beta"], d["g"],
+                                  d["cu_seqlens"], cache, pos)
+
+
+def _check_cache_equal(c, ref, C):
+    assert bit_equal(c.S_run, ref.S_run) and bit_equal(c.S_chunk, ref.S_chunk)
+    pos = c.pos.cpu()
+    assert torch.equal(pos, ref.pos.cpu())
+    for n in range(pos.shape[0]):  # buffered rows of the current chunk
+        p = int(pos[n, 0])
+        for name in ["kbuf", "vbuf", "bbuf", "gbuf"]:
+            a, b = getattr(c, name)[n, :p], getattr(ref, name)[n, :p]
+            assert torch.equal(a.cpu().view(torch.uint8), b.cpu().view(torch.uint8)), name
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (16, "f32")])
+def test_prefill_continue_equals_one_prefill(d, dtype):
+    """Prefill a first part that stops inside a chunk, then continue with the
+    rest through gdn_prefill_continue (twice): outputs, final states and cache
+    equal one prefill of the whole sequences, bit for bit."""
+    a = [70, 64, 1, 130, 0, 129, 5]
+    b = [50, 0, 100, 3, 64, 200, 0]
+    c = [9, 77, 0, 61, 1, 2, 11]
+    tot = [x + y + z for x, y, z in zip(a, b, c)]
+    say(f"case: continuation d{d} {dtype} parts {a} + {b} + {c}")
+    inp = make_inputs(tot, 2, 4, d, dtype, seed=43, h0="normal")
+    shape = shape_for(inp)
+    C = shape.C
+    o_full, h_full, c_full = run_prefill(inp, cache=True)
+    pa, _ = _token_range(inp, [0] * len(a), a)
+    _, _, cache = run_prefill(pa, cache=True)
+    starts = list(a)
+    for part in (b, c):
+        pb, idx = _token_range(inp, starts, part)
+        pos = [s % C for s in starts]
+        assert torch.equal(cache.pos.cpu()[:, 0], torch.tensor(pos, dtype=torch.int32))
+        o, hT = _continue(pb, cache, shape, pos)
+        assert bit_equal(o, o_full[idx.cuda()]), "o"
+        starts = [s + m for s, m in zip(starts, part)]
+    assert bit_equal(hT, h_full), "hT"
+    _check_cache_equal(cache, c_full, C)
+
+
+def test_decode_then_continue_equals_one_prefill():
+    """Prefill, a few decode steps (positions spread over the chunk), then a
+    continuation: equals one prefill, bit for bit; decoding afterwards still
+    matches."""
+    a = [70, 64, 1, 130, 0, 129]
+    steps, b, tail = 7, [90, 1, 64, 0, 130, 57], 5
+    tot = [x + steps + y + tail for x, y in zip(a, b)]
+    say(f"case: prefill {a} + decode {steps} + continue {b} + decode {tail}")
+    inp = make_inputs(tot, 2, 4, 128, "bf16", seed=44, h0="normal")
+    shape = shape_for(inp)
+    C = shape.C
+    o_full, h_full, c_full = run_prefill(inp, cache=True)
+    pa, _ = _token_range(inp, [0] * len(a), a)
+    _, _, cache = run_prefill(pa, cache=True)
+    cu = inp["cu_seqlens"].tolist()
+    N = len(a)
+
+    def step_tokens(starts):
+        idx = torch.tensor([cu[n] + starts[n] for n in range(N)])
+        d = {k: inp[k][idx].cuda().contiguous() for k in ["q", "k", "v", "beta", "g"]}
+        o = B.gdn_decode_step(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], cache)
+        assert bit_equal(o, o_full[(idx).cuda()]), "decode o"
+
+    starts = list(a)
+    for _ in range(steps):
+        step_tokens(starts)
+        starts = [s + 1 for s in starts]
+    pb, idx = _token_range(inp, starts, b)
+    o, _ = _continue(pb, cache, shape, [s % C for s in starts])
+    assert bit_equal(o, o_full[idx.cuda()]), "continue o"
+    starts = [s + m for s, m in zip(starts, b)]
+    for _ in range(tail):
+        step_tokens(starts)
+        starts = [s + 1 for s in starts]
+    assert bit_equal(cache.S_run, h_full)
+    _check_cache_equal(cache, c_full, C)
