@@ -193,6 +193,21 @@ int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs,
                 size_t ws_bytes, void* stream);
 
 /*
+ * gdn_fwd_bwd with the input-shaped gradients dq, dk [T, H_qk, d_k] and dv
+ * [T, H_v, d_v] written in grad_dtype: GDN_F32 (then identical to
+ * gdn_fwd_bwd) or GDN_BF16, the fp32 result rounded to nearest even (the
+ * trainer that keeps its parameters and activations in bf16).  dbeta, dg and
+ * dh0 stay fp32.  GDN_ERR_INVALID_ARG for any other grad_dtype.
+ */
+int gdn_fwd_bwd_ex(const gdn_shape_t* shape, int32_t n_seqs,
+                   const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                   const void* q, const void* k, const void* v, const float* beta,
+                   const float* g, const float* h0, const float* dO,
+                   const float* dhT, float* o, float* hT, int32_t grad_dtype,
+                   void* dq, void* dk, void* dv, float* dbeta, float* dg,
+                   float* dh0, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Native-mixed baseline (not the CPR contract): prefill whose outputs come
  * from the chunk form instead of the token recurrence,
  *     o_p = exp(G_p) S_c q_p + sum_{r<=p} (q_p . k_r) exp(G_p - G_r) Delta_r

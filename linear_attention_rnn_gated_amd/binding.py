@@ -25,7 +25,7 @@ OP_PREFILL, OP_DECODE, OP_FWD_BWD, OP_PREFILL_CHUNKED, OP_PREFILL_CONTINUE = 0, 
 EXPORTS = ["gdn_workspace_bytes", "gdn_cache_init", "gdn_prefill", "gdn_decode_step",
            "gdn_fwd_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_contract_id",
            "gdn_contract_check", "gdn_error_string", "gdn_prefill_chunked",
-           "gdn_prefill_continue"]
+           "gdn_prefill_continue", "gdn_fwd_bwd_ex"]
 
 
 class Shape(ctypes.Structure):
@@ -72,6 +72,9 @@ def lib():
         L.gdn_fwd_bwd.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_fwd_bwd.restype = ctypes.c_int
+        L.gdn_fwd_bwd_ex.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                     vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_fwd_bwd_ex.restype = ctypes.c_int
         L.gdn_profile_enable.argtypes = [ctypes.c_int]
         L.gdn_profile_enable.restype = ctypes.c_int
         L.gdn_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -311,8 +314,10 @@ def gdn_decode_step(shape, q, k, v, beta, g, cache, pos_host=None, ws=None, out=
     return o
 
 
-def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=None):
-    """Trainer forward + backward.  Returns dict(o, hT, dq, dk, dv, dbeta, dg, dh0)."""
+def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=None,
+                grad_dtype=torch.float32):
+    """Trainer forward + backward.  Returns dict(o, hT, dq, dk, dv, dbeta, dg, dh0);
+    dq, dk, dv in grad_dtype (float32 or bfloat16), the rest float32."""
     dev = q.device
     T = q.shape[0]
     n = cu_seqlens.numel() - 1
@@ -331,16 +336,18 @@ def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=N
     cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
     cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
     f32 = dict(dtype=torch.float32, device=dev)
+    gd = dict(dtype=grad_dtype, device=dev)
+    code = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}[grad_dtype]
     r = dict(o=torch.empty(T, Hv, d, **f32), hT=torch.empty(n, Hv, d, d, **f32),
-             dq=torch.empty(T, Hq, d, **f32), dk=torch.empty(T, Hq, d, **f32),
-             dv=torch.empty(T, Hv, d, **f32), dbeta=torch.empty(T, Hv, **f32),
+             dq=torch.empty(T, Hq, d, **gd), dk=torch.empty(T, Hq, d, **gd),
+             dv=torch.empty(T, Hv, d, **gd), dbeta=torch.empty(T, Hv, **f32),
              dg=torch.empty(T, Hv, **f32), dh0=torch.empty(n, Hv, d, d, **f32))
     ws = _workspace(shape, n, T, OP_FWD_BWD, dev, ws)
-    st = lib().gdn_fwd_bwd(ctypes.byref(shape), n, _ptr(cu_dev),
-                           ctypes.c_void_p(cu_host.data_ptr()), _ptr(q), _ptr(k), _ptr(v),
-                           _ptr(beta), _ptr(g), _ptr(h0), _ptr(dO), _ptr(dhT), _ptr(r["o"]),
-                           _ptr(r["hT"]), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]),
-                           _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dh0"]), _ptr(ws),
-                           ws.numel(), _stream(dev))
-    _check(st, "gdn_fwd_bwd")
+    st = lib().gdn_fwd_bwd_ex(ctypes.byref(shape), n, _ptr(cu_dev),
+                              ctypes.c_void_p(cu_host.data_ptr()), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(beta), _ptr(g), _ptr(h0), _ptr(dO), _ptr(dhT), _ptr(r["o"]),
+                              _ptr(r["hT"]), code, _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]),
+                              _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dh0"]), _ptr(ws),
+                              ws.numel(), _stream(dev))
+    _check(st, "gdn_fwd_bwd_ex")
     return r

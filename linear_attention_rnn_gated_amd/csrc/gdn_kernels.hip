@@ -1284,16 +1284,30 @@ struct BwdIO {
   float* MdM;             // [slot][H_v] <S, dS'> of each chunk (matrix-core path)
   float* dqv;             // [T][H_v][D] per value head
   float* dkv;             // [T][H_v][D]
-  float* dv;              // [T][H_v][D]
+  void* dv;               // [T][H_v][D], fp32 or (grad_bf16) bf16
   float* dbeta;           // [T][H_v]
   float* dg;              // [T][H_v]
-  float* dq;              // [T][H_qk][D]
-  float* dk;
+  void* dq;               // [T][H_qk][D], fp32 or (grad_bf16) bf16
+  void* dk;
   float* dh0;             // [N][H_v][D][D]
   int N, H_qk, H_v, l2;
+  int grad_bf16;          // dq, dk, dv as bf16 (round to nearest even)
   float scale;
   int64_t T, max_state_slot;
 };
+
+// Element i of a gradient output: fp32, or bf16 rounded to nearest even from
+// the fp32 value (a NaN stays a NaN).
+__device__ __forceinline__ void st_grad(void* base, int64_t i, float x, int bf16) {
+  if (bf16) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t r = (u & 0x7fffffffu) > 0x7f800000u ? (u >> 16) | 0x40u
+                                                        : (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    static_cast<uint16_t*>(base)[i] = static_cast<uint16_t>(r);
+  } else {
+    static_cast<float*>(base)[i] = x;
+  }
+}
 
 // Chunk item of a backward kernel: slot = blockIdx.x over every chunk.
 template <int C>
@@ -1674,7 +1688,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdIO io) {
     for (int r = 0; r < p; ++r) ak = fmaf(sdA[p][r], sK[r][i], ak);
     for (int q = p + 1; q < L; ++q) ak = fmaf(sdA[q][p], sK[q][i], ak);
     io.dkv[o] = ak;
-    io.dv[o] = sB[p] * sY[p][D + i];
+    st_grad(io.dv, o, sB[p] * sY[p][D + i], io.grad_bf16);
   }
   if (tid == 0) {  // dg = reverse running sum of dG within the chunk
     float acc = 0.0f;
@@ -2674,7 +2688,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   for (int e_ = 0; e_ < (C * D) / 512; ++e_) {
     const int e = tid + 512 * e_;
     const int pp = e / D, j = e % D;
-    if (pp < L) io.dv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + j] = sB[pp] * sY[pp * YS + D + j];
+    if (pp < L)
+      st_grad(io.dv, (tok0 + pp) * vs + static_cast<int64_t>(h) * D + j, sB[pp] * sY[pp * YS + D + j],
+              io.grad_bf16);
   }
   // dg: reverse running sum over the chunk (p descending), taken by one lane
   // from registers; then every lane stores its token
@@ -2724,7 +2740,8 @@ __global__ __launch_bounds__(256) void k_bwd_qk(BwdIO io) {
       if (D > 64) g1 = g1 + row[l + 64];
     }
     const float mul = which == 0 ? io.scale : 1.0f;
-    float* dst = (which == 0 ? io.dq : io.dk) + vec * D;
+    void* dst = which == 0 ? io.dq : io.dk;
+    const int64_t d0 = vec * D;
     if (io.l2) {
       const TIn* x = static_cast<const TIn*>(which == 0 ? io.q : io.k) + vec * D;
       const float x0 = l < D ? ldin(x + l) : 0.0f;
@@ -2737,11 +2754,11 @@ __global__ __launch_bounds__(256) void k_bwd_qk(BwdIO io) {
       float dot = fmaf(n1, g1, n0 * g0);
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
-      if (l < D) dst[l] = mul * r * (g0 - n0 * dot);
-      if (D > 64) dst[l + 64] = mul * r * (g1 - n1 * dot);
+      if (l < D) st_grad(dst, d0 + l, mul * r * (g0 - n0 * dot), io.grad_bf16);
+      if (D > 64) st_grad(dst, d0 + l + 64, mul * r * (g1 - n1 * dot), io.grad_bf16);
     } else {
-      if (l < D) dst[l] = mul * g0;
-      if (D > 64) dst[l + 64] = mul * g1;
+      if (l < D) st_grad(dst, d0 + l, mul * g0, io.grad_bf16);
+      if (D > 64) st_grad(dst, d0 + l + 64, mul * g1, io.grad_bf16);
     }
   }
 }
@@ -3149,8 +3166,8 @@ template <int D, int C, typename TIn>
 int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const gdn::Layout& L,
                    const int32_t* cu, const void* q, const void* k, const void* v,
                    const float* beta, const float* g, const float* h0, const float* dO,
-                   const float* dhT, float* o, float* hT, float* dq, float* dk, float* dv,
-                   float* dbeta, float* dg, float* dh0, char* ws, hipStream_t st) {
+                   const float* dhT, float* o, float* hT, void* dq, void* dk, void* dv,
+                   int grad_bf16, float* dbeta, float* dg, float* dh0, char* ws, hipStream_t st) {
   int32_t* cu_chunks = reinterpret_cast<int32_t*>(ws + L.cu_chunks);
   int32_t* cu_full = reinterpret_cast<int32_t*>(ws + L.cu_full);
   float* qk = reinterpret_cast<float*>(ws + L.qk);
@@ -3214,6 +3231,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   b.dqv = reinterpret_cast<float*>(ws + L.dqv);
   b.dkv = reinterpret_cast<float*>(ws + L.dkv);
   b.dv = dv; b.dbeta = dbeta; b.dg = dg; b.dq = dq; b.dk = dk; b.dh0 = dh0;
+  b.grad_bf16 = grad_bf16;
   b.N = N; b.H_qk = s->H_qk; b.H_v = s->H_v; b.l2 = s->qk_l2norm; b.scale = s->scale;
   b.T = cnt.T; b.max_state_slot = L.state_slots;
   const dim3 cgrid(static_cast<unsigned>(cnt.chunks > 0 ? cnt.chunks : 1), s->H_v);
@@ -3455,13 +3473,15 @@ int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q, con
   });
 }
 
-int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
-                const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
-                const float* beta, const float* g, const float* h0, const float* dO,
-                const float* dhT, float* o, float* hT, float* dq, float* dk, float* dv,
-                float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+int gdn_fwd_bwd_ex(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                   const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
+                   const float* beta, const float* g, const float* h0, const float* dO,
+                   const float* dhT, float* o, float* hT, int32_t grad_dtype, void* dq, void* dk,
+                   void* dv, float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
+                   void* stream) {
   int rc = gdn::check_shape(shape);
   if (rc != GDN_OK) return rc;
+  if (grad_dtype != GDN_F32 && grad_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host) return GDN_ERR_INVALID_ARG;
   gdn::Counts cnt;
   if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
@@ -3476,10 +3496,20 @@ int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seql
   if (n_seqs == 0) return GDN_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
+  const int bf16 = grad_dtype == GDN_BF16 ? 1 : 0;
   return dispatch(shape, [&]<int D, int C, typename TIn>() {
     return launch_fwd_bwd<D, C, TIn>(shape, n_seqs, cnt, L, cu_seqlens_dev, q, k, v, beta, g, h0,
-                                     dO, dhT, o, hT, dq, dk, dv, dbeta, dg, dh0, w, st);
+                                     dO, dhT, o, hT, dq, dk, dv, bf16, dbeta, dg, dh0, w, st);
   });
+}
+
+int gdn_fwd_bwd(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
+                const float* beta, const float* g, const float* h0, const float* dO,
+                const float* dhT, float* o, float* hT, float* dq, float* dk, float* dv,
+                float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+  return gdn_fwd_bwd_ex(shape, n_seqs, cu_seqlens_dev, cu_seqlens_host, q, k, v, beta, g, h0, dO,
+                        dhT, o, hT, GDN_F32, dq, dk, dv, dbeta, dg, dh0, ws, ws_bytes, stream);
 }
 
 int gdn_prefill_chunked(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,

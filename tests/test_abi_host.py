@@ -195,3 +195,15 @@ def test_prefill_continue_argument_checks():
     small = (ctypes.byref(s), 2, a, cu, (ctypes.c_int32 * 2)(3, 63), a, a, a, a, a,
              ctypes.byref(cache), a, None, a, w_pre, None)
     assert L.gdn_prefill_continue(*small) == B.GDN_ERR_WORKSPACE
+
+
+def test_fwd_bwd_ex_grad_dtype_check():
+    """gdn_fwd_bwd_ex takes grad_dtype GDN_F32 or GDN_BF16 only."""
+    L = B.lib()
+    s = good_shape()
+    cu = (ctypes.c_int32 * 2)(0, 10)
+    a = ctypes.c_void_p(16)
+    args = lambda gd: (ctypes.byref(s), 1, a, cu, a, a, a, a, a, None, a, None, a, a, gd, a, a, a,
+                       a, a, a, None, 0, None)
+    assert L.gdn_fwd_bwd_ex(*args(7)) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_fwd_bwd_ex(*args(B.GDN_BF16)) == B.GDN_ERR_WORKSPACE

@@ -115,3 +115,33 @@ def test_fwd_bwd_b8_t4096_full_size():
     r2 = run_fwd_bwd(inp)
     for k in ["o"] + GRADS:
         assert bit_equal(r1[k], r2[k]), k
+
+
+@pytest.mark.parametrize("dtype,lens,d,Hq,Hv", [
+    ("f32", [37, 16, 5], 16, 1, 2),
+    ("bf16", [150, 64, 1, 77], 128, 2, 4),
+])
+def test_fwd_bwd_bf16_gradient_outputs(dtype, lens, d, Hq, Hv):
+    """grad_dtype=bf16: dq, dk, dv are the fp32 gradients rounded to nearest
+    even (bit for bit what torch's fp32 -> bf16 conversion gives); everything
+    else is unchanged.  Against the oracle the bar adds bf16's half ulp."""
+    say(f"case: fwd_bwd bf16 gradient outputs, {dtype} d{d} lens={lens} H {Hq}/{Hv}")
+    inp = make_inputs(lens, Hq, Hv, d, dtype, seed=34, h0="normal", with_do=True)
+    shape = shape_for(inp)
+    dd = to_dev(inp)
+    args = (shape, dd["q"], dd["k"], dd["v"], dd["beta"], dd["g"], dd["cu_seqlens"], dd["do"])
+    r32 = B.gdn_fwd_bwd(*args, h0=dd["h0"])
+    r16 = B.gdn_fwd_bwd(*args, h0=dd["h0"], grad_dtype=torch.bfloat16)
+    for k in ["dq", "dk", "dv"]:
+        assert r16[k].dtype == torch.bfloat16
+        assert torch.equal(r16[k].view(torch.int16), r32[k].to(torch.bfloat16).view(torch.int16)), k
+    for k in ["o", "hT", "dbeta", "dg", "dh0"]:
+        assert bit_equal(r16[k], r32[k]), k
+    ref = oracle_bwd(inp)
+    for k in ["dq", "dk", "dv"]:
+        got = r16[k].double().cpu().numpy()
+        bar = 2.0 ** -8 * np.abs(ref[k]) + TOL[dtype] * (max(1.0, float(np.max(np.abs(ref[k]))))
+                                                       if dtype == "f32" and d == 128 else 1.0)
+        err = np.abs(got - ref[k])
+        say(f"  {k}: max err {err.max():.2e}, max err / bar {(err / bar).max():.2f}")
+        assert np.all(err <= bar), k
