@@ -3,11 +3,14 @@
 Main line: prefill throughput (tokens/s) on B=4, T=2048, 16 q/k heads, 32 v
 heads, d=128, C=64, bf16 inputs, fp32 state and arithmetic, h0 ~ N(0, 0.02).
 A "step" is one gdn_prefill call over that batch, inputs already in HBM.
-Also reported: decode us/step for 64 sequences after a 4096-token prefill
-(256 steps, resync steps included), and the fp64 oracle's CPU throughput on a
-bounded sample of the prefill workload.
+Also reported: the same batch through the native-mixed baseline
+(gdn_prefill_chunked), decode us/step for 64 sequences after a 4096-token
+prefill (256 steps, resync steps included), trainer fwd+bwd on B=8, T=4096,
+a packed varlen prefill (32 sequences, lengths uniform in [128, 8192]), and
+the fp64 oracle's CPU throughput on a bounded sample of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+                       [--no-train] [--no-varlen]
 """
 
 import argparse
@@ -45,6 +48,7 @@ def measured_traffic(kernel):
 PREFILL = dict(N=4, T=2048, H_qk=16, H_v=32, d=128, C=64)
 DECODE = dict(N=64, P=4096, S=256, H_qk=16, H_v=32, d=128, C=64)
 TRAIN = dict(N=8, T=4096, H_qk=16, H_v=32, d=128, C=64)
+VARLEN = dict(N=32, lo=128, hi=8192, seed=4, H_qk=16, H_v=32, d=128, C=64)
 
 
 def r_flops_per_token_head(d):
@@ -78,6 +82,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--train-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (the reference kernel for "
@@ -167,6 +172,49 @@ def bench_native_mixed(args, B, torch, pf):
     return dict(ms_per_step=round(ms_step, 4), tokens_per_s=round(T / (ms_step * 1e-3), 1),
                 cpr_over_native=round(pf["ms_per_step"] / ms_step, 3),
                 per_kernel_us=per_kernel)
+
+
+def bench_varlen(args, B, torch, make_inputs):
+    """One packed gdn_prefill over 32 sequences of lengths uniform in
+    [128, 8192] (about 148k tokens at seed 4)."""
+    c = VARLEN
+    dev = "cuda"
+    inp = make_inputs(("uniform", c["N"], c["lo"], c["hi"]), c["H_qk"], c["H_v"], c["d"], "bf16",
+                      seed=c["seed"], h0="zero", device=dev)
+    shape = B.make_shape(c["H_qk"], c["H_v"], c["d"], c["C"], torch.bfloat16)
+    T = inp["T"]
+    ws = torch.empty(B.workspace_bytes(shape, c["N"], T, B.OP_PREFILL), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty(T, c["H_v"], c["d"], dtype=torch.float32, device=dev)
+    cu = inp["cu_seqlens"].to(dev)
+
+    def step():
+        B.gdn_prefill(shape, inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], cu,
+                      h0=None, ws=ws, out=o)
+
+    step()
+    torch.cuda.synchronize()
+    B.profile_read("")
+    B.profile_enable(True)
+    reps = 5
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.profile_enable(False)
+    per = {}
+    for name in ["k_plan", "k_prep", "k_wy", "k_scan", "k_rec"]:
+        ms, n = B.profile_read(name)
+        per[name] = round(1e3 * ms / max(n, 1), 1)
+    ms_step = 1e3 * (t1 - t0) / reps
+    rec_flops = r_flops_per_token_head(c["d"]) * T * c["H_v"]
+    return dict(ms_per_step=round(ms_step, 3), tokens=T,
+                tokens_per_s=round(T / (ms_step * 1e-3), 1),
+                k_rec_tflops=round(rec_flops / (per["k_rec"] * 1e-6) / 1e12, 2),
+                per_kernel_us=per,
+                workload="varlen prefill, 32 seqs, lengths U[128, 8192] (seed 4), 16 q/k / 32 v "
+                         "heads, d128 C64 bf16, h0 = 0")
 
 
 def bench_decode(args, B, torch, make_inputs):
@@ -360,6 +408,8 @@ def main():
         line["decode"] = dc
     if not args.no_train:
         line["fwd_bwd"] = bench_fwd_bwd(args, B, torch, make_inputs)
+    if not args.no_varlen:
+        line["varlen"] = bench_varlen(args, B, torch, make_inputs)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(pf["inputs"])
     print(json.dumps(line), flush=True)

@@ -34,13 +34,18 @@ def make_inputs(lens, H_qk, H_v, d, dtype="bf16", seed=0, h0="zero",
     beta, g [T, H_v] fp32; h0 [N, H_v, d, d_v] fp32 or None; do [T, H_v, d_v]
     fp32 or None; cu_seqlens int32 [N + 1]; plus the shape fields.  With
     device="cuda" the tensors are drawn there by that device's generator (same
-    recipe, different stream of numbers; used for large benchmark inputs).
+    recipe, different stream of numbers; used for large benchmark inputs); the
+    lengths of the uniform mix are the CPU generator's first draw on every
+    device, so a benchmark's batch has the tests' lengths.
     """
     d_v = d if d_v is None else d_v
     gen = torch.Generator(device=device).manual_seed(seed)
     if isinstance(lens, tuple) and lens and lens[0] == "uniform":
         _, n, lo, hi = lens
-        lens = [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=gen, device=device)]
+        if torch.device(device).type == "cpu":
+            lens = [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=gen)]
+        else:
+            lens = uniform_lengths(n, lo, hi, seed)
     lens = [int(x) for x in lens]
     T = sum(lens)
     N = len(lens)
