@@ -1806,6 +1806,17 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
     *reinterpret_cast<float4*>(sQ + p * S1 + 4 * i4) = sel4(p < L, q4, z);
   }
   if (tid < C) sG[tid] = io.G[sh * C + tid];
+  // dO rows, fetched now (after the loads the products wait for) and staged
+  // once Q and K are dead
+  const float* dO = io.dO + (tok0 * io.H_v + h) * D;
+  float4 po[(C * (D / 4)) / 256];
+#pragma unroll
+  for (int e_ = 0; e_ < (C * (D / 4)) / 256; ++e_) {
+    const int e = tid + 256 * e_;
+    const int p = e / (D / 4), i4 = e % (D / 4);
+    const int pc = p < L ? p : L - 1;
+    po[e_] = *reinterpret_cast<const float4*>(dO + static_cast<int64_t>(pc) * io.H_v * D + 4 * i4);
+  }
   __syncthreads();
   float P[4][4];  // rows p = 16 w + 4 g + r, columns r' = 16 nb + l16
 #pragma unroll
@@ -1824,15 +1835,11 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) PT[(16 * nb + l16) * S2 + 16 * w + 4 * g + r] = P[nb][r];
-  const float* dO = io.dO + (tok0 * io.H_v + h) * D;
-  static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
 #pragma unroll
   for (int e_ = 0; e_ < (C * (D / 4)) / 256; ++e_) {
     const int e = tid + 256 * e_;
     const int p = e / (D / 4), i4 = e % (D / 4);
-    const int pc = p < L ? p : L - 1;
-    const float4 x = *reinterpret_cast<const float4*>(dO + static_cast<int64_t>(pc) * io.H_v * D + 4 * i4);
-    *reinterpret_cast<float4*>(sO + p * S1 + 4 * i4) = sel4(p < L, x, float4{0.0f, 0.0f, 0.0f, 0.0f});
+    *reinterpret_cast<float4*>(sO + p * S1 + 4 * i4) = sel4(p < L, po[e_], float4{0.0f, 0.0f, 0.0f, 0.0f});
   }
   __syncthreads();
   float* E = io.E + sh * static_cast<int64_t>(C) * D;
