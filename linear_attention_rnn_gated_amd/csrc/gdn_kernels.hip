@@ -2730,42 +2730,62 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
 
 // Sum over the value heads of each group (ascending head order), then the L2
 // norm backward: dx = s r (dxh - n (n . dxh)), n = x r, r = (sum x^2 + eps)^-1/2.
+// Each wave takes kQkVecs consecutive (token, q/k head) vectors; their loads
+// are issued together, and every vector keeps the lanes and order of the
+// one-vector form.
+constexpr int kQkVecs = 4;
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void k_bwd_qk(BwdIO io) {
-  const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // t*H_qk + hq
-  if (vec >= io.T * io.H_qk) return;
-  const int64_t t = vec / io.H_qk;
-  const int hq = static_cast<int>(vec - t * io.H_qk);
+  const int64_t nvec = io.T * io.H_qk;
+  const int64_t vec0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kQkVecs;
+  if (vec0 >= nvec) return;
   const int G = io.H_v / io.H_qk;
   const int l = threadIdx.x & 63;
+  int64_t vecs[kQkVecs];  // t * H_qk + hq, clamped into range (extra ones are not stored)
+#pragma unroll
+  for (int v = 0; v < kQkVecs; ++v) vecs[v] = vec0 + v < nvec ? vec0 + v : nvec - 1;
   for (int which = 0; which < 2; ++which) {  // 0: q, 1: k
     const float* src = which == 0 ? io.dqv : io.dkv;
-    float g0 = 0.0f, g1 = 0.0f;
+    float g0[kQkVecs], g1[kQkVecs], x0[kQkVecs], x1[kQkVecs];
+#pragma unroll
+    for (int v = 0; v < kQkVecs; ++v) {
+      g0[v] = 0.0f;
+      g1[v] = 0.0f;
+      const TIn* x = static_cast<const TIn*>(which == 0 ? io.q : io.k) + vecs[v] * D;
+      x0[v] = l < D ? ldin(x + l) : 0.0f;
+      x1[v] = D > 64 ? ldin(x + l + 64) : 0.0f;
+    }
     for (int gg = 0; gg < G; ++gg) {
-      const float* row = src + (t * io.H_v + static_cast<int64_t>(hq) * G + gg) * D;
-      if (l < D) g0 = g0 + row[l];
-      if (D > 64) g1 = g1 + row[l + 64];
+#pragma unroll
+      for (int v = 0; v < kQkVecs; ++v) {
+        const int64_t t = vecs[v] / io.H_qk;
+        const int hq = static_cast<int>(vecs[v] - t * io.H_qk);
+        const float* row = src + (t * io.H_v + static_cast<int64_t>(hq) * G + gg) * D;
+        if (l < D) g0[v] = g0[v] + row[l];
+        if (D > 64) g1[v] = g1[v] + row[l + 64];
+      }
     }
     const float mul = which == 0 ? io.scale : 1.0f;
     void* dst = which == 0 ? io.dq : io.dk;
-    const int64_t d0 = vec * D;
-    if (io.l2) {
-      const TIn* x = static_cast<const TIn*>(which == 0 ? io.q : io.k) + vec * D;
-      const float x0 = l < D ? ldin(x + l) : 0.0f;
-      const float x1 = D > 64 ? ldin(x + l + 64) : 0.0f;
-      float ss = fmaf(x1, x1, x0 * x0);
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-      const float r = 1.0f / sqrtf(ss + gdn::kNormEps);
-      const float n0 = x0 * r, n1 = x1 * r;
-      float dot = fmaf(n1, g1, n0 * g0);
+    for (int v = 0; v < kQkVecs; ++v) {
+      if (vec0 + v >= nvec) break;  // uniform over the wave
+      const int64_t d0 = (vec0 + v) * D;
+      if (io.l2) {
+        float ss = fmaf(x1[v], x1[v], x0[v] * x0[v]);
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
-      if (l < D) st_grad(dst, d0 + l, mul * r * (g0 - n0 * dot), io.grad_bf16);
-      if (D > 64) st_grad(dst, d0 + l + 64, mul * r * (g1 - n1 * dot), io.grad_bf16);
-    } else {
-      if (l < D) st_grad(dst, d0 + l, mul * g0, io.grad_bf16);
-      if (D > 64) st_grad(dst, d0 + l + 64, mul * g1, io.grad_bf16);
+        for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+        const float r = 1.0f / sqrtf(ss + gdn::kNormEps);
+        const float n0 = x0[v] * r, n1 = x1[v] * r;
+        float dot = fmaf(n1, g1[v], n0 * g0[v]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+        if (l < D) st_grad(dst, d0 + l, mul * r * (g0[v] - n0 * dot), io.grad_bf16);
+        if (D > 64) st_grad(dst, d0 + l + 64, mul * r * (g1[v] - n1 * dot), io.grad_bf16);
+      } else {
+        if (l < D) st_grad(dst, d0 + l, mul * g0[v], io.grad_bf16);
+        if (D > 64) st_grad(dst, d0 + l + 64, mul * g1[v], io.grad_bf16);
+      }
     }
   }
 }
@@ -3281,8 +3301,9 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   }
   if (nvec > 0) {
     Timed t_("k_bwd_qk", st);
-    hipLaunchKernelGGL((k_bwd_qk<D, TIn>), dim3(static_cast<unsigned>((nvec + 3) / 4)), dim3(256),
-                       0, st, b);
+    hipLaunchKernelGGL((k_bwd_qk<D, TIn>),
+                       dim3(static_cast<unsigned>((nvec + 4 * kQkVecs - 1) / (4 * kQkVecs))),
+                       dim3(256), 0, st, b);
   }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
