@@ -259,26 +259,71 @@ def bench_decode(args, B, torch, make_inputs):
             if rc != 0:
                 raise RuntimeError(f"gdn_decode_step: {rc}")
 
-    run_steps()  # warm-up pass
-    times = []
-    per = {"k_decode": [0.0, 0], "k_wy_resync": [0.0, 0], "k_scan_resync": [0.0, 0]}
-    for rep in range(args.decode_reps):
+    def restore():
         for dst, src in zip(cache.tensors(), snap.tensors()):
             dst.copy_(src)
         torch.cuda.synchronize()
-        B.profile_read("")
-        B.profile_enable(True)
+
+    run_steps()  # warm-up pass
+    # wall clock without the timing events, then one pass with them for the
+    # per-kernel split
+    times = []
+    for rep in range(args.decode_reps):
+        restore()
         t0 = time.perf_counter()
         run_steps()
         torch.cuda.synchronize()
         times.append(time.perf_counter() - t0)
-        B.profile_enable(False)
-        for name in per:
-            ms, n = B.profile_read(name)
-            per[name][0] += ms
-            per[name][1] += n
+    per = {"k_decode": [0.0, 0], "k_wy_resync": [0.0, 0], "k_scan_resync": [0.0, 0]}
+    restore()
+    B.profile_read("")
+    B.profile_enable(True)
+    run_steps()
+    torch.cuda.synchronize()
+    B.profile_enable(False)
+    for name in per:
+        ms, n = B.profile_read(name)
+        per[name][0] += ms
+        per[name][1] += n
+    # the same 256 calls captured once in a HIP graph and replayed (the serving
+    # form: the host mirror of pos records the resync launches where they fall)
+    graph = torch.cuda.CUDAGraph()
+    restore()
+    with torch.cuda.graph(graph):
+        stc = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for s in range(S):
+            a = args_s[s]
+            rc = L.gdn_decode_step(shp, N, a[0], a[1], a[2], a[3], a[4], csp, a[5], op, wsp,
+                                   wsn, stc)
+            if rc != 0:
+                raise RuntimeError(f"gdn_decode_step (capture): {rc}")
+    gtimes = []
+    for rep in range(args.decode_reps):
+        restore()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        gtimes.append(time.perf_counter() - t0)
     us_step = 1e6 * min(times) / S
-    dec_us = 1e3 * per["k_decode"][0] / max(per["k_decode"][1], 1)
+    us_graph = 1e6 * min(gtimes) / S
+    # k_decode's own duration: the first C - 1 steps (no resync falls there,
+    # every sequence starts at a chunk edge) between two events on the launch
+    # stream; events around every launch would add their own cost to a 40 us
+    # kernel
+    assert int(pos0.max()) == 0
+    nwin = c["C"] - 1
+    dwin = []
+    for rep in range(args.decode_reps):
+        restore()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(nwin):
+            a = args_s[s]
+            L.gdn_decode_step(shp, N, a[0], a[1], a[2], a[3], a[4], csp, a[5], op, wsp, wsn, st)
+        e1.record()
+        torch.cuda.synchronize()
+        dwin.append(e0.elapsed_time(e1) * 1e3 / nwin)
+    dec_us = min(dwin)
     G = c["H_v"] // c["H_qk"]
     step_bytes_alg = decode_bytes_per_seq_head(c["d"], c["C"], G) * N * c["H_v"]
     dec_kernel_bytes = (2 * c["d"] * c["d"] * 4 + (2 * c["d"] * 2) / G + c["d"] * 2 + 8 +
@@ -286,8 +331,11 @@ def bench_decode(args, B, torch, make_inputs):
     achieved = dec_kernel_bytes / (dec_us * 1e-6) / 1e9
     return dict(us_per_step=round(us_step, 2),
                 step_hbm_frac=round(step_bytes_alg / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                us_per_step_graph=round(us_graph, 2),
+                step_hbm_frac_graph=round(step_bytes_alg / (us_graph * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                 per_kernel={k: dict(avg_us=1e3 * v[0] / max(v[1], 1), launches=v[1])
                             for k, v in per.items()},
+                k_decode_window_us=round(dec_us, 2),
                 roofline=dict(kernel="k_decode", bound="hbm", achieved=round(achieved, 1),
                               peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(achieved / PEAK_HBM_GBS, 4),
