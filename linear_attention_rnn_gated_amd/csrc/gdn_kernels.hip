@@ -140,6 +140,20 @@ __global__ void k_plan(const int32_t* __restrict__ cu, int N, int C, int32_t* __
   }
 }
 
+// Sequences by length, longest first (ties by index): order[rank] = n.  One
+// thread per sequence counts the sequences ranked ahead of it.
+__global__ void k_order(const int32_t* __restrict__ cu, int N, int32_t* __restrict__ order) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const int32_t Ln = cu[n + 1] - cu[n];
+  int rank = 0;
+  for (int m = 0; m < N; ++m) {
+    const int32_t Lm = cu[m + 1] - cu[m];
+    rank += (Lm > Ln || (Lm == Ln && m < n)) ? 1 : 0;
+  }
+  order[rank] = n;
+}
+
 // ---------------------------------------------------------------------------
 // Prep: normalised k and q (times scale) in fp32, written head-major and
 // interleaved: qk[hq][t][0][:] = k-hat, qk[hq][t][1][:] = q-hat.  A chunk's
@@ -344,6 +358,7 @@ struct ScanIO {
   int N, H_qk, H_v;
   int64_t T;
   int64_t max_state_slot, max_full_slot;
+  const int32_t* order;  // nullable: sequences longest first (d = 128 scan)
 };
 
 template <int D, int C, int TILE, int MODE>
@@ -507,12 +522,15 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
   __shared__ float sLam[C];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t vb = xcd_block(nb8);
+  // ordered launches keep the dispatch order (consecutive blocks go to
+  // consecutive XCDs), so the longest sequences start first on every XCD
+  const int64_t vb = io.order ? static_cast<int64_t>(blockIdx.x) : xcd_block(nb8);
   if (vb >= nblocks) return;
   const int half = static_cast<int>(vb % 2);
   const int h = static_cast<int>((vb / 2) % io.H_v);
-  const int n = static_cast<int>(vb / (2 * io.H_v));
+  int n = static_cast<int>(vb / (2 * io.H_v));
   if (n >= io.N) return;
+  if (io.order) n = io.order[n];  // longest sequences first: their chains start earliest
   const int hq = h / (io.H_v / io.H_qk);
   const int j = 64 * half + 16 * w + l16;  // this lane's column of d_v
   const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
@@ -3045,6 +3063,20 @@ void launch_scan(const ScanIO& io, int64_t N, int H_v, hipStream_t st) {
   }
 }
 
+// Longest-first order of the chunk scan's sequences when its blocks need
+// several rounds of the GPU (more than two per CU): the longest chains then
+// start first.  The scan of each (sequence, head) is the same either way.
+const int32_t* scan_order(const int32_t* cu, int32_t N, int H_v, const gdn::Layout& L, char* ws,
+                          hipStream_t st) {
+  if (N < 2 || L.order == 0 || static_cast<int64_t>(N) * H_v * 2 <= 2 * kPersistentBlocks)
+    return nullptr;
+  int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
+  Timed t_("k_plan", st);
+  hipLaunchKernelGGL(k_order, dim3(static_cast<unsigned>((N + 255) / 256)), dim3(256), 0, st, cu, N,
+                     order);
+  return order;
+}
+
 template <int D, int C, typename TIn>
 int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const gdn::Layout& L,
                    const int32_t* cu, const void* q, const void* k, const void* v,
@@ -3086,6 +3118,7 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     if (cache) { io.S_run = cache->S_run; io.S_chunk = cache->S_chunk; io.pos = cache->pos; }
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
     io.max_state_slot = L.state_slots; io.max_full_slot = L.full_slots;
+    io.order = scan_order(cu, N, s->H_v, L, ws, st);
     if (N > 0) {
       Timed t_("k_scan", st);
       launch_scan<D, C, kFull>(io, N, s->H_v, st);
@@ -3230,6 +3263,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     io.cu_full = cu_full; io.h0 = h0; io.states = states; io.hT = hT; io.Dl = Dl;
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
     io.max_state_slot = L.state_slots; io.max_full_slot = L.state_slots;
+    io.order = scan_order(cu, N, s->H_v, L, ws, st);
     Timed t_("k_scan", st);
     launch_scan<D, C, kAll>(io, N, s->H_v, st);
   }
@@ -3352,6 +3386,7 @@ int launch_prefill_chunked(const gdn_shape_t* s, int32_t N, const gdn::Counts& c
       io.Dl = Dl;
       io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
       io.max_state_slot = L.state_slots; io.max_full_slot = L.state_slots;
+      io.order = scan_order(cu, N, s->H_v, L, ws, st);
       Timed t_("k_scan", st);
       launch_scan<D, C, kAll>(io, N, s->H_v, st);
     }

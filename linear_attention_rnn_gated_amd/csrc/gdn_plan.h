@@ -38,6 +38,7 @@ struct Layout {
   size_t U = 0;          // f32 [full_slots, H_v, C, d]
   size_t G = 0;          // f32 [full_slots, H_v, C]
   size_t states = 0;     // f32 [state_slots, H_v, d, d]  chunk-start states
+  size_t order = 0;      // int32 [N]  sequences longest first (chunk scan)
   // trainer forward + backward only (W, U, G then use chunk slots)
   size_t Dl = 0;         // f32 [state_slots, H_v, C, d]  Delta = U - W S^T
   size_t E = 0;          // f32 [state_slots, H_v, C, d]  P^T dO
