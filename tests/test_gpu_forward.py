@@ -490,3 +490,47 @@ def test_decode_then_continue_equals_one_prefill():
         starts = [s + 1 for s in starts]
     assert bit_equal(cache.S_run, h_full)
     _check_cache_equal(cache, c_full, C)
+
+
+# ------------------------------------------------------------------ batch sizes
+
+def test_prefill_b4_t2048_batch_sizes_1_2_4():
+    """The B4 T2048 prefill (16 q/k / 32 v heads, d128) run as one batch of 4,
+    two batches of 2 and four batches of 1: every sequence's outputs and final
+    state are the same bits."""
+    say("case: prefill B4 T2048 as batches of 4 / 2 / 1")
+    inp = make_inputs([2048] * 4, 16, 32, 128, "bf16", seed=1, h0="normal")
+    o4, h4, _ = run_prefill(inp)
+    cu = inp["cu_seqlens"].tolist()
+    for group in ([0, 1], [2, 3], [0], [1], [2], [3]):
+        o, h, _ = run_prefill(sub_inputs(inp, group))
+        off = 0
+        for j, n in enumerate(group):
+            L = cu[n + 1] - cu[n]
+            assert bit_equal(o[off:off + L], o4[cu[n]:cu[n + 1]]), f"o seq {n} in {group}"
+            assert bit_equal(h[j], h4[n]), f"hT seq {n} in {group}"
+            off += L
+
+
+def test_decode_batches_64_32_1():
+    """Decode of 64 sequences (prefill 130 + 70 steps, crossing chunk edges),
+    and of 32 of them and of one alone: per-sequence outputs and states equal
+    bit for bit."""
+    n_all, pre, steps = 64, 130, 70
+    say(f"case: decode batches 64 / 32 / 1, prefill {pre} + {steps} steps")
+    inp = make_inputs([pre + steps] * n_all, 2, 4, 128, "bf16", seed=45, h0="normal")
+    shape = shape_for(inp)
+
+    def run(seqs):
+        sub = sub_inputs(inp, seqs)
+        first, _ = _token_range(sub, [0] * len(seqs), [pre] * len(seqs))
+        _, _, cache = run_prefill(first, cache=True)
+        return decode_tokens(sub, cache, shape, pre, steps), cache
+
+    o_all, c_all = run(list(range(n_all)))
+    for seqs in (list(range(0, n_all, 2)), [37]):
+        o, c = run(seqs)
+        for j, n in enumerate(seqs):
+            assert bit_equal(o[:, j], o_all[:, n]), f"o seq {n}"
+            assert bit_equal(c.S_run[j], c_all.S_run[n]), f"S_run seq {n}"
+            assert bit_equal(c.S_chunk[j], c_all.S_chunk[n]), f"S_chunk seq {n}"
