@@ -412,7 +412,7 @@ def cpu_baseline(inp):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               "the layer shards by sequence/head without communication, see the design notes",
               file=sys.stderr)
         sys.exit(2)

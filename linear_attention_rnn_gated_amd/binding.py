@@ -49,7 +49,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+            raise RuntimeError(f"{LIB_PATH} is not built; run linear_attention_rnn_gated_amd/build.py "
                                "(the GPU path has no fallback)")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -140,7 +140,7 @@ def contract_id():
 
 
 def contract_check(other_id):
-    """GDN_OK (0) if another build's contract id equals this build's."""
+    """GDN_OK (0) if another library's contract id equals this library's."""
     return lib().gdn_contract_check(other_id.encode())
 
 

@@ -14,7 +14,7 @@ namespace gdn {
 constexpr float kNormEps = 1e-6f;  // inside the L2 norm: x / sqrt(sum x^2 + eps)
 constexpr size_t kAlign = 256;     // every workspace region starts on 256 bytes
 
-// Shapes this build is compiled for (the "claims"): d_k == d_v == d, chunk C.
+// Shapes the library is compiled for (the "claims"): d_k == d_v == d, chunk C.
 struct Claim {
   int d, C;
 };
