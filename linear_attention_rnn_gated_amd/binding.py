@@ -196,10 +196,23 @@ def gdn_cache_init(shape, n, device, in_dtype, h0=None):
     return c
 
 
+def _cu_pair(cu_seqlens, dev, cu_seqlens_host):
+    """Device and host int32 copies of cu_seqlens.  A caller that keeps a host
+    copy (cu_seqlens_host, CPU int32 [N+1], same values) saves the
+    device-to-host copy, which waits for the stream, on every call."""
+    cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    if cu_seqlens_host is None:
+        return cu_dev, cu_seqlens.to("cpu", torch.int32).contiguous()
+    if (cu_seqlens_host.device.type != "cpu" or cu_seqlens_host.dtype != torch.int32
+            or cu_seqlens_host.numel() != cu_seqlens.numel()):
+        raise ValueError("cu_seqlens_host: expected a CPU int32 tensor shaped like cu_seqlens")
+    return cu_dev, cu_seqlens_host.contiguous()
+
+
 def gdn_prefill(shape, q, k, v, beta, g, cu_seqlens, h0=None, cache=None, want_hT=True,
-                ws=None, out=None):
-    """Packed prefill.  cu_seqlens: int32 device tensor [N+1] (a host copy is
-    taken here).  Returns (o, hT)."""
+                ws=None, out=None, cu_seqlens_host=None):
+    """Packed prefill.  cu_seqlens: int32 device tensor [N+1]; its host copy is
+    taken here unless cu_seqlens_host is given.  Returns (o, hT)."""
     dev = q.device
     T = q.shape[0]
     n = cu_seqlens.numel() - 1
@@ -212,8 +225,7 @@ def gdn_prefill(shape, q, k, v, beta, g, cu_seqlens, h0=None, cache=None, want_h
     _req(g, torch.float32, (T, Hv), "g")
     if h0 is not None:
         _req(h0, torch.float32, (n, Hv, d, d), "h0")
-    cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
-    cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    cu_dev, cu_host = _cu_pair(cu_seqlens, dev, cu_seqlens_host)
     o = torch.empty(T, Hv, d, dtype=torch.float32, device=dev) if out is None else out
     hT = torch.empty(n, Hv, d, d, dtype=torch.float32, device=dev) if want_hT else None
     ws = _workspace(shape, n, T, OP_PREFILL, dev, ws)
@@ -228,7 +240,7 @@ def gdn_prefill(shape, q, k, v, beta, g, cu_seqlens, h0=None, cache=None, want_h
 
 
 def gdn_prefill_continue(shape, q, k, v, beta, g, cu_seqlens, cache, pos_host, want_hT=True,
-                         ws=None, out=None):
+                         ws=None, out=None, cu_seqlens_host=None):
     """Next tokens of sequences whose cache stands anywhere inside a chunk.
     pos_host: each sequence's position in its current chunk (host int32 [N],
     the value of cache.pos).  Returns (o, hT) of the new tokens."""
@@ -242,8 +254,7 @@ def gdn_prefill_continue(shape, q, k, v, beta, g, cu_seqlens, cache, pos_host, w
     _req(v, idt, (T, Hv, d), "v")
     _req(beta, torch.float32, (T, Hv), "beta")
     _req(g, torch.float32, (T, Hv), "g")
-    cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
-    cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    cu_dev, cu_host = _cu_pair(cu_seqlens, dev, cu_seqlens_host)
     pos = torch.as_tensor(pos_host, dtype=torch.int32).to("cpu").contiguous()
     if pos.numel() != n:
         raise ValueError(f"pos_host: expected {n} values, got {pos.numel()}")
@@ -261,7 +272,7 @@ def gdn_prefill_continue(shape, q, k, v, beta, g, cu_seqlens, cache, pos_host, w
 
 
 def gdn_prefill_chunked(shape, q, k, v, beta, g, cu_seqlens, h0=None, want_hT=True, ws=None,
-                        out=None):
+                        out=None, cu_seqlens_host=None):
     """Native-mixed baseline prefill (chunk-form outputs; not bit-identical to
     gdn_prefill / decode).  Returns (o, hT)."""
     dev = q.device
@@ -276,8 +287,7 @@ def gdn_prefill_chunked(shape, q, k, v, beta, g, cu_seqlens, h0=None, want_hT=Tr
     _req(g, torch.float32, (T, Hv), "g")
     if h0 is not None:
         _req(h0, torch.float32, (n, Hv, d, d), "h0")
-    cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
-    cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    cu_dev, cu_host = _cu_pair(cu_seqlens, dev, cu_seqlens_host)
     o = torch.empty(T, Hv, d, dtype=torch.float32, device=dev) if out is None else out
     hT = torch.empty(n, Hv, d, d, dtype=torch.float32, device=dev) if want_hT else None
     ws = _workspace(shape, n, T, OP_PREFILL_CHUNKED, dev, ws)
@@ -315,7 +325,7 @@ def gdn_decode_step(shape, q, k, v, beta, g, cache, pos_host=None, ws=None, out=
 
 
 def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=None,
-                grad_dtype=torch.float32):
+                grad_dtype=torch.float32, cu_seqlens_host=None):
     """Trainer forward + backward.  Returns dict(o, hT, dq, dk, dv, dbeta, dg, dh0);
     dq, dk, dv in grad_dtype (float32 or bfloat16), the rest float32."""
     dev = q.device
@@ -333,8 +343,7 @@ def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=N
         _req(h0, torch.float32, (n, Hv, d, d), "h0")
     if dhT is not None:
         _req(dhT, torch.float32, (n, Hv, d, d), "dhT")
-    cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
-    cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    cu_dev, cu_host = _cu_pair(cu_seqlens, dev, cu_seqlens_host)
     f32 = dict(dtype=torch.float32, device=dev)
     gd = dict(dtype=grad_dtype, device=dev)
     code = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}[grad_dtype]

@@ -966,18 +966,34 @@ __device__ __forceinline__ void load_block(OpBlock& x, cfloat_p kq, cfloat_p kn,
 // barrier stops the compiler from hoisting more scalar loads than the SGPR
 // file holds.  Neither changes any operation or its order.  (Prefetching a
 // block ahead measured slower: scalar loads complete out of order, so every
-// wait is an all-outstanding wait.)
+// wait is an all-outstanding wait.)  After each block's wait the pass
+// touches the next token's query line and the key line two tokens ahead
+// (p0, p1; folded into `sink` one block later, so the next block's wait
+// retires them): the following tokens' operand loads then hit the scalar
+// cache.  The reads stay inside the prep buffer's two spare token rows.
 template <int DK, int D>  // DK: elements of the row this lane holds; D: head dimension
 __device__ __forceinline__ void r_token_pass(float (&s)[DK], cfloat_p kq, cfloat_p kn, float alpha,
-                                             float delta, float& o, float& an) {
+                                             float delta, float& o, float& an, uint32_t& p0,
+                                             uint32_t& p1, uint32_t& sink) {
   constexpr int NB = DK / RB;
   static_assert(DK % RB == 0, "row part must be whole operand blocks");
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     OpBlock x;
     load_block<D>(x, kq, kn, b);
+    {
+      const int i = b * RB;
+      s[i] = fmaf(delta, x.k[0], alpha * s[i]);
+      o = fmaf(s[i], x.q[0], o);
+      an = fmaf(s[i], x.n[0], an);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sink ^= p0 ^ p1;
+    p0 = __float_as_uint(kq[2 * D + D + b * RB]);
+    p1 = __float_as_uint(kq[4 * D + b * RB]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
+    for (int r = 1; r < RB; ++r) {
       const int i = b * RB + r;
       s[i] = fmaf(delta, x.k[r], alpha * s[i]);
       o = fmaf(s[i], x.q[r], o);
@@ -1100,6 +1116,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   }
   // g, beta and v are loaded one token ahead; the last token reloads itself
   // rather than reading past the chunk
+  uint32_t pp0 = 0, pp1 = 0, psink = 0;
   float gn = gt[0], bn = bt[0], vn = ldin(&sv[wp][0][lane]);
   for (int t = 0; t < L; ++t) {
     const float alpha = expf(gn);
@@ -1113,7 +1130,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     const float delta = b * (vj - u);
     cfloat_p kn = kq + 2 * D;  // past the chunk's end on its last token: read, never used
     float o = 0.0f, an = 0.0f;
-    r_token_pass<DK, D>(s, kq, kn, alpha, delta, o, an);
+    r_token_pass<DK, D>(s, kq, kn, alpha, delta, o, an, pp0, pp1, psink);
     if constexpr (KS == 2) {
       const int par = t & 1;  // a slot is rewritten two barriers after it was read
       xa[par][wl][lane] = an;
@@ -1129,6 +1146,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     // the next token's k loads and must keep the values live across iterations
     asm volatile("" : "+s"(kq));
   }
+  asm volatile("" :: "s"(psink ^ pp0 ^ pp1));
   if (L == C) return;
   // tail chunk: the running state is the sequence's final state, and the
   // partial chunk's tokens go to the decode buffers

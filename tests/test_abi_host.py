@@ -207,3 +207,17 @@ def test_fwd_bwd_ex_grad_dtype_check():
                        a, a, a, None, 0, None)
     assert L.gdn_fwd_bwd_ex(*args(7)) == B.GDN_ERR_INVALID_ARG
     assert L.gdn_fwd_bwd_ex(*args(B.GDN_BF16)) == B.GDN_ERR_WORKSPACE
+
+
+def test_host_copy_of_cu_seqlens_checked():
+    """The binding takes a caller's host copy of cu_seqlens only as CPU int32
+    of the same length."""
+    import torch
+    cu = torch.tensor([0, 5, 9], dtype=torch.int32)
+    dev, host = B._cu_pair(cu, "cpu", None)
+    assert host.tolist() == [0, 5, 9] and dev.dtype == torch.int32
+    _, host = B._cu_pair(cu, "cpu", cu.clone())
+    assert host.tolist() == [0, 5, 9]
+    for bad in (cu.to(torch.int64), cu[:2].clone()):
+        with pytest.raises(ValueError):
+            B._cu_pair(cu, "cpu", bad)

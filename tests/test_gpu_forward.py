@@ -534,3 +534,27 @@ def test_decode_batches_64_32_1():
             assert bit_equal(o[:, j], o_all[:, n]), f"o seq {n}"
             assert bit_equal(c.S_run[j], c_all.S_run[n]), f"S_run seq {n}"
             assert bit_equal(c.S_chunk[j], c_all.S_chunk[n]), f"S_chunk seq {n}"
+
+
+# ------------------------------------------------------------------ host copy
+
+def test_host_copy_of_cu_seqlens_same_bits():
+    """Passing the host copy of cu_seqlens (no device-to-host copy per call)
+    changes nothing: prefill and trainer outputs are the same bits."""
+    say("case: cu_seqlens_host given / not given, ragged d128 bf16")
+    inp = make_inputs([200, 64, 1, 130], 2, 4, 128, "bf16", seed=61, h0="normal")
+    shape = shape_for(inp)
+    d = to_dev(inp, "cuda")
+    cu_h = inp["cu_seqlens"].to("cpu", torch.int32)
+    o1, h1 = B.gdn_prefill(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"],
+                           h0=d["h0"])
+    o2, h2 = B.gdn_prefill(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"],
+                           h0=d["h0"], cu_seqlens_host=cu_h)
+    assert bit_equal(o1, o2) and bit_equal(h1, h2)
+    dO = torch.randn(inp["T"], 4, 128, generator=torch.Generator().manual_seed(62)).cuda()
+    r1 = B.gdn_fwd_bwd(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], dO,
+                       h0=d["h0"])
+    r2 = B.gdn_fwd_bwd(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], dO,
+                       h0=d["h0"], cu_seqlens_host=cu_h)
+    for key in r1:
+        assert bit_equal(r1[key], r2[key]), key
