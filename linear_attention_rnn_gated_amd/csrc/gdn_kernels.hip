@@ -509,16 +509,16 @@ __device__ __forceinline__ int64_t xcd_block(int64_t nb8) {
 // registers: Delta (k = i) from the state, S' (k = p) from lam * Delta.
 // Summation orders: Delta starts from U and adds the k-steps (ib = 0..7,
 // r = 0..3); S' starts from gam_C S and adds the k-steps (pb = 0..3,
-// r = 0..3).  W (rows p) and K^T (rows i) of a chunk sit in LDS; the next
+// r = 0..3).  W and K (rows p) of a chunk sit in LDS; the next
 // chunk's W, K, U and G are fetched into registers while the current chunk
 // computes.  Decode resync runs this same kernel on the chunk buffers.
 template <int C, int MODE>
 __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, int64_t nb8) {
-  constexpr int D = 128, WS = D + 4, TS = C + 4, NQ = C * D / 4 / 256;  // float4 per thread
+  constexpr int D = 128, WS = D + 4, NQ = C * D / 4 / 256;  // float4 per thread
   static_assert(C == 64 && NQ == 8, "tiling assumes C = 64, D = 128");
   constexpr bool RESYNC = MODE == kResync;
-  __shared__ __attribute__((aligned(16))) float sW[C * WS];   // W[p][i]
-  __shared__ __attribute__((aligned(16))) float sKT[D * TS];  // K[p][i] at [i][p]
+  __shared__ __attribute__((aligned(16))) float sW[C * WS];  // W[p][i]
+  __shared__ __attribute__((aligned(16))) float sK[C * WS];  // K[p][i]
   __shared__ float sLam[C];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -611,16 +611,13 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
   for (int64_t c = 0; c < nsteps; ++c) {
     const int64_t fs = fslot0 + c;
     __syncthreads();  // the previous step's LDS reads are done
+    // W and K go to LDS as loaded (no register transpose: a transpose of the
+    // prefetched quads would make the loads complete before this chunk computes)
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) *reinterpret_cast<float4*>(sW + (r0 + m) * WS + 4 * cq) = nx.w[m];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {  // K^T: four consecutive rows p per 16-byte store
-      const float4* k4 = nx.k + 4 * hh;
-      float* dst = sKT + (4 * cq) * TS + r0 + 4 * hh;
-      *reinterpret_cast<float4*>(dst) = float4{k4[0].x, k4[1].x, k4[2].x, k4[3].x};
-      *reinterpret_cast<float4*>(dst + TS) = float4{k4[0].y, k4[1].y, k4[2].y, k4[3].y};
-      *reinterpret_cast<float4*>(dst + 2 * TS) = float4{k4[0].z, k4[1].z, k4[2].z, k4[3].z};
-      *reinterpret_cast<float4*>(dst + 3 * TS) = float4{k4[0].w, k4[1].w, k4[2].w, k4[3].w};
+    for (int m = 0; m < NQ; ++m) {
+      const float4 wv = nx.w[m];  // stored negated: Delta adds (-W) S^T
+      *reinterpret_cast<float4*>(sW + (r0 + m) * WS + 4 * cq) = float4{-wv.x, -wv.y, -wv.z, -wv.w};
+      *reinterpret_cast<float4*>(sK + (r0 + m) * WS + 4 * cq) = nx.k[m];
     }
     const float glast = nx.glast;
     if (tid < C) sLam[tid] = expf(glast - nx.gv);
@@ -639,21 +636,28 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
     for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) dl[pb][r] = u[pb][r];
-#pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      float4 a[4];
+    // A operands (-W) are read from LDS one k block ahead of their use
+    float4 a[2][4];
+    auto read_w = [&](float4 (&x)[4], int ib) {
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb)
-        a[pb] = *reinterpret_cast<const float4*>(sW + (16 * pb + l16) * WS + 16 * ib + 4 * g);
+        x[pb] = *reinterpret_cast<const float4*>(sW + (16 * pb + l16) * WS + 16 * ib + 4 * g);
+    };
+    read_w(a[0], 0);
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(-a[pb].x, st[ib][0], dl[pb]);
+    for (int ib = 0; ib < 8; ++ib) {
+      const float4(&x)[4] = a[ib & 1];
+      if (ib + 1 < 8) read_w(a[(ib + 1) & 1], ib + 1);
+      __builtin_amdgcn_sched_barrier(0);  // the reads issue before this block's products
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(-a[pb].y, st[ib][1], dl[pb]);
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].x, st[ib][0], dl[pb]);
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(-a[pb].z, st[ib][2], dl[pb]);
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].y, st[ib][1], dl[pb]);
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(-a[pb].w, st[ib][3], dl[pb]);
-      __builtin_amdgcn_sched_barrier(0);  // keep operand reads per k block
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].z, st[ib][2], dl[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].w, st[ib][3], dl[pb]);
+      __builtin_amdgcn_sched_barrier(0);  // at most one k block of reads in flight
     }
     if (MODE == kAll) {
       const brsrc_t rd = make_rsrc(io.Dl + (fs * io.H_v + h) * CD, C * D * 4u);
@@ -670,22 +674,28 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
     const float gam = expf(glast);
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib) st[ib] = gam * st[ib];
+    // A operand K^T (i = 16 (4 h2 + q) + l16, p = 16 pb + 4 g + r), a column
+    // of K, read from LDS one group of four tiles ahead of its use
+    float ak[2][4][4];
+    auto read_k = [&](float (&x)[4][4], int pb, int h2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[q][r] = sK[(16 * pb + 4 * g + r) * WS + 16 * (4 * h2 + q) + l16];
+    };
+    read_k(ak[0], 0, 0);
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {  // two groups of four tiles
-        float4 a[4];
+        const int it = 2 * pb + h2;
+        const float(&x)[4][4] = ak[it & 1];
+        if (it + 1 < 8) read_k(ak[(it + 1) & 1], (it + 1) / 2, (it + 1) % 2);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          a[q] = *reinterpret_cast<const float4*>(sKT + (16 * (4 * h2 + q) + l16) * TS + 16 * pb + 4 * g);
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].x, dl[pb][0], st[4 * h2 + q]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].y, dl[pb][1], st[4 * h2 + q]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].z, dl[pb][2], st[4 * h2 + q]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].w, dl[pb][3], st[4 * h2 + q]);
+          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(x[q][r], dl[pb][r], st[4 * h2 + q]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -822,34 +832,46 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
   }
   __syncthreads();
   if (tid < C) sBG[tid] = sB[tid] * expf(sG[tid]);
-  // Gram rows p = 16 w + 4 g + r, columns r' = 16 cb + l16 (lower blocks only)
+  // Gram tiles (row block rb, column block cb <= rb): rows p = 16 rb + 4 g + r,
+  // columns r' = 16 cb + l16.  The ten lower tiles are spread 3/3/2/2 over the
+  // waves; each tile's k-steps run in the same order whichever wave owns it.
+  // Tiles above the diagonal block are never read.
   {
-    v4f kk[4];
+    constexpr int kTiles = 3;
+    int trb[kTiles], tcb[kTiles];
+    const int nt = w < 2 ? 3 : 2;
+    if (w == 0) { trb[0] = 0; tcb[0] = 0; trb[1] = 3; tcb[1] = 3; trb[2] = 3; tcb[2] = 0; }
+    else if (w == 1) { trb[0] = 1; tcb[0] = 1; trb[1] = 2; tcb[1] = 2; trb[2] = 3; tcb[2] = 1; }
+    else if (w == 2) { trb[0] = 1; tcb[0] = 0; trb[1] = 3; tcb[1] = 2; trb[2] = 0; tcb[2] = 0; }
+    else { trb[0] = 2; tcb[0] = 0; trb[1] = 2; tcb[1] = 1; trb[2] = 0; tcb[2] = 0; }
+    v4f kk[kTiles];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) kk[cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < kTiles; ++t) kk[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s4 = 0; s4 < 8; ++s4) {
-      const float4 a4 = *reinterpret_cast<const float4*>(sK + (16 * w + l16) * KS + 32 * g + 4 * s4);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if (cb > w) continue;
-        const float4 b4 = *reinterpret_cast<const float4*>(sK + (16 * cb + l16) * KS + 32 * g + 4 * s4);
-        kk[cb] = mfma4(a4.x, b4.x, kk[cb]);
-        kk[cb] = mfma4(a4.y, b4.y, kk[cb]);
-        kk[cb] = mfma4(a4.z, b4.z, kk[cb]);
-        kk[cb] = mfma4(a4.w, b4.w, kk[cb]);
+      for (int t = 0; t < kTiles; ++t) {
+        if (t >= nt) continue;
+        const float4 a4 = *reinterpret_cast<const float4*>(sK + (16 * trb[t] + l16) * KS + 32 * g + 4 * s4);
+        const float4 b4 = *reinterpret_cast<const float4*>(sK + (16 * tcb[t] + l16) * KS + 32 * g + 4 * s4);
+        kk[t] = mfma4(a4.x, b4.x, kk[t]);
+        kk[t] = mfma4(a4.y, b4.y, kk[t]);
+        kk[t] = mfma4(a4.z, b4.z, kk[t]);
+        kk[t] = mfma4(a4.w, b4.w, kk[t]);
       }
     }
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int t = 0; t < kTiles; ++t) {
+      if (t >= nt) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = 16 * w + 4 * g + r, q = 16 * cb + l16;
+        const int p = 16 * trb[t] + 4 * g + r, q = 16 * tcb[t] + l16;
         // operands read and exp taken unconditionally: a select, not a branch
         const float gpq = expf(sG[p] - sG[q]);
-        const float a = sB[p] * (kk[cb][r] * gpq);
-        sA[p * AS + q] = (cb <= w && q < p) ? a : 0.0f;
+        const float a = sB[p] * (kk[t][r] * gpq);
+        sA[p * AS + q] = q < p ? a : 0.0f;
       }
+    }
   }
   __syncthreads();
   float* out = (isW ? io.W : io.U) + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
@@ -2150,16 +2172,16 @@ __global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
 // group g is the B operand of the k-step that lane group g supplies as
 // k = 16 ib + 4 g + r, so dDelta (k = i) takes the state straight from
 // registers, and the update (k = p) takes dDelta and gam dO, held the same way,
-// straight from registers too.  Per chunk, K (rows p), Q^T and W^T (rows i)
-// sit in LDS and the next chunk's copies are fetched into registers while the
-// current one computes.
+// straight from registers too.  Per chunk, K, Q and W (rows p) sit in LDS
+// and the next chunk's copies are fetched into registers while the current
+// one computes.
 template <int C>
 __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
-  constexpr int D = 128, KS = D + 4, TS = C + 4, NQ = C * D / 4 / 512;  // float4 per thread
+  constexpr int D = 128, KS = D + 4, NQ = C * D / 4 / 512;  // float4 per thread
   static_assert(C == 64 && NQ == 4, "tiling assumes C = 64, D = 128");
-  __shared__ __attribute__((aligned(16))) float sK[C * KS];   // K[p][i]
-  __shared__ __attribute__((aligned(16))) float sQT[D * TS];  // Q[p][i] at [i][p]
-  __shared__ __attribute__((aligned(16))) float sWT[D * TS];  // W[p][i] at [i][p]
+  __shared__ __attribute__((aligned(16))) float sK[C * KS];  // K[p][i]
+  __shared__ __attribute__((aligned(16))) float sQ[C * KS];  // Q[p][i]
+  __shared__ __attribute__((aligned(16))) float sW[C * KS];  // W[p][i]
   __shared__ float sGam[C], sLam[C];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2241,21 +2263,14 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     const int64_t sh = (slot0 + c) * io.H_v + h;
     const int rows = rows_of(c);
     __syncthreads();  // the previous chunk's LDS reads are done
+    // K, Q and W go to LDS as loaded (no register transpose: a transpose of the
+    // prefetched quads would make the loads complete before this chunk computes)
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) *reinterpret_cast<float4*>(sK + (r0 + m) * KS + 4 * cq) = nx.k[m];
-    {  // Q^T, W^T: four consecutive rows p per 16-byte store
-      const float4* q4 = nx.q;
-      const float4* w4 = nx.wv;
-      float* dq = sQT + (4 * cq) * TS + r0;
-      float* dw = sWT + (4 * cq) * TS + r0;
-      *reinterpret_cast<float4*>(dq) = float4{q4[0].x, q4[1].x, q4[2].x, q4[3].x};
-      *reinterpret_cast<float4*>(dq + TS) = float4{q4[0].y, q4[1].y, q4[2].y, q4[3].y};
-      *reinterpret_cast<float4*>(dq + 2 * TS) = float4{q4[0].z, q4[1].z, q4[2].z, q4[3].z};
-      *reinterpret_cast<float4*>(dq + 3 * TS) = float4{q4[0].w, q4[1].w, q4[2].w, q4[3].w};
-      *reinterpret_cast<float4*>(dw) = float4{w4[0].x, w4[1].x, w4[2].x, w4[3].x};
-      *reinterpret_cast<float4*>(dw + TS) = float4{w4[0].y, w4[1].y, w4[2].y, w4[3].y};
-      *reinterpret_cast<float4*>(dw + 2 * TS) = float4{w4[0].z, w4[1].z, w4[2].z, w4[3].z};
-      *reinterpret_cast<float4*>(dw + 3 * TS) = float4{w4[0].w, w4[1].w, w4[2].w, w4[3].w};
+    for (int m = 0; m < NQ; ++m) {
+      *reinterpret_cast<float4*>(sK + (r0 + m) * KS + 4 * cq) = nx.k[m];
+      *reinterpret_cast<float4*>(sQ + (r0 + m) * KS + 4 * cq) = nx.q[m];
+      const float4 wv = nx.wv[m];  // stored negated: the update adds (-W^T) dDelta
+      *reinterpret_cast<float4*>(sW + (r0 + m) * KS + 4 * cq) = float4{-wv.x, -wv.y, -wv.z, -wv.w};
     }
     const float gcur = nx.gv, glast = nx.glast;
     float ec[4][4], dc[4][4];  // land while dDelta is computed
@@ -2276,21 +2291,28 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     v4f dd[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) dd[pb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      float4 a[4];
+    // A operands (K) are read from LDS one k block ahead of their use
+    float4 a[2][4];
+    auto read_k = [&](float4 (&x)[4], int ib) {
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb)
-        a[pb] = *reinterpret_cast<const float4*>(sK + (16 * pb + l16) * KS + 16 * ib + 4 * g);
+        x[pb] = *reinterpret_cast<const float4*>(sK + (16 * pb + l16) * KS + 16 * ib + 4 * g);
+    };
+    read_k(a[0], 0);
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(a[pb].x, st[ib][0], dd[pb]);
+    for (int ib = 0; ib < 8; ++ib) {
+      const float4(&x)[4] = a[ib & 1];
+      if (ib + 1 < 8) read_k(a[(ib + 1) & 1], ib + 1);
+      __builtin_amdgcn_sched_barrier(0);  // the reads issue before this block's products
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(a[pb].y, st[ib][1], dd[pb]);
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].x, st[ib][0], dd[pb]);
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(a[pb].z, st[ib][2], dd[pb]);
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].y, st[ib][1], dd[pb]);
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(a[pb].w, st[ib][3], dd[pb]);
-      __builtin_amdgcn_sched_barrier(0);  // keep operand reads per k block
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].z, st[ib][2], dd[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].w, st[ib][3], dd[pb]);
+      __builtin_amdgcn_sched_barrier(0);  // at most one k block of reads in flight
     }
     const brsrc_t rd = make_rsrc(io.dD + sh * CD, C * D * 4u);
 #pragma unroll
@@ -2312,31 +2334,29 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
       for (int r = 0; r < 4; ++r) dcv[pb][r] = dc[pb][r];
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib) st[ib] = gl * st[ib];
+    // A operand Q^T or -W^T (i = 16 (4 h2 + q) + l16, p = 16 pb + 4 g + r), a
+    // column of Q or -W, read from LDS one group of four tiles ahead of its use
+    float aq[2][4][4];
+    auto read_qw = [&](float (&x)[4][4], int it) {
+      const float* src = (it < 8 ? sQ : sW) + (16 * ((it % 8) / 2) + 4 * g) * KS + 16 * (4 * (it % 2)) + l16;
 #pragma unroll
-    for (int op = 0; op < 2; ++op) {  // Q^T (gam dO), then -W^T dDelta
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
+        for (int r = 0; r < 4; ++r) x[q][r] = src[r * KS + 16 * q];
+    };
+    read_qw(aq[0], 0);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {  // two groups of four tiles, chains interleaved
-          float4 a[4];
+    for (int it = 0; it < 16; ++it) {  // Q^T (gam dO), then -W^T dDelta; (pb, h2) per op
+      const int op = it / 8, pb = (it % 8) / 2, h2 = it % 2;
+      const float(&x)[4][4] = aq[it & 1];
+      if (it + 1 < 16) read_qw(aq[(it + 1) & 1], it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const v4f bv = op == 0 ? dcv[pb] : dd[pb];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float* src = (op == 0 ? sQT : sWT) + (16 * (4 * h2 + q) + l16) * TS + 16 * pb + 4 * g;
-            const float4 x = *reinterpret_cast<const float4*>(src);
-            a[q] = op == 0 ? x : float4{-x.x, -x.y, -x.z, -x.w};
-          }
-          const v4f bv = op == 0 ? dcv[pb] : dd[pb];
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].x, bv[0], st[4 * h2 + q]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].y, bv[1], st[4 * h2 + q]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].z, bv[2], st[4 * h2 + q]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(a[q].w, bv[3], st[4 * h2 + q]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(x[q][r], bv[r], st[4 * h2 + q]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   const brsrc_t rh0 = make_rsrc(io.dh0 + nh * DD, D * D * 4u);
