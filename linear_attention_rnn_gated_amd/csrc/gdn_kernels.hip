@@ -564,27 +564,41 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
     float u[4][4];
     float gv, glast;
   };
-  auto load_ops = [&](Ops& o, int64_t c) {
-    const int64_t fs = fslot0 + c;
-    const int64_t sh = fs * io.H_v + h;
+  // The loads come in NQ parts (part m: W and K rows r0 + m, two of the U
+  // values, and G with part 0) so that they can be issued between the
+  // matrix-core products of a chunk step.
+  struct OpRes {
+    brsrc_t rk, rw, ru;
+    int64_t sh;
+  };
+  auto op_res = [&](int64_t c) {
+    OpRes r;
+    r.sh = (fslot0 + c) * io.H_v + h;
     const int rows = RESYNC ? C : static_cast<int>(L - c * C < C ? L - c * C : C);
     const float* kb = RESYNC ? io.khat + (static_cast<int64_t>(n) * C * io.H_qk + hq) * D
                              : io.khat + (static_cast<int64_t>(hq) * io.T + tok0 + c * C) * 2 * D;
-    const brsrc_t rk = make_rsrc(kb, static_cast<uint32_t>(rows) * kst);  // rows past the end read 0
-    const brsrc_t rw = make_rsrc(io.W + sh * CD, C * D * 4u);
-    const brsrc_t ru = make_rsrc(io.U + sh * CD, C * D * 4u);
+    r.rk = make_rsrc(kb, static_cast<uint32_t>(rows) * kst);  // rows past the end read 0
+    r.rw = make_rsrc(io.W + r.sh * CD, C * D * 4u);
+    r.ru = make_rsrc(io.U + r.sh * CD, C * D * 4u);
+    return r;
+  };
+  auto load_part = [&](Ops& o, const OpRes& rs, int m) {
+    o.w[m] = ldbuf4(rs.rw, fq, static_cast<uint32_t>(m * D * 4));
+    o.k[m] = ldbuf4(rs.rk, fk + static_cast<uint32_t>(m) * kst, 0u);
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-      o.w[m] = ldbuf4(rw, fq, static_cast<uint32_t>(m * D * 4));
-      o.k[m] = ldbuf4(rk, fk + static_cast<uint32_t>(m) * kst, 0u);
+    for (int e = 0; e < 2; ++e) {
+      const int pb = m / 2, r = 2 * (m % 2) + e;
+      o.u[pb][r] = ldbuf(rs.ru, fj, static_cast<uint32_t>((16 * pb + r) * D * 4), static_cast<const float*>(nullptr));
     }
+    if (m == 0) {
+      o.gv = tid < C ? io.G[rs.sh * C + tid] : 0.0f;
+      o.glast = io.G[rs.sh * C + C - 1];
+    }
+  };
+  auto load_ops = [&](Ops& o, int64_t c) {
+    const OpRes rs = op_res(c);
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        o.u[pb][r] = ldbuf(ru, fj, static_cast<uint32_t>((16 * pb + r) * D * 4), static_cast<const float*>(nullptr));
-    o.gv = tid < C ? io.G[sh * C + tid] : 0.0f;
-    o.glast = io.G[sh * C + C - 1];
+    for (int m = 0; m < NQ; ++m) load_part(o, rs, m);
   };
 
   // S^T tiles (i = 16 ib + 4 g + r, j)
@@ -626,8 +640,12 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
     for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) u[pb][r] = nx.u[pb][r];
-    if (c + 1 < nsteps) load_ops(nx, c + 1);  // lands while this step computes
-    if (!RESYNC) store_state(io.states + ((slot0 + c) * io.H_v + h) * DD);  // chunk-start state
+    // the next chunk's operands and this chunk's start state (a store) are
+    // issued between the Delta products below, a part per k block
+    const bool more = c + 1 < nsteps;
+    const OpRes nres = op_res(more ? c + 1 : c);
+    const brsrc_t rst = RESYNC ? make_rsrc(io.W, 0u)  // no chunk-start states in resync
+                               : make_rsrc(io.states + ((slot0 + c) * io.H_v + h) * DD, D * D * 4u);
     __syncthreads();
     // ---- Delta tiles (p = 16 pb + 4 g + r, j) = U - W S^T, k = i
     // (the four tiles' chains are interleaved; each keeps its own k order)
@@ -648,6 +666,11 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
     for (int ib = 0; ib < 8; ++ib) {
       const float4(&x)[4] = a[ib & 1];
       if (ib + 1 < 8) read_w(a[(ib + 1) & 1], ib + 1);
+      if (!RESYNC) {  // rows 16 ib + 4 g + r of the chunk-start state
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rst, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+      }
+      if (more) load_part(nx, nres, ib);
       __builtin_amdgcn_sched_barrier(0);  // the reads issue before this block's products
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].x, st[ib][0], dl[pb]);
@@ -895,9 +918,12 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) acc[ct] = mfma4(a, Y[bj][ct][s4], acc[ct]);
       }
-    // forward substitution inside the block
+    // forward substitution inside the block: row pp (solved) is subtracted
+    // from every row of the block with its coefficient; the coefficients of
+    // rows at or above pp are the zeros of the diagonal tile, so those rows
+    // keep their values (up to the sign of a zero).  Row 15 updates nothing.
 #pragma unroll
-    for (int pp = 0; pp < 16; ++pp) {
+    for (int pp = 0; pp < 15; ++pp) {
       const int gp = pp >> 2, rp = pp & 3;
       float a[4];
 #pragma unroll
@@ -906,10 +932,7 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
       for (int ct = 0; ct < 4; ++ct) {
         const float y = __shfl(acc[ct][rp], l16 + 16 * gp, 64);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float upd = fmaf(-a[r], y, acc[ct][r]);
-          acc[ct][r] = 4 * g + r > pp ? upd : acc[ct][r];
-        }
+        for (int r = 0; r < 4; ++r) acc[ct][r] = fmaf(-a[r], y, acc[ct][r]);
       }
     }
 #pragma unroll
@@ -2213,21 +2236,35 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     float gv, glast;  // G[tid] (tid < C) and G[C - 1]
   };
   auto rows_of = [&](int64_t c) { return static_cast<int>(Lseq - c * C < C ? Lseq - c * C : C); };
-  auto load_ops = [&](Ops& o, int64_t c) {
-    const int64_t sh = (slot0 + c) * io.H_v + h;
+  // The loads come in NQ parts (part m: K, Q and W rows r0 + m, and G with
+  // part 0) so that they can be issued between the matrix-core products.
+  struct OpRes {
+    brsrc_t rq, rw;
+    int64_t sh;
+  };
+  auto op_res = [&](int64_t c) {
+    OpRes r;
+    r.sh = (slot0 + c) * io.H_v + h;
     const int rows = rows_of(c);
-    const brsrc_t rq = make_rsrc(io.qk + (static_cast<int64_t>(hq) * io.T + s0 + c * C) * 2 * D,
-                                 static_cast<uint32_t>(rows) * 2 * D * 4u);
-    const brsrc_t rw = make_rsrc(io.W + sh * CD, C * D * 4u);
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-      const uint32_t mq = fq + static_cast<uint32_t>(m * 2 * D * 4);
-      o.k[m] = ldbuf4(rq, mq, 0u);
-      o.q[m] = ldbuf4(rq, mq + D * 4u, 0u);
-      o.wv[m] = ldbuf4(rw, fw, static_cast<uint32_t>(m * D * 4));  // padded rows of W are 0
+    r.rq = make_rsrc(io.qk + (static_cast<int64_t>(hq) * io.T + s0 + c * C) * 2 * D,
+                     static_cast<uint32_t>(rows) * 2 * D * 4u);
+    r.rw = make_rsrc(io.W + r.sh * CD, C * D * 4u);
+    return r;
+  };
+  auto load_part = [&](Ops& o, const OpRes& rs, int m) {
+    const uint32_t mq = fq + static_cast<uint32_t>(m * 2 * D * 4);
+    o.k[m] = ldbuf4(rs.rq, mq, 0u);
+    o.q[m] = ldbuf4(rs.rq, mq + D * 4u, 0u);
+    o.wv[m] = ldbuf4(rs.rw, fw, static_cast<uint32_t>(m * D * 4));  // padded rows of W are 0
+    if (m == 0) {
+      o.gv = tid < C ? io.G[rs.sh * C + tid] : 0.0f;
+      o.glast = io.G[rs.sh * C + C - 1];
     }
-    o.gv = tid < C ? io.G[sh * C + tid] : 0.0f;
-    o.glast = io.G[sh * C + C - 1];
+  };
+  auto load_ops = [&](Ops& o, int64_t c) {
+    const OpRes rs = op_res(c);
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) load_part(o, rs, m);
   };
   // E and dO of a chunk in accumulator layout: (p = 16 pb + 4 g + r, j)
   auto load_ed = [&](float (&e)[4][4], float (&d)[4][4], int64_t c) {
@@ -2279,13 +2316,11 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
       sLam[tid] = expf(glast - gcur);
       sGam[tid] = expf(gcur);
     }
-    if (c > 0) load_ops(nx, c - 1);  // the next chunk's operands land while this one computes
-    // this chunk's incoming state gradient
+    // the next chunk's operands and this chunk's incoming state gradient (a
+    // store) are issued between the dDelta products below, a part per k block
+    const bool more = c > 0;
+    const OpRes nres = op_res(more ? c - 1 : c);
     const brsrc_t rs = make_rsrc(io.dstates + sh * DD, D * D * 4u);
-#pragma unroll
-    for (int ib = 0; ib < 8; ++ib)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rs, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
     __syncthreads();  // sGam, sLam ready
     // dDelta tiles (p = 16 pb + 4 g + r, j): k = i from the state registers
     v4f dd[4];
@@ -2303,6 +2338,9 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     for (int ib = 0; ib < 8; ++ib) {
       const float4(&x)[4] = a[ib & 1];
       if (ib + 1 < 8) read_k(a[(ib + 1) & 1], ib + 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rs, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+      if (more && ib < NQ) load_part(nx, nres, ib);
       __builtin_amdgcn_sched_barrier(0);  // the reads issue before this block's products
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].x, st[ib][0], dd[pb]);
