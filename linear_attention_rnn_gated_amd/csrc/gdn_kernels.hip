@@ -836,16 +836,22 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
   __syncthreads();
   // values of this wave's U columns: (row 16 bi + 4 g + r, column cbase + 16 ct + l16)
   float vpre[4][4][4];
+  if (isW) {  // wave-uniform: the W waves need no values
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-      {  // read unconditionally (in bounds) and select: no per-element branch
-        const float x = ldin(sV + (16 * bi + 4 * g + r) * D + cbase + 16 * ct + l16);
-        vpre[bi][ct][r] = isW ? 0.0f : x;
-      }
+        for (int r = 0; r < 4; ++r) vpre[bi][ct][r] = 0.0f;
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vpre[bi][ct][r] = ldin(sV + (16 * bi + 4 * g + r) * D + cbase + 16 * ct + l16);
+  }
   if (tid == 0) {  // running sum of g, p ascending
     float acc = 0.0f;
     for (int p = 0; p < C; ++p) {
@@ -922,17 +928,26 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
     // from every row of the block with its coefficient; the coefficients of
     // rows at or above pp are the zeros of the diagonal tile, so those rows
     // keep their values (up to the sign of a zero).  Row 15 updates nothing.
+    // The coefficients of four consecutive pivots are one 16-byte read per row.
 #pragma unroll
-    for (int pp = 0; pp < 15; ++pp) {
-      const int gp = pp >> 2, rp = pp & 3;
-      float a[4];
+    for (int pq = 0; pq < 4; ++pq) {
+      float4 aq[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = sA[(16 * bi + 4 * g + r) * AS + 16 * bi + pp];
+      for (int r = 0; r < 4; ++r)
+        aq[r] = *reinterpret_cast<const float4*>(sA + (16 * bi + 4 * g + r) * AS + 16 * bi + 4 * pq);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const float y = __shfl(acc[ct][rp], l16 + 16 * gp, 64);
+      for (int e = 0; e < 4; ++e) {
+        const int pp = 4 * pq + e;
+        if (pp == 15) continue;
+        float a[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[ct][r] = fmaf(-a[r], y, acc[ct][r]);
+        for (int r = 0; r < 4; ++r) a[r] = e == 0 ? aq[r].x : e == 1 ? aq[r].y : e == 2 ? aq[r].z : aq[r].w;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const float y = __shfl(acc[ct][e], l16 + 16 * pq, 64);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ct][r] = fmaf(-a[r], y, acc[ct][r]);
+        }
       }
     }
 #pragma unroll
