@@ -123,21 +123,32 @@ __device__ __forceinline__ void l2norm_wave(const TIn* __restrict__ x, float mul
 
 // ---------------------------------------------------------------------------
 // Device planner: per-sequence prefix counts of chunks (ceil) and full chunks
-// (floor).  One thread; N is small next to the token count.
+// (floor).  One thread; N is small next to the token count.  It runs in the
+// first thread of the prep kernel (one launch fewer on the path), or alone in
+// k_plan when there is nothing to normalise.
+struct PlanArgs {
+  const int32_t* cu;  // nullptr: no plan
+  int N, C;
+  int32_t* cu_chunks;
+  int32_t* cu_full;
+};
+__device__ __forceinline__ void plan_counts(const PlanArgs& p) {
+  int32_t a = 0, b = 0;
+  p.cu_chunks[0] = 0;
+  p.cu_full[0] = 0;
+  for (int n = 0; n < p.N; ++n) {
+    int32_t L = p.cu[n + 1] - p.cu[n];
+    if (L < 0) L = 0;
+    a += (L + p.C - 1) / p.C;
+    b += L / p.C;
+    p.cu_chunks[n + 1] = a;
+    p.cu_full[n + 1] = b;
+  }
+}
 __global__ void k_plan(const int32_t* __restrict__ cu, int N, int C, int32_t* __restrict__ cu_chunks,
                        int32_t* __restrict__ cu_full) {
   if (blockIdx.x != 0 || threadIdx.x != 0) return;
-  int32_t a = 0, b = 0;
-  cu_chunks[0] = 0;
-  cu_full[0] = 0;
-  for (int n = 0; n < N; ++n) {
-    int32_t L = cu[n + 1] - cu[n];
-    if (L < 0) L = 0;
-    a += (L + C - 1) / C;
-    b += L / C;
-    cu_chunks[n + 1] = a;
-    cu_full[n + 1] = b;
-  }
+  plan_counts(PlanArgs{cu, N, C, cu_chunks, cu_full});
 }
 
 // Sequences by length, longest first (ties by index): order[rank] = n.  One
@@ -165,7 +176,8 @@ constexpr int kPrepVecs = 4;
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void k_prep(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                               float* __restrict__ qk, int64_t T, int H_qk,
-                                              float scale, int l2) {
+                                              float scale, int l2, PlanArgs plan) {
+  if (plan.cu && blockIdx.x == 0 && threadIdx.x == 0) plan_counts(plan);
   const int64_t nvec = T * H_qk;
   const int64_t vec0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepVecs;
   if (vec0 >= nvec) return;
@@ -3168,6 +3180,24 @@ const int32_t* scan_order(const int32_t* cu, int32_t N, int H_v, const gdn::Layo
   return order;
 }
 
+// The chunk plan and the prep layout: one prep launch whose first thread
+// also writes the plan, or the planner alone when there are no tokens.
+template <int D, typename TIn>
+void launch_plan_prep(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const int32_t* cu,
+                      const void* q, const void* k, float* qk, int32_t* cu_chunks, int32_t* cu_full,
+                      hipStream_t st) {
+  const int64_t nvec = cnt.T * s->H_qk;
+  if (nvec <= 0) {
+    Timed t_("k_plan", st);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, st, cu, N, s->C, cu_chunks, cu_full);
+    return;
+  }
+  Timed t_("k_prep", st);
+  hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256), 0, st,
+                     static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T, s->H_qk,
+                     s->scale, s->qk_l2norm, PlanArgs{cu, N, s->C, cu_chunks, cu_full});
+}
+
 template <int D, int C, typename TIn>
 int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const gdn::Layout& L,
                    const int32_t* cu, const void* q, const void* k, const void* v,
@@ -3183,17 +3213,7 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   float* Gs = reinterpret_cast<float*>(ws + L.G);
   float* states = reinterpret_cast<float*>(ws + L.states);
 
-  if (!gathered) {
-    Timed t_("k_plan", st);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, st, cu, N, C, cu_chunks, cu_full);
-  }
-  const int64_t nvec = cnt.T * s->H_qk;
-  if (nvec > 0 && !gathered) {
-    Timed t_("k_prep", st);
-    hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256), 0,
-                       st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
-                       s->H_qk, s->scale, s->qk_l2norm);
-  }
+  if (!gathered) launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, st);
   if (cnt.full > 0) {
     ChunkIO io{};
     io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_full;
@@ -3327,17 +3347,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   float* Gs = reinterpret_cast<float*>(ws + L.G);
   float* states = reinterpret_cast<float*>(ws + L.states);
   float* Dl = reinterpret_cast<float*>(ws + L.Dl);
-  {
-    Timed t_("k_plan", st);
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, st, cu, N, C, cu_chunks, cu_full);
-  }
-  const int64_t nvec = cnt.T * s->H_qk;
-  if (nvec > 0) {
-    Timed t_("k_prep", st);
-    hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256), 0,
-                       st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
-                       s->H_qk, s->scale, s->qk_l2norm);
-  }
+  launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, st);
   if (cnt.chunks > 0) {
     ChunkIO io{};
     io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_chunks;
@@ -3424,6 +3434,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
         hipLaunchKernelGGL((k_bwd_chunk<D, C, TIn>), cgrid, dim3(256), 0, st, b);
     }
   }
+  const int64_t nvec = cnt.T * s->H_qk;
   if (nvec > 0) {
     Timed t_("k_bwd_qk", st);
     hipLaunchKernelGGL((k_bwd_qk<D, TIn>),
@@ -3451,17 +3462,7 @@ int launch_prefill_chunked(const gdn_shape_t* s, int32_t N, const gdn::Counts& c
     float* Gs = reinterpret_cast<float*>(ws + L.G);
     float* states = reinterpret_cast<float*>(ws + L.states);
     float* Dl = reinterpret_cast<float*>(ws + L.Dl);
-    {
-      Timed t_("k_plan", st);
-      hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, st, cu, N, C, cu_chunks, cu_full);
-    }
-    const int64_t nvec = cnt.T * s->H_qk;
-    if (nvec > 0) {
-      Timed t_("k_prep", st);
-      hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256),
-                         0, st, static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T,
-                         s->H_qk, s->scale, s->qk_l2norm);
-    }
+    launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, st);
     if (cnt.chunks > 0) {
       ChunkIO io{};
       io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_chunks;
