@@ -2141,6 +2141,20 @@ __global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
     int64_t slot, tok0;
     int h, L;
     const bool ok = bwd_item_at<C>(io, it, slot, h, tok0, L);
+    const int64_t sh = ok ? slot * io.H_v + h : 0;
+    const int n = 16 * w + l16;  // the X row this lane streams
+    const float* x1 = io.states + sh * DD + n * D + 4 * g;
+    const float* x2 = io.dstates + sh * DD + n * D + 4 * g;
+    // this lane's 16-byte pieces of its S and dS' rows, one per k step, loaded
+    // two steps ahead (the first two before the staging barriers)
+    float4 p1[D / 16], p2[D / 16];
+    if (ok) {
+#pragma unroll
+      for (int s4 = 0; s4 < 2; ++s4) {
+        p1[s4] = *reinterpret_cast<const float4*>(x1 + 16 * s4);
+        p2[s4] = *reinterpret_cast<const float4*>(x2 + 16 * s4);
+      }
+    }
     __syncthreads();  // the previous item's LDS reads are done
 #pragma unroll
     for (int m = 0; m < NY; ++m)
@@ -2149,24 +2163,19 @@ __global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
     __syncthreads();
     if (it + gridDim.x < nitems) load_y(ypre, it + gridDim.x);
     if (!ok) continue;  // uniform over the block
-    const int64_t sh = slot * io.H_v + h;
-    const int n = 16 * w + l16;  // the X row this lane streams
-    const float* x1 = io.states + sh * DD + n * D + 4 * g;
-    const float* x2 = io.dstates + sh * DD + n * D + 4 * g;
     v4f acc[3][4];
 #pragma unroll
     for (int pr = 0; pr < 3; ++pr)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[pr][mb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     float mdm = 0.0f;
-    float4 a1 = *reinterpret_cast<const float4*>(x1), a2 = *reinterpret_cast<const float4*>(x2);
-#pragma unroll 2
+#pragma unroll
     for (int s4 = 0; s4 < D / 16; ++s4) {
-      const float4 c1 = a1, c2 = a2;
-      if (s4 + 1 < D / 16) {
-        a1 = *reinterpret_cast<const float4*>(x1 + 16 * (s4 + 1));
-        a2 = *reinterpret_cast<const float4*>(x2 + 16 * (s4 + 1));
+      if (s4 + 2 < D / 16) {
+        p1[s4 + 2] = *reinterpret_cast<const float4*>(x1 + 16 * (s4 + 2));
+        p2[s4 + 2] = *reinterpret_cast<const float4*>(x2 + 16 * (s4 + 2));
       }
+      const float4 c1 = p1[s4], c2 = p2[s4];
       mdm = fmaf(c1.x, c2.x, mdm);
       mdm = fmaf(c1.y, c2.y, mdm);
       mdm = fmaf(c1.z, c2.z, mdm);
@@ -2190,6 +2199,7 @@ __global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
         acc[1][mb] = mfma4(y1.w, c1.w, acc[1][mb]);
         acc[2][mb] = mfma4(y2.w, c2.w, acc[2][mb]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep each step's loads two steps ahead
     }
 #pragma unroll
     for (int pr = 0; pr < 3; ++pr) {
@@ -2699,8 +2709,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) acc[ct] = mfma4(a, Y[bj][ct][s4], acc[ct]);
         }
+      // row pp (solved) is subtracted from the rows above it; the coefficients
+      // of rows at or below pp are the zeros of the masked Gram tile, so those
+      // rows keep their values (up to the sign of a zero).  Row 0 updates nothing.
 #pragma unroll
-      for (int pp = 15; pp >= 0; --pp) {
+      for (int pp = 15; pp >= 1; --pp) {
         const int gp = pp >> 2, rp = pp & 3;
         const int prow = 16 * bi + pp;
         float a[4];
@@ -2710,10 +2723,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
         for (int ct = 0; ct < 2; ++ct) {
           const float y = __shfl(acc[ct][rp], l16 + 16 * gp, 64);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float upd = fmaf(-a[r], y, acc[ct][r]);
-            acc[ct][r] = 4 * g + r < pp ? upd : acc[ct][r];
-          }
+          for (int r = 0; r < 4; ++r) acc[ct][r] = fmaf(-a[r], y, acc[ct][r]);
         }
       }
 #pragma unroll
