@@ -69,6 +69,9 @@ def compare(inp, r, tol, dhT=None, seqs=None, hv=None, rows=None, scale=1.0, rel
     ("f32", [37, 16, 5], 16, 1, 2),
     ("bf16", [150, 64, 1, 77], 128, 2, 4),
     ("f32", [130, 64], 128, 1, 2),
+    ("bf16", [70], 128, 1, 1),
+    ("bf16", [100, 37], 128, 1, 3),
+    ("bf16", [90, 20], 128, 2, 8),
 ])
 def test_fwd_bwd_parity(dtype, lens, d, Hq, Hv):
     say(f"case: fwd_bwd {dtype} d{d} lens={lens} H {Hq}/{Hv}")

@@ -156,6 +156,27 @@ def test_decode_continues_prefill_bit_exactly(pre, use_pos_host):
     assert torch.equal(cache.pos.cpu(), c_full.pos.cpu())
 
 
+@pytest.mark.parametrize("Hq,Hv", [(1, 1), (1, 3), (2, 8)])
+def test_head_group_ratios_prefill_parity_and_decode(Hq, Hv):
+    """Value heads per q/k head of 1, 3 and 4: prefill parity with the oracle,
+    and a prefix prefill plus decode across a chunk edge equals one prefill."""
+    total, pre = 100, 30
+    say(f"case: head groups H_qk={Hq} H_v={Hv}, 2 x {total} tokens, decode from {pre}")
+    inp = make_inputs([total] * 2, Hq, Hv, 128, "bf16", seed=41, h0="normal")
+    o_full, h_full, _ = run_prefill(inp, cache=True)
+    check_parity(inp, o_full, h_full, TOL["bf16"])
+    first = dict(inp)
+    idx = torch.cat([torch.arange(n * total, n * total + pre) for n in range(2)])
+    for key in ["q", "k", "v", "beta", "g"]:
+        first[key] = inp[key][idx].contiguous()
+    first["cu_seqlens"] = torch.tensor([0, pre, 2 * pre], dtype=torch.int32)
+    _, _, cache = run_prefill(first, cache=True)
+    od = decode_tokens(inp, cache, shape_for(inp), pre, total - pre)
+    for n in range(2):
+        assert bit_equal(od[:, n], o_full[n * total + pre:(n + 1) * total]), f"o seq {n}"
+    assert bit_equal(cache.S_run, h_full)
+
+
 def test_mixed_position_decode_equals_prefill():
     """Sequences sitting at different offsets inside their chunks decode together
     (one call per step, each sequence resyncing on its own step); every output
