@@ -767,12 +767,14 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
 // group g supplying i = 32 g + s).  The solve is blocked by 16 rows: block
 // row b starts from its right-hand side, subtracts A[b][c] Y[c] for the solved
 // blocks c < b on the matrix cores (k-steps s = 0..3, group g supplying row
-// 4 g + s of block c), then runs forward substitution inside the block, row
-// by row, each solved row broadcast across the wave with a shuffle.  Wave w
-// owns 64 columns: W[:, 64w..] for w < 2, U[:, 64(w-2)..] for w >= 2.  Decode
-// resync runs this same kernel.
+// 4 g + s of block c), then multiplies by the inverse of its unit lower
+// triangular diagonal block, T_b = (I + A_bb)^-1, also on the matrix cores.
+// Each T_b is formed once per chunk by forward substitution on the identity
+// (row by row, each solved row broadcast across the wave with a shuffle).
+// Wave w owns 64 columns: W[:, 64w..] for w < 2, U[:, 64(w-2)..] for w >= 2.
+// Decode resync runs this same kernel.
 template <int C, typename TIn, int MODE>
-__global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_wy_mfma(ChunkIO io) {
   constexpr int D = 128;
   constexpr int KS = D + 4;  // row stride of sK
   constexpr int AS = C + 4;  // row stride of sA
@@ -915,6 +917,31 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
     }
   }
   __syncthreads();
+  // T_b = (I + A_bb)^-1 for the diagonal 16 x 16 blocks: wave w inverts block
+  // w by forward substitution on the identity (pivot rows 0..14 in order; the
+  // coefficients at or above the pivot are the diagonal tile's zeros), holding
+  // T[4 g + r][l16] in register r, and stores it row-major in an upper tile of
+  // A (those tiles are never read as A).
+  constexpr int kTRow[4] = {0, 0, 0, 1}, kTCol[4] = {1, 2, 3, 2};
+  {
+    const int tb = w;
+    v4f t;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[r] = 4 * g + r == l16 ? 1.0f : 0.0f;
+#pragma unroll
+    for (int pp = 0; pp < 15; ++pp) {
+      float a[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = sA[(16 * tb + 4 * g + r) * AS + 16 * tb + pp];
+      const float y = __shfl(t[pp & 3], l16 + 16 * (pp >> 2), 64);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] = fmaf(-a[r], y, t[r]);
+    }
+    const int trow = tb == 3 ? 1 : 0, tcol = tb == 3 ? 2 : tb + 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sA[(16 * trow + 4 * g + r) * AS + 16 * tcol + l16] = t[r];
+  }
+  __syncthreads();
   float* out = (isW ? io.W : io.U) + (slot * io.H_v + h) * static_cast<int64_t>(C) * D;
   v4f Y[4][4];  // [row block][column tile], accumulator layout
 #pragma unroll
@@ -936,31 +963,24 @@ __global__ __launch_bounds__(256) void k_wy_mfma(ChunkIO io) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) acc[ct] = mfma4(a, Y[bj][ct][s4], acc[ct]);
       }
-    // forward substitution inside the block: row pp (solved) is subtracted
-    // from every row of the block with its coefficient; the coefficients of
-    // rows at or above pp are the zeros of the diagonal tile, so those rows
-    // keep their values (up to the sign of a zero).  Row 15 updates nothing.
-    // The coefficients of four consecutive pivots are one 16-byte read per row.
+    // the block's rows: Y_bi = T_bi (right-hand side - sum_bj A_bi,bj Y_bj) on
+    // the matrix cores, k-steps r = 0..3 with lane group g supplying row 4 g + r
+    {
+      const float4 tl = *reinterpret_cast<const float4*>(sA + (16 * kTRow[bi] + l16) * AS +
+                                                          16 * kTCol[bi] + 4 * g);
+      v4f yv[4];
 #pragma unroll
-    for (int pq = 0; pq < 4; ++pq) {
-      float4 aq[4];
+      for (int ct = 0; ct < 4; ++ct) yv[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        aq[r] = *reinterpret_cast<const float4*>(sA + (16 * bi + 4 * g + r) * AS + 16 * bi + 4 * pq);
+      for (int ct = 0; ct < 4; ++ct) yv[ct] = mfma4(tl.x, acc[ct][0], yv[ct]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pp = 4 * pq + e;
-        if (pp == 15) continue;
-        float a[4];
+      for (int ct = 0; ct < 4; ++ct) yv[ct] = mfma4(tl.y, acc[ct][1], yv[ct]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = e == 0 ? aq[r].x : e == 1 ? aq[r].y : e == 2 ? aq[r].z : aq[r].w;
+      for (int ct = 0; ct < 4; ++ct) yv[ct] = mfma4(tl.z, acc[ct][2], yv[ct]);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const float y = __shfl(acc[ct][e], l16 + 16 * pq, 64);
+      for (int ct = 0; ct < 4; ++ct) yv[ct] = mfma4(tl.w, acc[ct][3], yv[ct]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ct][r] = fmaf(-a[r], y, acc[ct][r]);
-        }
-      }
+      for (int ct = 0; ct < 4; ++ct) acc[ct] = yv[ct];
     }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -3736,8 +3756,8 @@ int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
 }
 
 const char* gdn_contract_id(void) {
-  return "gdn-cpr/v7;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
-         "B=mfma16x16x4-wy-blocked16,mfma16x16x4-scan-regB;prep=wave-butterfly;src=" GDN_SOURCE_DIGEST;
+  return "gdn-cpr/v8;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
+         "B=mfma16x16x4-wy-blocked16-diaginv,mfma16x16x4-scan-regB;prep=wave-butterfly;src=" GDN_SOURCE_DIGEST;
 }
 
 int gdn_contract_check(const char* id) {
