@@ -774,18 +774,17 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
 // Wave w owns 64 columns: W[:, 64w..] for w < 2, U[:, 64(w-2)..] for w >= 2.
 // Decode resync runs this same kernel.
 template <int C, typename TIn, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_wy_mfma(ChunkIO io) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_wy_mfma(ChunkIO io) {
   constexpr int D = 128;
   constexpr int KS = D + 4;  // row stride of sK
   constexpr int AS = C + 4;  // row stride of sA
   static_assert(C == 64, "tiling assumes C = 64");
   constexpr bool RESYNC = MODE == kResync;
-  // V is staged (coalesced) in the space A takes later
-  constexpr int VWORDS = C * D * static_cast<int>(sizeof(TIn)) / 4, AWORDS = C * AS;
+  // A takes K's space once the Gram products have read K (34.5 KB of LDS per
+  // block: four blocks per CU)
+  static_assert(C * AS <= C * KS, "A fits in K's space");
   __shared__ __attribute__((aligned(16))) float sK[C * KS];
-  __shared__ __attribute__((aligned(16))) float sAV[AWORDS > VWORDS ? AWORDS : VWORDS];
-  float* sA = sAV;
-  TIn* sV = reinterpret_cast<TIn*>(sAV);
+  float* sA = sK;
   __shared__ float sB[C], sG[C], sBG[C];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -817,18 +816,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const bool isW = w < 2;
   const int cbase = 64 * (w & 1);
   const TIn* v = static_cast<const TIn*>(io.v) + tok0 * io.H_v * D + static_cast<int64_t>(h) * D;
-  // rows past a partial chunk's end read the last row (in bounds) and are zeroed
-  constexpr int EPV = 16 / static_cast<int>(sizeof(TIn));  // elements per 16 bytes
-  static_assert((C * (D / EPV)) % 256 == 0, "whole rounds");
+  // right-hand-side sources of this wave's columns, (row 16 bi + 4 g + r,
+  // column cbase + 16 ct + l16): V straight from memory for the U waves (rows
+  // past a partial chunk's end are outside the buffer range and read 0), K from
+  // LDS for the W waves below
+  float rpre[4][4][4];
+  if (!isW) {  // wave-uniform
+    constexpr uint32_t ES = sizeof(TIn);
+    const uint32_t rs = static_cast<uint32_t>(io.H_v) * D * ES;  // row stride, bytes
+    const brsrc_t rv = make_rsrc(v, static_cast<uint32_t>(L - 1) * rs + D * ES);
+    const uint32_t vo = static_cast<uint32_t>(4 * g) * rs + static_cast<uint32_t>(cbase + l16) * ES;
 #pragma unroll
-  for (int e_ = 0; e_ < (C * (D / EPV)) / 256; ++e_) {
-    const int e = tid + 256 * e_;
-    const int p = e / (D / EPV), c4 = e % (D / EPV);
-    const int pc = p < L ? p : L - 1;
-    const uint4 x = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(pc) * io.H_v * D + c4 * EPV);
-    const bool in = p < L;
-    *reinterpret_cast<uint4*>(sV + p * D + c4 * EPV) =
-        uint4{in ? x.x : 0u, in ? x.y : 0u, in ? x.z : 0u, in ? x.w : 0u};
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          rpre[bi][ct][r] = ldbuf(rv, vo, static_cast<uint32_t>(16 * bi + r) * rs + 16u * ct * ES,
+                                  static_cast<const TIn*>(nullptr));
   }
   static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
 #pragma unroll
@@ -848,23 +853,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     sBG[tid] = tid < L ? gx : 0.0f;  // raw g for now
   }
   __syncthreads();
-  // values of this wave's U columns: (row 16 bi + 4 g + r, column cbase + 16 ct + l16)
-  float vpre[4][4][4];
-  if (isW) {  // wave-uniform: the W waves need no values
+  if (isW) {  // wave-uniform
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vpre[bi][ct][r] = 0.0f;
-  } else {
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vpre[bi][ct][r] = ldin(sV + (16 * bi + 4 * g + r) * D + cbase + 16 * ct + l16);
+        for (int r = 0; r < 4; ++r) rpre[bi][ct][r] = sK[(16 * bi + 4 * g + r) * KS + cbase + 16 * ct + l16];
   }
   if (tid == 0) {  // running sum of g, p ascending
     float acc = 0.0f;
@@ -903,6 +898,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         kk[t] = mfma4(a4.w, b4.w, kk[t]);
       }
     }
+    __syncthreads();  // every wave's Gram reads of K are done: A overwrites K
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       if (t >= nt) continue;
@@ -951,8 +947,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = 16 * bi + 4 * g + r, col = cbase + 16 * ct + l16;
-        const float wv = sBG[p] * sK[p * KS + col], uv = sB[p] * vpre[bi][ct][r];
+        const int p = 16 * bi + 4 * g + r;
+        const float wv = sBG[p] * rpre[bi][ct][r], uv = sB[p] * rpre[bi][ct][r];
         acc[ct][r] = isW ? wv : uv;
       }
 #pragma unroll
