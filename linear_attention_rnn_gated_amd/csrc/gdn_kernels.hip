@@ -826,14 +826,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const uint32_t rs = static_cast<uint32_t>(io.H_v) * D * ES;  // row stride, bytes
     const brsrc_t rv = make_rsrc(v, static_cast<uint32_t>(L - 1) * rs + D * ES);
     const uint32_t vo = static_cast<uint32_t>(4 * g) * rs + static_cast<uint32_t>(cbase + l16) * ES;
+    // A partial chunk (only in the all-chunks mode) relies on the range check
+    // for its missing rows, so there the row is part of the lane offset (the
+    // hardware range-checks the lane offset, not the scalar one); a full chunk
+    // keeps the row in the scalar offset.  The branch is uniform per block.
+    if (MODE != kAll || L == C) {
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+      for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          rpre[bi][ct][r] = ldbuf(rv, vo, static_cast<uint32_t>(16 * bi + r) * rs + 16u * ct * ES,
-                                  static_cast<const TIn*>(nullptr));
+          for (int r = 0; r < 4; ++r)
+            rpre[bi][ct][r] = ldbuf(rv, vo, static_cast<uint32_t>(16 * bi + r) * rs + 16u * ct * ES,
+                                    static_cast<const TIn*>(nullptr));
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            rpre[bi][ct][r] = ldbuf(rv, vo + static_cast<uint32_t>(16 * bi + r) * rs + 16u * ct * ES, 0u,
+                                    static_cast<const TIn*>(nullptr));
+    }
   }
   static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
 #pragma unroll
@@ -2217,13 +2232,16 @@ __global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each step's loads two steps ahead
     }
+    // products out through buffer stores: lane part (row 4 g, column n) in a
+    // VGPR, the row block and row in an SGPR
+    const uint32_t fo = 4u * static_cast<uint32_t>(4 * g * D + n);
 #pragma unroll
     for (int pr = 0; pr < 3; ++pr) {
-      float* out = (pr == 0 ? io.SdO : pr == 1 ? io.SdD : io.DsD) + sh * CD;
+      const brsrc_t ro = make_rsrc((pr == 0 ? io.SdO : pr == 1 ? io.SdD : io.DsD) + sh * CD, C * D * 4u);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[(16 * mb + 4 * g + r) * D + n] = acc[pr][mb][r];
+        for (int r = 0; r < 4; ++r) stbuf(acc[pr][mb][r], ro, fo, static_cast<uint32_t>((16 * mb + r) * D * 4));
     }
     // <S, dS'>: wave butterfly, then the 8 wave sums in ascending order
 #pragma unroll
