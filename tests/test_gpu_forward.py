@@ -156,9 +156,10 @@ def test_decode_continues_prefill_bit_exactly(pre, use_pos_host):
     assert torch.equal(cache.pos.cpu(), c_full.pos.cpu())
 
 
-@pytest.mark.parametrize("Hq,Hv", [(1, 1), (1, 3), (2, 8)])
+@pytest.mark.parametrize("Hq,Hv", [(1, 1), (1, 3), (2, 8), (1, 8)])
 def test_head_group_ratios_prefill_parity_and_decode(Hq, Hv):
-    """Value heads per q/k head of 1, 3 and 4: prefill parity with the oracle,
+    """Value heads per q/k head of 1, 3, 4 and 8 (the largest group the library
+    accepts): prefill parity with the oracle,
     and a prefix prefill plus decode across a chunk edge equals one prefill."""
     total, pre = 100, 30
     say(f"case: head groups H_qk={Hq} H_v={Hv}, 2 x {total} tokens, decode from {pre}")
@@ -175,6 +176,16 @@ def test_head_group_ratios_prefill_parity_and_decode(Hq, Hv):
     for n in range(2):
         assert bit_equal(od[:, n], o_full[n * total + pre:(n + 1) * total]), f"o seq {n}"
     assert bit_equal(cache.S_run, h_full)
+
+
+def test_long_sequence_parity():
+    """One 32768-token sequence (512 chunks in one serial scan, token offsets
+    past 2^15 per head): o and the final state against the oracle."""
+    lens = [32768]
+    say(f"case: long sequence {lens[0]} tokens, H_qk=1 H_v=2, d128 bf16")
+    inp = make_inputs(lens, 1, 2, 128, "bf16", seed=43, h0="normal")
+    o, hT, _ = run_prefill(inp)
+    check_parity(inp, o, hT, TOL["bf16"])
 
 
 def test_mixed_position_decode_equals_prefill():
