@@ -210,9 +210,10 @@ def _cu_pair(cu_seqlens, dev, cu_seqlens_host):
 
 
 def gdn_prefill(shape, q, k, v, beta, g, cu_seqlens, h0=None, cache=None, want_hT=True,
-                ws=None, out=None, cu_seqlens_host=None):
+                ws=None, out=None, cu_seqlens_host=None, hT_out=None):
     """Packed prefill.  cu_seqlens: int32 device tensor [N+1]; its host copy is
-    taken here unless cu_seqlens_host is given.  Returns (o, hT)."""
+    taken here unless cu_seqlens_host is given.  out / hT_out: optional
+    caller-owned o [T, H_v, d] and hT [N, H_v, d, d] fp32.  Returns (o, hT)."""
     dev = q.device
     T = q.shape[0]
     n = cu_seqlens.numel() - 1
@@ -227,7 +228,12 @@ def gdn_prefill(shape, q, k, v, beta, g, cu_seqlens, h0=None, cache=None, want_h
         _req(h0, torch.float32, (n, Hv, d, d), "h0")
     cu_dev, cu_host = _cu_pair(cu_seqlens, dev, cu_seqlens_host)
     o = torch.empty(T, Hv, d, dtype=torch.float32, device=dev) if out is None else out
-    hT = torch.empty(n, Hv, d, d, dtype=torch.float32, device=dev) if want_hT else None
+    _req(o, torch.float32, (T, Hv, d), "out")
+    if hT_out is not None:
+        _req(hT_out, torch.float32, (n, Hv, d, d), "hT_out")
+        hT = hT_out
+    else:
+        hT = torch.empty(n, Hv, d, d, dtype=torch.float32, device=dev) if want_hT else None
     ws = _workspace(shape, n, T, OP_PREFILL, dev, ws)
     cs = cache.struct() if cache is not None else None
     st = lib().gdn_prefill(ctypes.byref(shape), n, _ptr(cu_dev),
@@ -325,9 +331,10 @@ def gdn_decode_step(shape, q, k, v, beta, g, cache, pos_host=None, ws=None, out=
 
 
 def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=None,
-                grad_dtype=torch.float32, cu_seqlens_host=None):
+                grad_dtype=torch.float32, cu_seqlens_host=None, out=None):
     """Trainer forward + backward.  Returns dict(o, hT, dq, dk, dv, dbeta, dg, dh0);
-    dq, dk, dv in grad_dtype (float32 or bfloat16), the rest float32."""
+    dq, dk, dv in grad_dtype (float32 or bfloat16), the rest float32.  out:
+    optional dict of caller-owned tensors for some or all of those outputs."""
     dev = q.device
     T = q.shape[0]
     n = cu_seqlens.numel() - 1
@@ -351,6 +358,9 @@ def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=N
              dq=torch.empty(T, Hq, d, **gd), dk=torch.empty(T, Hq, d, **gd),
              dv=torch.empty(T, Hv, d, **gd), dbeta=torch.empty(T, Hv, **f32),
              dg=torch.empty(T, Hv, **f32), dh0=torch.empty(n, Hv, d, d, **f32))
+    for key, t in (out or {}).items():
+        _req(t, r[key].dtype, tuple(r[key].shape), f"out[{key!r}]")
+        r[key] = t
     ws = _workspace(shape, n, T, OP_FWD_BWD, dev, ws)
     st = lib().gdn_fwd_bwd_ex(ctypes.byref(shape), n, _ptr(cu_dev),
                               ctypes.c_void_p(cu_host.data_ptr()), _ptr(q), _ptr(k), _ptr(v),

@@ -103,12 +103,16 @@ def test_fwd_bwd_forward_is_prefill_and_deterministic():
 
 def test_fwd_bwd_b8_t4096_full_size():
     """B=8, T=4096, 16 q/k / 32 v heads, d=128, C=64, bf16, dO ~ N(0,1): oracle
-    on one q/k group of one sequence; bitwise run-to-run."""
+    on one q/k group of one sequence; forward o and hT equal gdn_prefill's bit
+    for bit; bitwise run-to-run."""
     say("case: fwd_bwd B8 T4096 H16/32 d128 (sampled oracle)")
     inp = make_inputs([4096] * 8, 16, 32, 128, "bf16", seed=3, h0="normal", with_do=True)
     r1 = run_fwd_bwd(inp)
     for k in GRADS:
         assert torch.isfinite(r1[k]).all(), k
+    o, hT, _ = run_prefill(inp)
+    assert bit_equal(r1["o"], o) and bit_equal(r1["hT"], hT), "fwd_bwd forward != prefill"
+    del o, hT
     hq, n = 6, 5
     gi, hv = group_slice(inp, hq)
     rows = rows_of(inp, [n])
