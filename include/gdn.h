@@ -149,6 +149,30 @@ int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q,
                     const float* g, gdn_cache_t* cache, const int32_t* pos_host,
                     float* o, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the fixed device scratch of gdn_decode_step_noalloc, per GPU. */
+#define GDN_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/*
+ * gdn_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and the same bits as gdn_decode_step, without the workspace:
+ * the resync's chunk factors go to a fixed device array of
+ * GDN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The resync runs in groups of sequences whose
+ * factors fit that array together (H_v * C * (2 d_k + 1) * 4 bytes per
+ * sequence: 15 sequences at H_v = 32, d = 128, C = 64), so a batch larger
+ * than one group costs two launches per extra group on the steps that
+ * resync (every step when pos_host is NULL).  No hipMalloc, hipFree or other
+ * allocating call is made.  GDN_ERR_WORKSPACE if a single sequence's factors
+ * do not fit.  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (e.g. on two streams) race and must not be issued; the
+ * array keeps the last call's contents, which no call reads before writing.
+ */
+int gdn_decode_step_noalloc(const gdn_shape_t* shape, int32_t n_seqs, const void* q,
+                            const void* k, const void* v, const float* beta,
+                            const float* g, gdn_cache_t* cache,
+                            const int32_t* pos_host, float* o, void* stream);
+
 /*
  * Chunked-prefill continuation: n_seqs sequences whose decode cache stands
  * anywhere inside a chunk (cache->pos = p, the same for every head of a

@@ -25,7 +25,7 @@ OP_PREFILL, OP_DECODE, OP_FWD_BWD, OP_PREFILL_CHUNKED, OP_PREFILL_CONTINUE = 0, 
 EXPORTS = ["gdn_workspace_bytes", "gdn_cache_init", "gdn_prefill", "gdn_decode_step",
            "gdn_fwd_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_contract_id",
            "gdn_contract_check", "gdn_error_string", "gdn_prefill_chunked",
-           "gdn_prefill_continue", "gdn_fwd_bwd_ex"]
+           "gdn_prefill_continue", "gdn_fwd_bwd_ex", "gdn_decode_step_noalloc"]
 
 
 class Shape(ctypes.Structure):
@@ -69,6 +69,8 @@ def lib():
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_decode_step.argtypes = [sp, i32, vp, vp, vp, vp, vp, cp, vp, vp, vp, sz, vp]
         L.gdn_decode_step.restype = ctypes.c_int
+        L.gdn_decode_step_noalloc.argtypes = [sp, i32, vp, vp, vp, vp, vp, cp, vp, vp, vp]
+        L.gdn_decode_step_noalloc.restype = ctypes.c_int
         L.gdn_fwd_bwd.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_fwd_bwd.restype = ctypes.c_int
@@ -327,6 +329,30 @@ def gdn_decode_step(shape, q, k, v, beta, g, cache, pos_host=None, ws=None, out=
                                _ptr(g), ctypes.byref(cs), ph, _ptr(o), _ptr(ws), ws.numel(),
                                _stream(dev))
     _check(st, "gdn_decode_step")
+    return o
+
+
+def gdn_decode_step_noalloc(shape, q, k, v, beta, g, cache, pos_host=None, out=None):
+    """gdn_decode_step without a workspace: the library's fixed device scratch
+    holds the resync's chunk factors (for callers that cannot allocate).  Pass
+    `out` (fp32 [N, H_v, d]) to keep this call free of allocations too."""
+    dev = q.device
+    n = q.shape[0]
+    d, Hq, Hv = shape.d_k, shape.H_qk, shape.H_v
+    idt = q.dtype
+    _req(q, idt, (n, Hq, d), "q")
+    _req(k, idt, (n, Hq, d), "k")
+    _req(v, idt, (n, Hv, d), "v")
+    _req(beta, torch.float32, (n, Hv), "beta")
+    _req(g, torch.float32, (n, Hv), "g")
+    o = torch.empty(n, Hv, d, dtype=torch.float32, device=dev) if out is None else out
+    _req(o, torch.float32, (n, Hv, d), "out")
+    cs = cache.struct()
+    ph = None if pos_host is None else ctypes.c_void_p(pos_host.data_ptr())
+    st = lib().gdn_decode_step_noalloc(ctypes.byref(shape), n, _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(beta), _ptr(g), ctypes.byref(cs), ph, _ptr(o),
+                                       _stream(dev))
+    _check(st, "gdn_decode_step_noalloc")
     return o
 
 

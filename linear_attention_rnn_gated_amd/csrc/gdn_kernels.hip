@@ -32,6 +32,13 @@
 #include "gdn.h"
 #include "gdn_plan.h"
 
+// Fixed device scratch of gdn_decode_step_noalloc (the resync's chunk factors),
+// for callers that cannot allocate device memory.  Each GPU the library runs
+// on holds its own copy until the process ends.  Host code never passes this
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// array's address on a device comes from hipGetSymbolAddress (scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using bf16_t = uint16_t;
@@ -3341,38 +3348,95 @@ int launch_prefill_continue(const gdn_shape_t* s, int32_t N, const gdn::Counts& 
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// The decode token step of N sequences (no workspace).
 template <int D, int C, typename TIn>
-int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const void* q,
-                  const void* k, const void* v, const float* beta, const float* g,
-                  const gdn_cache_t* cache, bool resync, float* o, char* ws, hipStream_t st) {
+void launch_token_step(const gdn_shape_t* s, int32_t N, const void* q, const void* k,
+                       const void* v, const float* beta, const float* g, const gdn_cache_t* cache,
+                       float* o, hipStream_t st) {
   DecIO io{};
   io.q = q; io.k = k; io.v = v; io.beta = beta; io.g = g; io.o = o;
   io.S_run = cache->S_run; io.kbuf = cache->kbuf; io.vbuf = cache->vbuf;
   io.bbuf = cache->bbuf; io.gbuf = cache->gbuf; io.pos = cache->pos;
   io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.l2 = s->qk_l2norm; io.scale = s->scale;
+  Timed t_("k_decode", st);
+  hipLaunchKernelGGL((k_decode<D, C, TIn>), dim3(N, s->H_v), dim3(64 * RowSplit<D>::WPH), 0, st, io);
+}
+
+// The decode resync of the N sequences of `cache` (the chunk form on their
+// chunk buffers; only those whose chunk just completed do any work), with the
+// chunk factors in W, U [N, H_v, C, D] and G [N, H_v, C].  Every (sequence,
+// head) is computed on its own, so a cache viewed from sequence n0 on
+// (cache_from) gives the same bits as the whole batch.
+template <int D, int C, typename TIn>
+void launch_resync(const gdn_shape_t* s, int32_t N, const gdn_cache_t* cache, float* W, float* U,
+                   float* Gs, hipStream_t st) {
+  ChunkIO ci{};
+  ci.khat = cache->kbuf; ci.v = cache->vbuf; ci.beta = cache->bbuf; ci.g = cache->gbuf;
+  ci.pos = cache->pos; ci.W = W; ci.U = U; ci.G = Gs;
+  ci.N = N; ci.H_qk = s->H_qk; ci.H_v = s->H_v;
+  ci.T = static_cast<int64_t>(N) * C; ci.max_slot = N;
   {
-    Timed t_("k_decode", st);
-    hipLaunchKernelGGL((k_decode<D, C, TIn>), dim3(N, s->H_v), dim3(64 * RowSplit<D>::WPH), 0, st, io);
+    Timed t_("k_wy_resync", st);
+    launch_wy<D, C, TIn, kResync>(ci, N, s->H_v, st);
   }
-  if (resync) {
-    float* W = reinterpret_cast<float*>(ws + L.W);
-    float* U = reinterpret_cast<float*>(ws + L.U);
-    float* Gs = reinterpret_cast<float*>(ws + L.G);
-    ChunkIO ci{};
-    ci.khat = cache->kbuf; ci.v = cache->vbuf; ci.beta = cache->bbuf; ci.g = cache->gbuf;
-    ci.pos = cache->pos; ci.W = W; ci.U = U; ci.G = Gs;
-    ci.N = N; ci.H_qk = s->H_qk; ci.H_v = s->H_v;
-    ci.T = static_cast<int64_t>(N) * C; ci.max_slot = N;
-    {
-      Timed t_("k_wy_resync", st);
-      launch_wy<D, C, TIn, kResync>(ci, N, s->H_v, st);
+  ScanIO si{};
+  si.khat = cache->kbuf; si.W = W; si.U = U; si.G = Gs;
+  si.S_run = cache->S_run; si.S_chunk = cache->S_chunk; si.pos = cache->pos;
+  si.N = N; si.H_qk = s->H_qk; si.H_v = s->H_v; si.max_full_slot = N;
+  Timed t_("k_scan_resync", st);
+  launch_scan<D, C, kResync>(si, N, s->H_v, st);
+}
+
+template <int D, int C, typename TIn>
+int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const void* q,
+                  const void* k, const void* v, const float* beta, const float* g,
+                  const gdn_cache_t* cache, bool resync, float* o, char* ws, hipStream_t st) {
+  launch_token_step<D, C, TIn>(s, N, q, k, v, beta, g, cache, o, st);
+  if (resync)
+    launch_resync<D, C, TIn>(s, N, cache, reinterpret_cast<float*>(ws + L.W),
+                             reinterpret_cast<float*>(ws + L.U), reinterpret_cast<float*>(ws + L.G),
+                             st);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// The cache of sequences [n0, N) of `c`, as a cache of its own.
+gdn_cache_t cache_from(const gdn_cache_t* c, const gdn_shape_t* s, int64_t n0) {
+  const int64_t d = s->d_k, C = s->C, Hq = s->H_qk, Hv = s->H_v;
+  const int64_t in = s->in_dtype == GDN_BF16 ? 2 : 4;
+  gdn_cache_t r = *c;
+  r.S_run = c->S_run + n0 * Hv * d * d;
+  r.S_chunk = c->S_chunk + n0 * Hv * d * d;
+  r.kbuf = c->kbuf + n0 * C * Hq * d;
+  r.vbuf = static_cast<char*>(c->vbuf) + n0 * C * Hv * d * in;
+  r.bbuf = c->bbuf + n0 * C * Hv;
+  r.gbuf = c->gbuf + n0 * C * Hv;
+  r.pos = c->pos + n0 * Hv;
+  return r;
+}
+
+// gdn_decode_step_noalloc: the token step of all N sequences, then the resync
+// in groups of `group` sequences whose chunk factors take turns in the fixed
+// scratch (in stream order, each group's scan has read them before the next
+// group's chunk-factor launch overwrites them).  With pos_host, groups with no
+// completing chunk are skipped.
+template <int D, int C, typename TIn>
+int launch_decode_noalloc(const gdn_shape_t* s, int32_t N, int32_t group, const gdn::Layout& Lg,
+                          const void* q, const void* k, const void* v, const float* beta,
+                          const float* g, const gdn_cache_t* cache, bool resync,
+                          const int32_t* pos_host, float* o, char* scr, hipStream_t st) {
+  launch_token_step<D, C, TIn>(s, N, q, k, v, beta, g, cache, o, st);
+  for (int32_t n0 = 0; resync && n0 < N; n0 += group) {
+    const int32_t m = N - n0 < group ? N - n0 : group;
+    if (pos_host) {
+      bool any = false;
+      for (int64_t e = static_cast<int64_t>(n0) * s->H_v; e < static_cast<int64_t>(n0 + m) * s->H_v; ++e)
+        any = any || pos_host[e] + 1 == C;
+      if (!any) continue;
     }
-    ScanIO si{};
-    si.khat = cache->kbuf; si.W = W; si.U = U; si.G = Gs;
-    si.S_run = cache->S_run; si.S_chunk = cache->S_chunk; si.pos = cache->pos;
-    si.N = N; si.H_qk = s->H_qk; si.H_v = s->H_v; si.max_full_slot = N;
-    Timed t_("k_scan_resync", st);
-    launch_scan<D, C, kResync>(si, N, s->H_v, st);
+    const gdn_cache_t sub = cache_from(cache, s, n0);
+    launch_resync<D, C, TIn>(s, m, &sub, reinterpret_cast<float*>(scr + Lg.W),
+                             reinterpret_cast<float*>(scr + Lg.U), reinterpret_cast<float*>(scr + Lg.G),
+                             st);
   }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -3539,6 +3603,36 @@ int launch_prefill_chunked(const gdn_shape_t* s, int32_t N, const gdn::Counts& c
   }
 }
 
+// Device address of `scratch` on the current device.  Looked up once per
+// device, with that device current, and kept: every GPU holds its own copy of
+// the array at its own address.
+int scratch_ptr(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GDN_ERR_HIP;
+  static std::mutex mu;
+  static std::vector<char*> ptrs;
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<size_t>(dev) >= ptrs.size()) ptrs.resize(static_cast<size_t>(dev) + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_HIP;
+    ptrs[dev] = static_cast<char*>(p);
+  }
+  *out = ptrs[dev];
+  return GDN_OK;
+}
+
+// Sequences whose resync chunk factors fit the fixed scratch together (at most
+// N; 0 if not even one sequence's do).
+int32_t noalloc_group(const gdn_shape_t* s, int32_t N) {
+  constexpr size_t cap = GDN_NOALLOC_SCRATCH_BYTES;
+  const size_t per = static_cast<size_t>(s->H_v) * s->C * (2 * static_cast<size_t>(s->d_k) + 1) * 4;
+  int64_t m = static_cast<int64_t>(cap / per);
+  if (m > N) m = N;
+  while (m > 0 && gdn::layout(s, static_cast<int32_t>(m), 0, GDN_OP_DECODE).total > cap) --m;
+  return static_cast<int32_t>(m);
+}
+
 // Calls f.template operator()<D, C, TIn>() for the shape's compiled variant.
 template <typename F>
 int dispatch(const gdn_shape_t* s, F&& f) {
@@ -3643,9 +3737,14 @@ int gdn_prefill_continue(const gdn_shape_t* shape, int32_t n_seqs, const int32_t
   });
 }
 
-int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q, const void* k,
-                    const void* v, const float* beta, const float* g, gdn_cache_t* cache,
-                    const int32_t* pos_host, float* o, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks shared by the two decode entry points; *resync tells
+// whether some sequence may complete its chunk (always, without pos_host).
+int check_decode(const gdn_shape_t* shape, int32_t n_seqs, const void* q, const void* k,
+                 const void* v, const float* beta, const float* g, const gdn_cache_t* cache,
+                 const int32_t* pos_host, const float* o, bool* resync) {
   int rc = gdn::check_shape(shape);
   if (rc != GDN_OK) return rc;
   if (n_seqs < 0) return GDN_ERR_INVALID_ARG;
@@ -3653,15 +3752,27 @@ int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q, con
   if (n_seqs > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
   if (!gdn::aligned16({q, k, v, beta, g, o})) return GDN_ERR_INVALID_ARG;
   if (n_seqs > 65535) return GDN_ERR_UNSUPPORTED;  // grid.x of the per-sequence launches
-  bool resync = true;
+  *resync = true;
   if (pos_host) {
-    resync = false;
+    *resync = false;
     const int64_t np = static_cast<int64_t>(n_seqs) * shape->H_v;
     for (int64_t e = 0; e < np; ++e) {
       if (pos_host[e] < 0 || pos_host[e] >= shape->C) return GDN_ERR_INVALID_ARG;
-      if (pos_host[e] + 1 == shape->C) resync = true;
+      if (pos_host[e] + 1 == shape->C) *resync = true;
     }
   }
+  return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q, const void* k,
+                    const void* v, const float* beta, const float* g, gdn_cache_t* cache,
+                    const int32_t* pos_host, float* o, void* ws, size_t ws_bytes, void* stream) {
+  bool resync = true;
+  int rc = check_decode(shape, n_seqs, q, k, v, beta, g, cache, pos_host, o, &resync);
+  if (rc != GDN_OK) return rc;
   const gdn::Layout L = gdn::layout(shape, n_seqs, 0, GDN_OP_DECODE);
   if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (n_seqs == 0) return GDN_OK;
@@ -3669,6 +3780,25 @@ int gdn_decode_step(const gdn_shape_t* shape, int32_t n_seqs, const void* q, con
   char* w = static_cast<char*>(ws);
   return dispatch(shape, [&]<int D, int C, typename TIn>() {
     return launch_decode<D, C, TIn>(shape, n_seqs, L, q, k, v, beta, g, cache, resync, o, w, st);
+  });
+}
+
+int gdn_decode_step_noalloc(const gdn_shape_t* shape, int32_t n_seqs, const void* q,
+                            const void* k, const void* v, const float* beta, const float* g,
+                            gdn_cache_t* cache, const int32_t* pos_host, float* o, void* stream) {
+  bool resync = true;
+  int rc = check_decode(shape, n_seqs, q, k, v, beta, g, cache, pos_host, o, &resync);
+  if (rc != GDN_OK) return rc;
+  if (n_seqs == 0) return GDN_OK;
+  const int32_t group = noalloc_group(shape, n_seqs);
+  if (group < 1) return GDN_ERR_WORKSPACE;  // one sequence's resync exceeds the scratch
+  char* scr = nullptr;
+  if ((rc = scratch_ptr(&scr)) != GDN_OK) return rc;
+  const gdn::Layout Lg = gdn::layout(shape, group, 0, GDN_OP_DECODE);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(shape, [&]<int D, int C, typename TIn>() {
+    return launch_decode_noalloc<D, C, TIn>(shape, n_seqs, group, Lg, q, k, v, beta, g, cache,
+                                            resync, pos_host, o, scr, st);
   });
 }
 

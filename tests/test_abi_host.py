@@ -221,3 +221,24 @@ def test_host_copy_of_cu_seqlens_checked():
     for bad in (cu.to(torch.int64), cu[:2].clone()):
         with pytest.raises(ValueError):
             B._cu_pair(cu, "cpu", bad)
+
+
+def test_no_alloc_decode_validation():
+    """gdn_decode_step_noalloc checks its arguments like gdn_decode_step and
+    refuses a shape whose single sequence's resync factors exceed the fixed
+    scratch (GDN_NOALLOC_SCRATCH_BYTES = 32 MiB), before any HIP call."""
+    L = B.lib()
+    a = ctypes.c_void_p(16)
+    cache = B.CacheStruct(*([16] * 7))
+    s = good_shape()
+    pos = (ctypes.c_int32 * 8)(0, 1, 2, 64, 0, 0, 0, 0)
+    assert L.gdn_decode_step_noalloc(ctypes.byref(s), 2, a, a, a, a, a, ctypes.byref(cache), pos,
+                                     a, None) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_decode_step_noalloc(ctypes.byref(s), 2, a, a, a, a, a, ctypes.byref(cache), None,
+                                     None, None) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_decode_step_noalloc(ctypes.byref(s), 0, a, a, a, a, a, ctypes.byref(cache), None,
+                                     a, None) == B.GDN_OK
+    # 1024 value heads at d = 128: 1024 * 64 * 257 * 4 bytes per sequence > 32 MiB
+    big = good_shape(H_qk=128, H_v=1024)
+    assert L.gdn_decode_step_noalloc(ctypes.byref(big), 1, a, a, a, a, a, ctypes.byref(cache),
+                                     None, a, None) == B.GDN_ERR_WORKSPACE
