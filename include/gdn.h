@@ -1,10 +1,11 @@
 /*
  * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet library, CPR schedule.
  *
- * The layer (Gated DeltaNet, named in the IsoExec write-up on agentlenshq.com,
- * section "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet"; equations as
- * published with the architecture, Yang et al., "Gated Delta Networks", ICLR
- * 2025), per sequence and value head h, with S a d_v x d_k fp32 matrix:
+ * The layer is Gated DeltaNet, named in the IsoExec write-up on agentlenshq.com
+ * (section "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet"), whose pages
+ * do not write its equations.  The definition implemented is the gated delta
+ * rule in the form in which the problem this library solves is stated, per
+ * sequence and value head h, with S a d_v x d_k fp32 matrix:
  *
  *     alpha_t = exp(g_t)
  *     S_t     = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
@@ -43,6 +44,9 @@
  *     kernels) and a host copy (validated and used to size the launches); both
  *     must hold the same values.  Kernels clamp every index to the buffers'
  *     extents, so a mismatch gives wrong values but no out-of-bounds access.
+ *     The host copy may be NULL: the call then first copies the device copy
+ *     to the host on `stream` and waits for it (the library's only host
+ *     synchronisation; a call made so cannot be captured in a graph).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
  *     the call returns without waiting.
  *   - Every argument is validated on the host before any launch; on a
@@ -252,13 +256,47 @@ int gdn_prefill_chunked(const gdn_shape_t* shape, int32_t n_seqs,
                         size_t ws_bytes, void* stream);
 
 /*
+ * Native-mixed baseline trainer step (not the CPR contract): gdn_fwd_bwd whose
+ * forward outputs o, and the final state of a sequence whose last chunk is
+ * partial, come from the chunk form (as in gdn_prefill_chunked) instead of
+ * the token recurrence; the backward is gdn_fwd_bwd's.  The same function
+ * within the parity tolerance, other bits.  It exists to measure what the
+ * bitwise guarantee costs the trainer (the write-up's stage table, CPR
+ * section: native mixed against CPR trainer fwd+bwd).  Arguments as
+ * gdn_fwd_bwd (fp32 gradients); workspace from gdn_workspace_bytes(...,
+ * GDN_OP_FWD_BWD).  d_k = d_v = 128 only (GDN_ERR_UNSUPPORTED otherwise).
+ */
+int gdn_fwd_bwd_chunked(const gdn_shape_t* shape, int32_t n_seqs,
+                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                        const void* q, const void* k, const void* v, const float* beta,
+                        const float* g, const float* h0, const float* dO,
+                        const float* dhT, float* o, float* hT, float* dq, float* dk,
+                        float* dv, float* dbeta, float* dg, float* dh0, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * Native-mixed baseline decode (not the CPR contract): the plain recurrent
+ * token step on the running state S [N, H_v, d_k, d_v] (in-out), with no
+ * chunk buffers, no position and no resync.  Its arithmetic per token is
+ * gdn_decode_step's token step, but without the resync its state leaves the
+ * prefill's bits after the first completed chunk.  It exists to measure what
+ * the bitwise guarantee costs decode (the write-up's stage table, CPR
+ * section: native mixed against CPR rollout decode).  q, k, v, beta, g, o as
+ * in gdn_decode_step; no workspace.
+ */
+int gdn_decode_step_native(const gdn_shape_t* shape, int32_t n_seqs, const void* q,
+                           const void* k, const void* v, const float* beta,
+                           const float* g, float* S, float* o, void* stream);
+
+/*
  * Kernel timing (instrumentation).  While enabled, every launch the entry
  * points make is bracketed by HIP events recorded on the call's stream.
  * gdn_profile_read waits for the recorded events, returns the summed
  * duration (ms) and launch count of the kernels whose name contains `kernel`
  * (e.g. "k_rec"; NULL or "" = all), and forgets them.  Kernel names:
  * k_plan, k_prep, k_wy, k_scan, k_rec, k_decode, k_wy_resync, k_scan_resync,
- * k_cache_init, k_chunk_o (gdn_prefill_chunked), k_cont_plan, k_cont_gather,
+ * k_cache_init, k_chunk_o (gdn_prefill_chunked, gdn_fwd_bwd_chunked),
+ * k_decode_native (gdn_decode_step_native), k_cont_plan, k_cont_gather,
  * k_cont_scatter (gdn_prefill_continue) and the k_bwd_* kernels of
  * gdn_fwd_bwd.  Events are created
  * by the library on first use and reused; no device memory is allocated.

@@ -25,7 +25,8 @@ OP_PREFILL, OP_DECODE, OP_FWD_BWD, OP_PREFILL_CHUNKED, OP_PREFILL_CONTINUE = 0, 
 EXPORTS = ["gdn_workspace_bytes", "gdn_cache_init", "gdn_prefill", "gdn_decode_step",
            "gdn_fwd_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_contract_id",
            "gdn_contract_check", "gdn_error_string", "gdn_prefill_chunked",
-           "gdn_prefill_continue", "gdn_fwd_bwd_ex", "gdn_decode_step_noalloc"]
+           "gdn_prefill_continue", "gdn_fwd_bwd_ex", "gdn_decode_step_noalloc",
+           "gdn_fwd_bwd_chunked", "gdn_decode_step_native"]
 
 
 class Shape(ctypes.Structure):
@@ -77,6 +78,11 @@ def lib():
         L.gdn_fwd_bwd_ex.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                      vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_fwd_bwd_ex.restype = ctypes.c_int
+        L.gdn_fwd_bwd_chunked.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_fwd_bwd_chunked.restype = ctypes.c_int
+        L.gdn_decode_step_native.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.gdn_decode_step_native.restype = ctypes.c_int
         L.gdn_profile_enable.argtypes = [ctypes.c_int]
         L.gdn_profile_enable.restype = ctypes.c_int
         L.gdn_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -201,8 +207,11 @@ def gdn_cache_init(shape, n, device, in_dtype, h0=None):
 def _cu_pair(cu_seqlens, dev, cu_seqlens_host):
     """Device and host int32 copies of cu_seqlens.  A caller that keeps a host
     copy (cu_seqlens_host, CPU int32 [N+1], same values) saves the
-    device-to-host copy, which waits for the stream, on every call."""
+    device-to-host copy, which waits for the stream, on every call.  With
+    cu_seqlens_host=False the library gets NULL and makes that copy itself."""
     cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    if cu_seqlens_host is False:
+        return cu_dev, None
     if cu_seqlens_host is None:
         return cu_dev, cu_seqlens.to("cpu", torch.int32).contiguous()
     if (cu_seqlens_host.device.type != "cpu" or cu_seqlens_host.dtype != torch.int32
@@ -239,7 +248,7 @@ def gdn_prefill(shape, q, k, v, beta, g, cu_seqlens, h0=None, cache=None, want_h
     ws = _workspace(shape, n, T, OP_PREFILL, dev, ws)
     cs = cache.struct() if cache is not None else None
     st = lib().gdn_prefill(ctypes.byref(shape), n, _ptr(cu_dev),
-                           ctypes.c_void_p(cu_host.data_ptr()), _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(cu_host), _ptr(q), _ptr(k), _ptr(v),
                            _ptr(beta), _ptr(g), _ptr(h0), _ptr(o), _ptr(hT),
                            ctypes.byref(cs) if cs is not None else None, _ptr(ws),
                            ws.numel(), _stream(dev))
@@ -271,7 +280,7 @@ def gdn_prefill_continue(shape, q, k, v, beta, g, cu_seqlens, cache, pos_host, w
     ws = _workspace(shape, n, T, OP_PREFILL_CONTINUE, dev, ws)
     cs = cache.struct()
     st = lib().gdn_prefill_continue(ctypes.byref(shape), n, _ptr(cu_dev),
-                                    ctypes.c_void_p(cu_host.data_ptr()),
+                                    _ptr(cu_host),
                                     ctypes.c_void_p(pos.data_ptr()), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(beta), _ptr(g), ctypes.byref(cs), _ptr(o), _ptr(hT),
                                     _ptr(ws), ws.numel(), _stream(dev))
@@ -300,7 +309,7 @@ def gdn_prefill_chunked(shape, q, k, v, beta, g, cu_seqlens, h0=None, want_hT=Tr
     hT = torch.empty(n, Hv, d, d, dtype=torch.float32, device=dev) if want_hT else None
     ws = _workspace(shape, n, T, OP_PREFILL_CHUNKED, dev, ws)
     st = lib().gdn_prefill_chunked(ctypes.byref(shape), n, _ptr(cu_dev),
-                                   ctypes.c_void_p(cu_host.data_ptr()), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(cu_host), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(beta), _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws),
                                    ws.numel(), _stream(dev))
     _check(st, "gdn_prefill_chunked")
@@ -356,8 +365,38 @@ def gdn_decode_step_noalloc(shape, q, k, v, beta, g, cache, pos_host=None, out=N
     return o
 
 
+def gdn_decode_step_native(shape, q, k, v, beta, g, S, out=None):
+    """Native-mixed baseline decode: the plain token step on the state S
+    (fp32 [N, H_v, d, d], updated in place); no chunk buffers, no resync.
+    Returns o."""
+    dev = q.device
+    n = q.shape[0]
+    d, Hq, Hv = shape.d_k, shape.H_qk, shape.H_v
+    idt = q.dtype
+    _req(q, idt, (n, Hq, d), "q")
+    _req(k, idt, (n, Hq, d), "k")
+    _req(v, idt, (n, Hv, d), "v")
+    _req(beta, torch.float32, (n, Hv), "beta")
+    _req(g, torch.float32, (n, Hv), "g")
+    _req(S, torch.float32, (n, Hv, d, d), "S")
+    o = torch.empty(n, Hv, d, dtype=torch.float32, device=dev) if out is None else out
+    _req(o, torch.float32, (n, Hv, d), "out")
+    st = lib().gdn_decode_step_native(ctypes.byref(shape), n, _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(beta), _ptr(g), _ptr(S), _ptr(o), _stream(dev))
+    _check(st, "gdn_decode_step_native")
+    return o
+
+
+def gdn_fwd_bwd_chunked(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=None,
+                        cu_seqlens_host=None):
+    """Native-mixed baseline trainer step: chunk-form forward outputs, the same
+    backward (fp32 gradients).  Returns dict(o, hT, dq, dk, dv, dbeta, dg, dh0)."""
+    return gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=h0, dhT=dhT, ws=ws,
+                       cu_seqlens_host=cu_seqlens_host, _native=True)
+
+
 def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=None,
-                grad_dtype=torch.float32, cu_seqlens_host=None, out=None):
+                grad_dtype=torch.float32, cu_seqlens_host=None, out=None, _native=False):
     """Trainer forward + backward.  Returns dict(o, hT, dq, dk, dv, dbeta, dg, dh0);
     dq, dk, dv in grad_dtype (float32 or bfloat16), the rest float32.  out:
     optional dict of caller-owned tensors for some or all of those outputs."""
@@ -388,8 +427,18 @@ def gdn_fwd_bwd(shape, q, k, v, beta, g, cu_seqlens, dO, h0=None, dhT=None, ws=N
         _req(t, r[key].dtype, tuple(r[key].shape), f"out[{key!r}]")
         r[key] = t
     ws = _workspace(shape, n, T, OP_FWD_BWD, dev, ws)
+    if _native:
+        if grad_dtype != torch.float32:
+            raise ValueError("gdn_fwd_bwd_chunked writes fp32 gradients")
+        st = lib().gdn_fwd_bwd_chunked(
+            ctypes.byref(shape), n, _ptr(cu_dev), _ptr(cu_host), _ptr(q), _ptr(k), _ptr(v),
+            _ptr(beta), _ptr(g), _ptr(h0), _ptr(dO), _ptr(dhT), _ptr(r["o"]), _ptr(r["hT"]),
+            _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dbeta"]), _ptr(r["dg"]),
+            _ptr(r["dh0"]), _ptr(ws), ws.numel(), _stream(dev))
+        _check(st, "gdn_fwd_bwd_chunked")
+        return r
     st = lib().gdn_fwd_bwd_ex(ctypes.byref(shape), n, _ptr(cu_dev),
-                              ctypes.c_void_p(cu_host.data_ptr()), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(cu_host), _ptr(q), _ptr(k), _ptr(v),
                               _ptr(beta), _ptr(g), _ptr(h0), _ptr(dO), _ptr(dhT), _ptr(r["o"]),
                               _ptr(r["hT"]), code, _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]),
                               _ptr(r["dbeta"]), _ptr(r["dg"]), _ptr(r["dh0"]), _ptr(ws),

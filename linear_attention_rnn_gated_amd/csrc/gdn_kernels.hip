@@ -1161,7 +1161,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   constexpr int NW = 8 / KS;       // (head, row part) pairs per block, at most
   __shared__ float xa[2][8][64];  // partial dots (parity, wave, lane)
   __shared__ float xo[2][8][64];
-  __shared__ TIn sv[NW][C][64];   // the chunk's v rows of each (head, row part)
+  // the chunk's v rows of each (head, row part); fp32 values at d = 128 are
+  // staged half a chunk at a time so that three blocks fit a CU's LDS
+  constexpr int SC = (sizeof(TIn) == 4 && D == 128) ? C / 2 : C;
+  __shared__ TIn sv[NW][SC][64];
   const int slot = blockIdx.x;
   const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wv = blockIdx.z * hpb * RS::WPH + wl;
@@ -1201,8 +1204,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     const int npair = static_cast<int>(blockDim.x >> 6) / KS;
     const TIn* vin = static_cast<const TIn*>(io.v);
     const int hb = blockIdx.y * G + blockIdx.z * hpb;  // first head of the block
-    for (int e = threadIdx.x; e < npair * C * 64; e += blockDim.x) {
-      const int q = e / (C * 64), tt = (e / 64) % C, ll = e % 64;
+    for (int e = threadIdx.x; e < npair * SC * 64; e += blockDim.x) {
+      const int q = e / (SC * 64), tt = (e / 64) % SC, ll = e % 64;
       const int row = (q % NH) * 64 + ll;
       const int tc = tt < L ? tt : L - 1;
       sv[q][tt][ll] = row < D ? vin[(tok0 + tc) * io.H_v * D + static_cast<int64_t>(hb + q / NH) * D + row]
@@ -1235,7 +1238,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     const int tn = t + 1 < L ? t + 1 : t;
     gn = gt[tn * bs];
     bn = bt[tn * bs];
-    vn = ldin(&sv[wp][tn][lane]);
+    if constexpr (SC < C) {
+      // the second half: every wave read its last first-half row (token SC - 1)
+      // one token ahead, before the previous token's exchange barrier
+      if (t == SC - 1 && L > SC) {  // tokens SC .. C - 1 (past the end: the last)
+        const int npair = static_cast<int>(blockDim.x >> 6) / KS;
+        const TIn* vin = static_cast<const TIn*>(io.v);
+        const int hb = blockIdx.y * G + blockIdx.z * hpb;
+        for (int e = threadIdx.x; e < npair * SC * 64; e += blockDim.x) {
+          const int q = e / (SC * 64), tt = (e / 64) % SC, ll = e % 64;
+          const int row = (q % NH) * 64 + ll;
+          const int tc = SC + tt < L ? SC + tt : L - 1;
+          sv[q][tt][ll] = row < D ? vin[(tok0 + tc) * io.H_v * D +
+                                        static_cast<int64_t>(hb + q / NH) * D + row]
+                                  : TIn(0);
+        }
+        __syncthreads();
+      }
+      vn = ldin(&sv[wp][tn >= SC ? tn - SC : tn][lane]);
+    } else {
+      vn = ldin(&sv[wp][tn][lane]);
+    }
     const float u = alpha * a;
     const float delta = b * (vj - u);
     cfloat_p kn = kq + 2 * D;  // past the chunk's end on its last token: read, never used
@@ -1315,8 +1338,10 @@ struct DecIO {
 
 // One decode token per (sequence, value head) block; waves split the state as
 // in k_rec (row parts, and d_k halves at d = 128, whose partial dots are
-// summed in the same order).
-template <int D, int C, typename TIn>
+// summed in the same order).  CPR = false is the plain recurrent decode of the
+// native-mixed baseline: the same token step on S_run, no chunk buffers, no
+// position, no resync.
+template <int D, int C, typename TIn, bool CPR = true>
 __global__ __launch_bounds__(256) void k_decode(DecIO io) {
   using RS = RowSplit<D>;
   constexpr int DK = RS::DK, KS = RS::KS;
@@ -1337,8 +1362,11 @@ __global__ __launch_bounds__(256) void k_decode(DecIO io) {
   const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
   const int64_t DD = static_cast<int64_t>(D) * D;
   const int i0 = kh * DK;
-  int p = io.pos[nh];
-  p = p < 0 ? 0 : (p >= C ? C - 1 : p);
+  int p = 0;
+  if constexpr (CPR) {
+    p = io.pos[nh];
+    p = p < 0 ? 0 : (p >= C ? C - 1 : p);
+  }
   if (threadIdx.x < 64) {
     const TIn* q = static_cast<const TIn*>(io.q) + (static_cast<int64_t>(n) * io.H_qk + hq) * D;
     const TIn* k = static_cast<const TIn*>(io.k) + (static_cast<int64_t>(n) * io.H_qk + hq) * D;
@@ -1380,17 +1408,21 @@ __global__ __launch_bounds__(256) void k_decode(DecIO io) {
     for (int i = 0; i < DK; ++i) sr[static_cast<int64_t>(i0 + i) * D + j] = s[i];
     if (kh == 0) {
       io.o[nh * D + j] = o;
-      const int64_t bt = static_cast<int64_t>(n) * C + p;
-      static_cast<TIn*>(io.vbuf)[(bt * io.H_v + h) * D + j] = v[nh * D + j];
-      if (h % G == 0) io.kbuf[(bt * io.H_qk + hq) * D + j] = sk[j];
-      if (j == 0) {
-        io.bbuf[bt * io.H_v + h] = b;
-        io.gbuf[bt * io.H_v + h] = gt;
+      if constexpr (CPR) {
+        const int64_t bt = static_cast<int64_t>(n) * C + p;
+        static_cast<TIn*>(io.vbuf)[(bt * io.H_v + h) * D + j] = v[nh * D + j];
+        if (h % G == 0) io.kbuf[(bt * io.H_qk + hq) * D + j] = sk[j];
+        if (j == 0) {
+          io.bbuf[bt * io.H_v + h] = b;
+          io.gbuf[bt * io.H_v + h] = gt;
+        }
       }
     }
   }
-  __syncthreads();  // every lane has read pos
-  if (threadIdx.x == 0) io.pos[nh] = (p + 1 == C) ? 0 : p + 1;
+  if constexpr (CPR) {
+    __syncthreads();  // every lane has read pos
+    if (threadIdx.x == 0) io.pos[nh] = (p + 1 == C) ? 0 : p + 1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -3399,6 +3431,20 @@ int launch_decode(const gdn_shape_t* s, int32_t N, const gdn::Layout& L, const v
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// The native-mixed baseline's decode: the plain token step on a state.
+template <int D, int C, typename TIn>
+int launch_decode_native(const gdn_shape_t* s, int32_t N, const void* q, const void* k,
+                         const void* v, const float* beta, const float* g, float* S, float* o,
+                         hipStream_t st) {
+  DecIO io{};
+  io.q = q; io.k = k; io.v = v; io.beta = beta; io.g = g; io.o = o; io.S_run = S;
+  io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.l2 = s->qk_l2norm; io.scale = s->scale;
+  Timed t_("k_decode_native", st);
+  hipLaunchKernelGGL((k_decode<D, C, TIn, false>), dim3(N, s->H_v), dim3(64 * RowSplit<D>::WPH), 0,
+                     st, io);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 // The cache of sequences [n0, N) of `c`, as a cache of its own.
 gdn_cache_t cache_from(const gdn_cache_t* c, const gdn_shape_t* s, int64_t n0) {
   const int64_t d = s->d_k, C = s->C, Hq = s->H_qk, Hv = s->H_v;
@@ -3441,12 +3487,18 @@ int launch_decode_noalloc(const gdn_shape_t* s, int32_t N, int32_t group, const 
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// native: the native-mixed baseline's trainer step, whose forward outputs come
+// from the chunk form (k_chunk_o over every chunk, the final state of a
+// sequence with a partial last chunk from the chunk-state scan) instead of the
+// token recurrence; the backward is the same.  d = 128 only.
 template <int D, int C, typename TIn>
 int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const gdn::Layout& L,
                    const int32_t* cu, const void* q, const void* k, const void* v,
                    const float* beta, const float* g, const float* h0, const float* dO,
                    const float* dhT, float* o, float* hT, void* dq, void* dk, void* dv,
-                   int grad_bf16, float* dbeta, float* dg, float* dh0, char* ws, hipStream_t st) {
+                   int grad_bf16, float* dbeta, float* dg, float* dh0, char* ws, hipStream_t st,
+                   bool native = false) {
+  if (native && D != 128) return GDN_ERR_UNSUPPORTED;
   int32_t* cu_chunks = reinterpret_cast<int32_t*>(ws + L.cu_chunks);
   int32_t* cu_full = reinterpret_cast<int32_t*>(ws + L.cu_full);
   float* qk = reinterpret_cast<float*>(ws + L.qk);
@@ -3470,13 +3522,24 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     ScanIO io{};
     io.khat = qk; io.W = W; io.U = U; io.G = Gs; io.cu = cu; io.cu_chunks = cu_chunks;
     io.cu_full = cu_full; io.h0 = h0; io.states = states; io.hT = hT; io.Dl = Dl;
+    if (native) io.hT_tail = hT;
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T;
     io.max_state_slot = L.state_slots; io.max_full_slot = L.state_slots;
     io.order = scan_order(cu, N, s->H_v, L, ws, st);
     Timed t_("k_scan", st);
     launch_scan<D, C, kAll>(io, N, s->H_v, st);
   }
-  if (cnt.chunks > 0) {
+  if (native && cnt.chunks > 0) {
+    if constexpr (D == 128) {
+      BwdIO b{};
+      b.qk = qk; b.cu = cu; b.cu_chunks = cu_chunks; b.G = Gs; b.states = states; b.Dl = Dl;
+      b.dqv = o;  // k_chunk_o's output
+      b.N = N; b.H_qk = s->H_qk; b.H_v = s->H_v; b.T = cnt.T; b.max_state_slot = L.state_slots;
+      Timed t_("k_chunk_o", st);
+      hipLaunchKernelGGL((k_chunk_o_m<C>), dim3(static_cast<unsigned>(cnt.chunks), s->H_v),
+                         dim3(512), 0, st, b);
+    }
+  } else if (cnt.chunks > 0) {
     RecIO io{};
     io.qk = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu;
     io.cu_chunks = cu_chunks; io.states = states; io.o = o; io.hT = hT;
@@ -3647,6 +3710,25 @@ int dispatch(const gdn_shape_t* s, F&& f) {
   return GDN_ERR_UNSUPPORTED;
 }
 
+// The host copy of cu_seqlens: the caller's, or, when cu_host is NULL, one
+// read back from the device copy (a copy enqueued on the stream and waited
+// for; the values are then validated like a caller's).
+int host_cu(const int32_t* cu_dev, const int32_t* cu_host, int32_t N, hipStream_t st,
+            std::vector<int32_t>& buf, const int32_t** out) {
+  if (cu_host) {
+    *out = cu_host;
+    return GDN_OK;
+  }
+  if (N < 0 || !cu_dev) return GDN_ERR_INVALID_ARG;
+  buf.assign(static_cast<size_t>(N) + 1, 0);
+  if (hipMemcpyAsync(buf.data(), cu_dev, buf.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return GDN_ERR_HIP;
+  *out = buf.data();
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -3684,12 +3766,16 @@ int gdn_prefill(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seql
                 gdn_cache_t* cache, void* ws, size_t ws_bytes, void* stream) {
   int rc = gdn::check_shape(shape);
   if (rc != GDN_OK) return rc;
-  if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host) return GDN_ERR_INVALID_ARG;
+  if (n_seqs < 0 || !cu_seqlens_dev) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, h0, o, hT})) return GDN_ERR_INVALID_ARG;
+  if (cache && (rc = gdn::check_cache(cache)) != GDN_OK) return rc;
+  std::vector<int32_t> cu_buf;
+  if ((rc = host_cu(cu_seqlens_dev, cu_seqlens_host, n_seqs, static_cast<hipStream_t>(stream),
+                    cu_buf, &cu_seqlens_host)) != GDN_OK)
+    return rc;
   gdn::Counts cnt;
   if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
   if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
-  if (!gdn::aligned16({q, k, v, beta, g, h0, o, hT})) return GDN_ERR_INVALID_ARG;
-  if (cache && (rc = gdn::check_cache(cache)) != GDN_OK) return rc;
   const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_PREFILL);
   if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (n_seqs == 0) return GDN_OK;
@@ -3708,13 +3794,16 @@ int gdn_prefill_continue(const gdn_shape_t* shape, int32_t n_seqs, const int32_t
                          void* stream) {
   int rc = gdn::check_shape(shape);
   if (rc != GDN_OK) return rc;
-  if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host || (n_seqs > 0 && !pos_host))
-    return GDN_ERR_INVALID_ARG;
+  if (n_seqs < 0 || !cu_seqlens_dev || (n_seqs > 0 && !pos_host)) return GDN_ERR_INVALID_ARG;
   if ((rc = gdn::check_cache(cache)) != GDN_OK) return rc;
+  if (!gdn::aligned16({q, k, v, beta, g, o, hT})) return GDN_ERR_INVALID_ARG;
+  std::vector<int32_t> cu_buf;
+  if ((rc = host_cu(cu_seqlens_dev, cu_seqlens_host, n_seqs, static_cast<hipStream_t>(stream),
+                    cu_buf, &cu_seqlens_host)) != GDN_OK)
+    return rc;
   gdn::Counts cnt;
   if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
   if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
-  if (!gdn::aligned16({q, k, v, beta, g, o, hT})) return GDN_ERR_INVALID_ARG;
   // the extended batch: each sequence's buffered tokens, then its new ones
   std::vector<int32_t> cux(static_cast<size_t>(n_seqs) + 1, 0);
   for (int32_t n = 0; n < n_seqs; ++n) {
@@ -3802,23 +3891,31 @@ int gdn_decode_step_noalloc(const gdn_shape_t* shape, int32_t n_seqs, const void
   });
 }
 
-int gdn_fwd_bwd_ex(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
-                   const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
-                   const float* beta, const float* g, const float* h0, const float* dO,
-                   const float* dhT, float* o, float* hT, int32_t grad_dtype, void* dq, void* dk,
-                   void* dv, float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+int fwd_bwd_entry(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                  const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
+                  const float* beta, const float* g, const float* h0, const float* dO,
+                  const float* dhT, float* o, float* hT, int32_t grad_dtype, void* dq, void* dk,
+                  void* dv, float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
+                  void* stream, bool native) {
   int rc = gdn::check_shape(shape);
   if (rc != GDN_OK) return rc;
+  if (native && shape->d_k != 128) return GDN_ERR_UNSUPPORTED;
   if (grad_dtype != GDN_F32 && grad_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host) return GDN_ERR_INVALID_ARG;
+  if (n_seqs < 0 || !cu_seqlens_dev) return GDN_ERR_INVALID_ARG;
+  if (n_seqs > 0 && (!hT || !dh0)) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, h0, dO, dhT, o, hT, dq, dk, dv, dbeta, dg, dh0}))
+    return GDN_ERR_INVALID_ARG;
+  std::vector<int32_t> cu_buf;
+  if ((rc = host_cu(cu_seqlens_dev, cu_seqlens_host, n_seqs, static_cast<hipStream_t>(stream),
+                    cu_buf, &cu_seqlens_host)) != GDN_OK)
+    return rc;
   gdn::Counts cnt;
   if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
   if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o || !dO || !dq || !dk || !dv || !dbeta ||
                     !dg))
-    return GDN_ERR_INVALID_ARG;
-  if (n_seqs > 0 && (!hT || !dh0)) return GDN_ERR_INVALID_ARG;
-  if (!gdn::aligned16({q, k, v, beta, g, h0, dO, dhT, o, hT, dq, dk, dv, dbeta, dg, dh0}))
     return GDN_ERR_INVALID_ARG;
   const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_FWD_BWD);
   if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
@@ -3828,7 +3925,48 @@ int gdn_fwd_bwd_ex(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_s
   const int bf16 = grad_dtype == GDN_BF16 ? 1 : 0;
   return dispatch(shape, [&]<int D, int C, typename TIn>() {
     return launch_fwd_bwd<D, C, TIn>(shape, n_seqs, cnt, L, cu_seqlens_dev, q, k, v, beta, g, h0,
-                                     dO, dhT, o, hT, dq, dk, dv, bf16, dbeta, dg, dh0, w, st);
+                                     dO, dhT, o, hT, dq, dk, dv, bf16, dbeta, dg, dh0, w, st,
+                                     native);
+  });
+}
+}  // namespace
+
+extern "C" {
+
+int gdn_fwd_bwd_ex(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                   const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v,
+                   const float* beta, const float* g, const float* h0, const float* dO,
+                   const float* dhT, float* o, float* hT, int32_t grad_dtype, void* dq, void* dk,
+                   void* dv, float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
+                   void* stream) {
+  return fwd_bwd_entry(shape, n_seqs, cu_seqlens_dev, cu_seqlens_host, q, k, v, beta, g, h0, dO,
+                       dhT, o, hT, grad_dtype, dq, dk, dv, dbeta, dg, dh0, ws, ws_bytes, stream,
+                       false);
+}
+
+int gdn_fwd_bwd_chunked(const gdn_shape_t* shape, int32_t n_seqs, const int32_t* cu_seqlens_dev,
+                        const int32_t* cu_seqlens_host, const void* q, const void* k,
+                        const void* v, const float* beta, const float* g, const float* h0,
+                        const float* dO, const float* dhT, float* o, float* hT, float* dq,
+                        float* dk, float* dv, float* dbeta, float* dg, float* dh0, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return fwd_bwd_entry(shape, n_seqs, cu_seqlens_dev, cu_seqlens_host, q, k, v, beta, g, h0, dO,
+                       dhT, o, hT, GDN_F32, dq, dk, dv, dbeta, dg, dh0, ws, ws_bytes, stream, true);
+}
+
+int gdn_decode_step_native(const gdn_shape_t* shape, int32_t n_seqs, const void* q, const void* k,
+                           const void* v, const float* beta, const float* g, float* S, float* o,
+                           void* stream) {
+  int rc = gdn::check_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (n_seqs < 0) return GDN_ERR_INVALID_ARG;
+  if (n_seqs > 0 && (!q || !k || !v || !beta || !g || !S || !o)) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, S, o})) return GDN_ERR_INVALID_ARG;
+  if (n_seqs > 65535) return GDN_ERR_UNSUPPORTED;  // grid.x
+  if (n_seqs == 0) return GDN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(shape, [&]<int D, int C, typename TIn>() {
+    return launch_decode_native<D, C, TIn>(shape, n_seqs, q, k, v, beta, g, S, o, st);
   });
 }
 
@@ -3848,11 +3986,15 @@ int gdn_prefill_chunked(const gdn_shape_t* shape, int32_t n_seqs, const int32_t*
   int rc = gdn::check_shape(shape);
   if (rc != GDN_OK) return rc;
   if (shape->d_k != 128) return GDN_ERR_UNSUPPORTED;
-  if (n_seqs < 0 || !cu_seqlens_dev || !cu_seqlens_host) return GDN_ERR_INVALID_ARG;
+  if (n_seqs < 0 || !cu_seqlens_dev) return GDN_ERR_INVALID_ARG;
+  if (!gdn::aligned16({q, k, v, beta, g, h0, o, hT})) return GDN_ERR_INVALID_ARG;
+  std::vector<int32_t> cu_buf;
+  if ((rc = host_cu(cu_seqlens_dev, cu_seqlens_host, n_seqs, static_cast<hipStream_t>(stream),
+                    cu_buf, &cu_seqlens_host)) != GDN_OK)
+    return rc;
   gdn::Counts cnt;
   if ((rc = gdn::count_chunks(cu_seqlens_host, n_seqs, shape->C, &cnt)) != GDN_OK) return rc;
   if (cnt.T > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
-  if (!gdn::aligned16({q, k, v, beta, g, h0, o, hT})) return GDN_ERR_INVALID_ARG;
   const gdn::Layout L = gdn::layout(shape, n_seqs, cnt.T, GDN_OP_PREFILL_CHUNKED);
   if (!ws || ws_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (n_seqs == 0) return GDN_OK;

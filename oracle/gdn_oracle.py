@@ -9,10 +9,9 @@ What is computed
 The layer is Gated DeltaNet (GDN).  The IsoExec pages name it (agentlenshq.com
 write-up "IsoExec: SkyRLにおけるトレーナーと推論のミスマッチを解消する",
 section "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet") but do not write
-its equations.  We take the gated delta rule as published with the
-architecture (Yang, Kautz, Hatamizadeh, "Gated Delta Networks: Improving Mamba2
-with Delta Rule", ICLR 2025): per value head, with the state S a d_v x d_k
-matrix,
+its equations.  The definition used here is the gated delta rule in the form
+in which the problem this library solves is stated: per value head, with the
+state S a d_v x d_k matrix,
 
     S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
     o_t = S_t q_t,
@@ -22,7 +21,7 @@ section of the write-up; daily.dev digest, Q&A "What is chunkwise-parallel
 recurrent (CPR)") is a schedule for evaluating exactly this function, so the
 oracle is the plain definition, evaluated token by token in fp64.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * the state is stored [d_k][d_v] (d_v fastest), i.e. the transpose of S;
   * g is log(alpha); beta and g are per value head;
   * value head h reads query/key head h // (H_v / H_qk) (contiguous groups);

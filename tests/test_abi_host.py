@@ -242,3 +242,22 @@ def test_no_alloc_decode_validation():
     big = good_shape(H_qk=128, H_v=1024)
     assert L.gdn_decode_step_noalloc(ctypes.byref(big), 1, a, a, a, a, a, ctypes.byref(cache),
                                      None, a, None) == B.GDN_ERR_WORKSPACE
+
+
+def test_native_mixed_entry_points_validation():
+    """The baseline's trainer step runs at d = 128 only; its decode step checks
+    pointers before any launch."""
+    L = B.lib()
+    a = ctypes.c_void_p(16)
+    cu = (ctypes.c_int32 * 2)(0, 10)
+    s16 = good_shape(d_k=16, d_v=16, C=16)
+    args = lambda s: (ctypes.byref(s), 1, a, cu, a, a, a, a, a, None, a, None, a, a, a, a, a, a,
+                      a, a, a, 1 << 40, None)
+    assert L.gdn_fwd_bwd_chunked(*args(s16)) == B.GDN_ERR_UNSUPPORTED
+    s = good_shape()
+    assert L.gdn_fwd_bwd_chunked(*(args(s)[:-3] + (a, 8, None))) == B.GDN_ERR_WORKSPACE
+    assert L.gdn_decode_step_native(ctypes.byref(s), 2, a, a, a, a, a, None, a, None) == \
+        B.GDN_ERR_INVALID_ARG
+    assert L.gdn_decode_step_native(ctypes.byref(s), 2, a, a, ctypes.c_void_p(20), a, a, a, a,
+                                    None) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_decode_step_native(ctypes.byref(s), 0, a, a, a, a, a, a, a, None) == B.GDN_OK

@@ -13,9 +13,14 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 # fp32 inputs: the 1e-5 max-abs bar holds as stated at d = 16 (the tiny fp32
-# configuration).  At d = 128 the gradients are O(10) and every one is an fp32
-# sum of hundreds of O(1) products, so fp32 rounding alone reaches ~1e-6 of the
-# gradient's scale; there the bar is 1e-5 relative to max|oracle gradient|.
+# configuration).  At d = 128 the gradients reach |g| ~ 30 and each element is
+# a chain of fixed-order fp32 sums (over the chunk's 64 rows, the 128 state
+# entries and the chunks of the reverse scan), so rounding alone gives an error
+# of about u * sqrt(n) per sum (u = 2^-24 = 6e-8, n ~ 200: ~1e-6 of the
+# gradient's scale).  The bar there is REL[k] * max(1, max|oracle gradient k|):
+# 2e-6 for most gradients, 4e-6 for dg, whose reverse running sum over the
+# whole sequence chains one more sum of up to T terms.
+REL = {"dq": 2e-6, "dk": 2e-6, "dv": 2e-6, "dbeta": 2e-6, "dg": 4e-6, "dh0": 2e-6}
 GRADS = ["dq", "dk", "dv", "dbeta", "dg", "dh0"]
 
 
@@ -57,7 +62,7 @@ def compare(inp, r, tol, dhT=None, seqs=None, hv=None, rows=None, scale=1.0, rel
             else:
                 got = got[:, hv]
         worst[k] = maxabs(got, want)
-        bars[k] = tol * max(1.0, float(np.max(np.abs(want)))) if relative else tol
+        bars[k] = REL[k] * max(1.0, float(np.max(np.abs(want)))) if relative else tol
     say("  max|grad-oracle|: " + " ".join(f"{k}={v:.2e}(bar {bars[k]:.1e})"
                                            for k, v in worst.items()))
     for k, v in worst.items():
@@ -152,3 +157,28 @@ def test_fwd_bwd_bf16_gradient_outputs(dtype, lens, d, Hq, Hv):
         err = np.abs(got - ref[k])
         say(f"  {k}: max err {err.max():.2e}, max err / bar {(err / bar).max():.2f}")
         assert np.all(err <= bar), k
+
+
+@pytest.mark.parametrize("dtype,lens,d,Hq,Hv", [
+    ("bf16", [150, 64, 1, 77, 0], 128, 2, 4),
+    ("f32", [130, 64], 128, 1, 2),
+])
+def test_native_mixed_fwd_bwd_parity(dtype, lens, d, Hq, Hv):
+    """gdn_fwd_bwd_chunked (the native-mixed baseline's trainer step: forward
+    outputs from the chunk form) computes the same function: o, hT and every
+    gradient against the oracle, with partial last chunks and an empty
+    sequence."""
+    say(f"case: native-mixed fwd_bwd {dtype} d{d} lens={lens} H {Hq}/{Hv}")
+    inp = make_inputs(lens, Hq, Hv, d, dtype, seed=35, h0="normal", with_do=True)
+    gen = torch.Generator().manual_seed(98)
+    dhT = torch.randn(len(lens), Hv, d, d, generator=gen)
+    shape = shape_for(inp)
+    dd = to_dev(inp)
+    r = B.gdn_fwd_bwd_chunked(shape, dd["q"], dd["k"], dd["v"], dd["beta"], dd["g"],
+                              dd["cu_seqlens"], dd["do"], h0=dd["h0"], dhT=dhT.cuda())
+    from gdn_helpers import oracle_fwd
+    ro, rh = oracle_fwd(inp)
+    e_o, e_h = maxabs(r["o"], ro), maxabs(r["hT"], rh)
+    say(f"  forward: max|o-oracle|={e_o:.2e} max|hT-oracle|={e_h:.2e}")
+    assert e_o <= TOL[dtype] and e_h <= TOL[dtype]
+    compare(inp, r, TOL[dtype], dhT=dhT, relative=(dtype == "f32" and d == 128))

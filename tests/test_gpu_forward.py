@@ -590,3 +590,50 @@ def test_host_copy_of_cu_seqlens_same_bits():
                        h0=d["h0"], cu_seqlens_host=cu_h)
     for key in r1:
         assert bit_equal(r1[key], r2[key]), key
+    say("  cu_seqlens_host NULL: the library copies the device copy itself")
+    o3, h3 = B.gdn_prefill(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"],
+                           h0=d["h0"], cu_seqlens_host=False)
+    assert bit_equal(o1, o3) and bit_equal(h1, h3)
+    r3 = B.gdn_fwd_bwd(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], dO,
+                       h0=d["h0"], cu_seqlens_host=False)
+    for key in r1:
+        assert bit_equal(r1[key], r3[key]), key
+    oc1, hc1 = B.gdn_prefill_chunked(shape, d["q"], d["k"], d["v"], d["beta"], d["g"],
+                                     d["cu_seqlens"], h0=d["h0"])
+    oc2, hc2 = B.gdn_prefill_chunked(shape, d["q"], d["k"], d["v"], d["beta"], d["g"],
+                                     d["cu_seqlens"], h0=d["h0"], cu_seqlens_host=False)
+    assert bit_equal(oc1, oc2) and bit_equal(hc1, hc2)
+    c1 = B.Cache(shape, 4, "cuda", torch.bfloat16)
+    B.gdn_prefill(shape, d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"],
+                  h0=d["h0"], cache=c1)
+    c2 = c1.clone()
+    nx = make_inputs([10, 70, 0, 5], 2, 4, 128, "bf16", seed=63)
+    nd = to_dev(nx, "cuda")
+    pos = [int(x) for x in c1.pos[:, 0].cpu()]
+    x1 = B.gdn_prefill_continue(shape, nd["q"], nd["k"], nd["v"], nd["beta"], nd["g"],
+                                nd["cu_seqlens"], c1, pos)
+    x2 = B.gdn_prefill_continue(shape, nd["q"], nd["k"], nd["v"], nd["beta"], nd["g"],
+                                nd["cu_seqlens"], c2, pos, cu_seqlens_host=False)
+    assert bit_equal(x1[0], x2[0]) and bit_equal(x1[1], x2[1])
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hv", [("bf16", 128, 2, 4), ("f32", 16, 2, 2)])
+def test_native_mixed_decode_parity(dtype, d, Hq, Hv):
+    """gdn_decode_step_native (the native-mixed baseline's plain recurrent
+    decode, no resync) computes the same function: 100 tokens from a random
+    initial state against the oracle, every output and the final state."""
+    steps, N = 100, 3
+    say(f"case: native-mixed decode {dtype} d{d}, {N} seqs x {steps} tokens")
+    inp = make_inputs([steps] * N, Hq, Hv, d, dtype, seed=45, h0="normal")
+    shape = shape_for(inp)
+    S = inp["h0"].cuda().clone()
+    outs = []
+    for s in range(steps):
+        idx = torch.tensor([n * steps + s for n in range(N)])
+        t = {k: inp[k][idx].cuda().contiguous() for k in ["q", "k", "v", "beta", "g"]}
+        outs.append(B.gdn_decode_step_native(shape, t["q"], t["k"], t["v"], t["beta"], t["g"], S))
+    od = torch.stack(outs, 1).reshape(N * steps, Hv, d)  # [N, steps] -> packed rows
+    ro, rh = oracle_fwd(inp)
+    e_o, e_h = maxabs(od, ro), maxabs(S, rh)
+    say(f"  max|o-oracle|={e_o:.2e} max|S-oracle|={e_h:.2e} (tol {TOL[dtype]})")
+    assert e_o <= TOL[dtype] and e_h <= TOL[dtype]

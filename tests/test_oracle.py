@@ -263,3 +263,50 @@ def test_dv_exact_by_linearity_and_zero_for_beta_zero():
     assert abs(np.sum(dv * e) - np.sum(do * (o1 - o0))) < 1e-10
     dv0 = recurrent_bwd(q, k, v, 0 * beta, g, cu, do, h0=h0)["dv"]
     assert np.all(dv0 == 0.0)
+
+
+# ---------------------------------------------------------------- normalisation pins
+
+def test_l2norm_unit_length_for_large_vectors_and_below_one_always():
+    # |x|^2 >> eps: the result has length 1 up to eps / (2 |x|^2); eps > 0 added
+    # inside the root makes every length strictly below 1.
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((50, 7)) * rng.uniform(0.5, 50.0, (50, 1))
+    n = np.linalg.norm(l2norm_rows(x), axis=-1)
+    sq = np.sum(x * x, axis=-1)
+    assert np.all(n < 1.0)
+    assert np.all(np.abs(1.0 - n) <= 1e-6 / (2 * sq) + 1e-15)
+
+
+def test_l2norm_keeps_direction_and_is_scale_invariant_up_to_eps():
+    # positive multiple of x; l2norm(c x) differs from l2norm(x) only through
+    # eps, by at most |1/c^2 - 1| eps / (2 |x|^2) relative, and grows with c
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((20, 5))
+    y = l2norm_rows(x)
+    ratio = y / x
+    assert np.all(ratio > 0) and np.allclose(ratio, ratio[:, :1], rtol=1e-14, atol=0)
+    sq = np.sum(x * x, axis=-1, keepdims=True)
+    for c in [0.5, 3.0, 1e3]:
+        yc = l2norm_rows(c * x)
+        bound = abs(1.0 / c ** 2 - 1.0) * 1e-6 / (2 * sq) + 1e-14
+        assert np.all(np.abs(yc - y) <= bound * np.abs(y))
+        if c > 1:
+            assert np.all(np.linalg.norm(yc, axis=-1) > np.linalg.norm(y, axis=-1))
+
+
+def test_l2norm_small_vectors_scale_by_inverse_root_eps():
+    # |x|^2 << eps: the result is x / sqrt(eps) (1e3 x), not a unit vector
+    x = np.array([[3e-9, -4e-9, 1e-9]])
+    y = l2norm_rows(x)
+    assert np.allclose(y, 1e3 * x, rtol=1e-10, atol=0)
+
+
+def test_l2norm_exact_where_the_root_is_exact():
+    # |x|^2 + eps = 1/4 exactly gives y = 2 x; rows are normalised separately
+    a = np.sqrt(0.25 - 1e-6)
+    x = np.array([[a, 0.0, 0.0], [0.0, 0.0, -a], [3.0, 4.0, 0.0]])
+    y = l2norm_rows(x)
+    assert np.allclose(y[0], [2 * a, 0, 0], rtol=1e-15, atol=0)
+    assert np.allclose(y[1], [0, 0, -2 * a], rtol=1e-15, atol=0)
+    assert abs(np.linalg.norm(y[2]) - 5.0 / np.sqrt(25.0 + 1e-6)) < 1e-15
