@@ -140,7 +140,7 @@ def wall_then_profile(step, n_wall, n_prof, names, B, torch):
     for _ in range(n_wall):
         step()
     torch.cuda.synchronize()
-    ms_step = 1e3 * (time.perf_counter() - t0) / n_wall
+    ms_step = 1e3 * (time.perf_counter() - t0) / n_wall if n_wall else 0.0
     B.profile_read("")  # drop anything recorded so far
     B.profile_enable(True)
     for _ in range(n_prof):
@@ -169,10 +169,13 @@ def bench_prefill(args, B, torch, make_inputs):
 
     for _ in range(args.warmup):
         step()
-    # the timed region itself carries the events around every launch, so the
-    # kernel durations behind the roofline are those of the timed steps
+    # the timed steps carry events around the roofline kernel's launches only
+    # (events around all four launches of a step add about 3% to it), so its
+    # duration is that of the timed steps; the other kernels' split comes from
+    # a separate pass with events around every launch
     torch.cuda.synchronize()
     B.profile_read("")  # drop anything recorded so far
+    B.profile_filter("k_rec")
     B.profile_enable(True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -180,10 +183,12 @@ def bench_prefill(args, B, torch, make_inputs):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     B.profile_enable(False)
-    per_kernel = {}
-    for name in ["k_plan", "k_prep", "k_wy", "k_scan", "k_rec"]:
-        ms, n = B.profile_read(name)
-        per_kernel[name] = dict(avg_us=1e3 * ms / max(n, 1), launches=n)
+    B.profile_filter("")
+    rec_ms, rec_n = B.profile_read("k_rec")
+    _, prof = wall_then_profile(step, 0, min(args.steps, 10),
+                                ["k_plan", "k_prep", "k_wy", "k_scan"], B, torch)
+    per_kernel = {name: dict(avg_us=1e3 * ms / max(n, 1), launches=n) for name, (ms, n) in prof.items()}
+    per_kernel["k_rec"] = dict(avg_us=1e3 * rec_ms / max(rec_n, 1), launches=rec_n)
     ms_step = 1e3 * (t1 - t0) / args.steps
     tokens = T
     rec_us = per_kernel["k_rec"]["avg_us"]

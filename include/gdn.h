@@ -303,6 +303,10 @@ int gdn_decode_step_native(const gdn_shape_t* shape, int32_t n_seqs, const void*
  * Thread-safe; records from concurrent calls are merged.
  */
 int gdn_profile_enable(int on);
+/* While timing is enabled, bracket only the launches whose kernel name
+ * contains `kernel` (NULL or "" = all, the default): fewer events in a timed
+ * loop.  Host only; GDN_OK. */
+int gdn_profile_filter(const char* kernel);
 int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches);
 
 /* Identifier of the compiled arithmetic contract (chunk lengths, epsilon,

@@ -26,7 +26,7 @@ EXPORTS = ["gdn_workspace_bytes", "gdn_cache_init", "gdn_prefill", "gdn_decode_s
            "gdn_fwd_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_contract_id",
            "gdn_contract_check", "gdn_error_string", "gdn_prefill_chunked",
            "gdn_prefill_continue", "gdn_fwd_bwd_ex", "gdn_decode_step_noalloc",
-           "gdn_fwd_bwd_chunked", "gdn_decode_step_native"]
+           "gdn_fwd_bwd_chunked", "gdn_decode_step_native", "gdn_profile_filter"]
 
 
 class Shape(ctypes.Structure):
@@ -85,6 +85,8 @@ def lib():
         L.gdn_decode_step_native.restype = ctypes.c_int
         L.gdn_profile_enable.argtypes = [ctypes.c_int]
         L.gdn_profile_enable.restype = ctypes.c_int
+        L.gdn_profile_filter.argtypes = [ctypes.c_char_p]
+        L.gdn_profile_filter.restype = ctypes.c_int
         L.gdn_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64)]
         L.gdn_profile_read.restype = ctypes.c_int
@@ -131,6 +133,11 @@ def workspace_bytes(shape, n_seqs, total_tokens, op):
 
 def profile_enable(on=True):
     _check(lib().gdn_profile_enable(int(bool(on))), "gdn_profile_enable")
+
+
+def profile_filter(kernel=""):
+    """Only launches whose kernel name contains `kernel` are timed ("" = all)."""
+    _check(lib().gdn_profile_filter(kernel.encode() if kernel else None), "gdn_profile_filter")
 
 
 def profile_read(kernel=""):

@@ -3154,6 +3154,7 @@ struct ProfRec {
 struct Profiler {
   std::mutex mu;
   bool on = false;
+  std::string filter;  // only launches whose name contains it (empty: all)
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
   hipEvent_t get() {
@@ -3179,6 +3180,7 @@ class Timed {
     Profiler& p = prof();
     std::lock_guard<std::mutex> g(p.mu);
     if (!p.on) return;
+    if (!p.filter.empty() && std::strstr(name, p.filter.c_str()) == nullptr) return;
     rec_.name = name;
     rec_.a = p.get();
     rec_.b = p.get();
@@ -4010,6 +4012,13 @@ int gdn_profile_enable(int on) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
   p.on = on != 0;
+  return GDN_OK;
+}
+
+int gdn_profile_filter(const char* kernel) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.filter = kernel ? kernel : "";
   return GDN_OK;
 }
 
