@@ -637,3 +637,34 @@ def test_native_mixed_decode_parity(dtype, d, Hq, Hv):
     e_o, e_h = maxabs(od, ro), maxabs(S, rh)
     say(f"  max|o-oracle|={e_o:.2e} max|S-oracle|={e_h:.2e} (tol {TOL[dtype]})")
     assert e_o <= TOL[dtype] and e_h <= TOL[dtype]
+
+
+def test_decode_3000_sequences_across_a_chunk_edge():
+    """A large decode batch (3000 sequences, grid.x = 3000): prefill 60 tokens,
+    decode 10 one at a time (every sequence resyncs after its 64th token),
+    equal to one 70-token prefill bit for bit; the no-allocation entry point
+    (twelve resync groups of the fixed scratch at this shape) gives the same
+    bits as gdn_decode_step."""
+    N, pre, total = 3000, 60, 70
+    say(f"case: decode {N} sequences, prefill {pre} + decode {total - pre}")
+    inp = make_inputs([total] * N, 1, 2, 128, "bf16", seed=81, h0="normal")
+    o_full, h_full, _ = run_prefill(inp)
+    shape = shape_for(inp)
+    first = dict(inp)
+    idx = torch.cat([torch.arange(n * total, n * total + pre) for n in range(N)])
+    for key in ["q", "k", "v", "beta", "g"]:
+        first[key] = inp[key][idx].contiguous()
+    first["cu_seqlens"] = torch.arange(0, (N + 1) * pre, pre, dtype=torch.int32)
+    _, _, cache = run_prefill(first, cache=True)
+    c2 = cache.clone()
+    od = decode_tokens(inp, cache, shape, pre, total - pre)
+    rows = torch.cat([torch.arange(n * total + pre, (n + 1) * total) for n in range(N)])
+    assert bit_equal(od.transpose(0, 1).reshape(-1, 2, 128), o_full[rows.cuda()])
+    assert bit_equal(cache.S_run, h_full)
+    cu = inp["cu_seqlens"].tolist()
+    for s in range(total - pre):
+        ix = torch.tensor([cu[n] + pre + s for n in range(N)])
+        t = {k: inp[k][ix].cuda().contiguous() for k in ["q", "k", "v", "beta", "g"]}
+        on = B.gdn_decode_step_noalloc(shape, t["q"], t["k"], t["v"], t["beta"], t["g"], c2)
+        assert bit_equal(on, od[s]), f"no-alloc step {s}"
+    assert bit_equal(c2.S_run, cache.S_run) and bit_equal(c2.S_chunk, cache.S_chunk)
