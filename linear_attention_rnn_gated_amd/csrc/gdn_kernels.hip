@@ -265,6 +265,17 @@ __device__ __forceinline__ const float* key_rows(const float* base, int64_t T, i
 // a full chunk executes the same operations in every mode.
 enum Mode { kFull = 0, kResync = 1, kAll = 2 };
 
+// Chunk-factor blocks, grid (8 G ceil(items / 8), H_qk): the G value heads of
+// a q/k group read the same keys, so the blocks of one group and item go out
+// 8 apart and land on the same XCD (blocks are dispatched round-robin over the
+// 8 XCDs) at about the same time; the later ones find the keys in its L2.
+// Items past the last one exit in the kernels' range checks.
+__device__ __forceinline__ void wy_item(int G, int64_t& item, int& h) {
+  const int64_t x = blockIdx.x;
+  item = (x / (8 * G)) * 8 + x % 8;
+  h = static_cast<int>(blockIdx.y) * G + static_cast<int>((x / 8) % G);
+}
+
 template <int D, int C, typename TIn, int MODE>
 __global__ __launch_bounds__(256) void k_wy(ChunkIO io) {
   constexpr bool RESYNC = MODE == kResync;
@@ -274,22 +285,25 @@ __global__ __launch_bounds__(256) void k_wy(ChunkIO io) {
   __shared__ float sY[C][2 * D];  // column t: W (t < D) or U (t >= D); owned by thread t
   __shared__ float sB[C], sG[C], sBG[C];
   const int tid = threadIdx.x;
-  const int h = blockIdx.y;
+  int64_t item;
+  int h;
+  wy_item(io.H_v / io.H_qk, item, h);
   const int hq = h / (io.H_v / io.H_qk);
   int64_t tok0, slot;
   int L = C;
   if (MODE == kResync) {
-    const int n = blockIdx.x;
+    if (item >= io.N) return;
+    const int n = static_cast<int>(item);
     if (io.pos[static_cast<int64_t>(n) * io.H_v + h] != 0) return;
     tok0 = static_cast<int64_t>(n) * C;
     slot = n;
   } else if (MODE == kFull) {
-    slot = blockIdx.x;
-    const int n = find_seq(io.cu_full, io.N, slot);
+    slot = item;
     if (slot >= io.cu_full[io.N]) return;
+    const int n = find_seq(io.cu_full, io.N, slot);
     tok0 = static_cast<int64_t>(io.cu[n]) + static_cast<int64_t>(slot - io.cu_full[n]) * C;
   } else {
-    slot = blockIdx.x;
+    slot = item;
     if (slot >= io.cu_full[io.N]) return;  // cu_full holds the chunk prefix in this mode
     const int n = find_seq(io.cu_full, io.N, slot);
     tok0 = static_cast<int64_t>(io.cu[n]) + static_cast<int64_t>(slot - io.cu_full[n]) * C;
@@ -520,9 +534,11 @@ __device__ __forceinline__ int64_t xcd_block(int64_t nb8) {
 // B, part 2 on the matrix cores (d = 128, C = 64): the chunk-state scan
 //   Delta = U - W S^T,   S' = gam_C S + sum_p lam_p Delta_p k_p^T
 // (gam_C = exp(G_C), lam_p = exp(G_C - G_p)), sequential over the chunks of a
-// sequence.  A block of 4 waves owns 64 columns j of d_v of one (sequence,
-// head); wave w holds S^T (rows i of d_k, its 16 columns j) as eight 16 x 16
-// accumulator tiles.  In that layout accumulator register r of lane group g
+// sequence.  A block of NW waves (4 or 8) owns 16 NW columns j of d_v of one
+// (sequence, head); wave w holds S^T (rows i of d_k, its 16 columns j) as
+// eight 16 x 16 accumulator tiles.  Every column is computed the same way
+// whatever the block width; eight waves stage each chunk's W and K once for
+// the whole head.  In that layout accumulator register r of lane group g
 // is the B operand of the k-step in which lane group g supplies
 // k = 16 b + 4 g + r, so both contractions take their B operand straight from
 // registers: Delta (k = i) from the state, S' (k = p) from lam * Delta.
@@ -531,27 +547,37 @@ __device__ __forceinline__ int64_t xcd_block(int64_t nb8) {
 // r = 0..3).  W and K (rows p) of a chunk sit in LDS; the next
 // chunk's W, K, U and G are fetched into registers while the current chunk
 // computes.  Decode resync runs this same kernel on the chunk buffers.
-template <int C, int MODE>
-__global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, int64_t nb8) {
-  constexpr int D = 128, WS = D + 4, NQ = C * D / 4 / 256;  // float4 per thread
-  static_assert(C == 64 && NQ == 8, "tiling assumes C = 64, D = 128");
+template <int C, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4))) void k_scan_mfma(ScanIO io,
+                                                                                            int64_t nblocks,
+                                                                                            int64_t nb8) {
+  constexpr int D = 128, WS = D + 4, NQ = C * D / 4 / (64 * NW);  // float4 of W (of K) per thread
+  constexpr int NB = D / (16 * NW);                                // blocks per (sequence, head)
+  static_assert(C == 64 && (NW == 4 || NW == 8), "tiling assumes C = 64, D = 128");
   constexpr bool RESYNC = MODE == kResync;
-  __shared__ __attribute__((aligned(16))) float sW[C * WS];  // W[p][i]
-  __shared__ __attribute__((aligned(16))) float sK[C * WS];  // K[p][i]
-  __shared__ float sLam[C];
+  // W, K and lam of chunk c sit in buffer c % NBUF (two buffers: the next
+  // chunk's operands go in while this chunk's are read; resync runs one step)
+  constexpr int NBUF = RESYNC ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) float sW[NBUF][C * WS];  // W[p][i]
+  __shared__ __attribute__((aligned(16))) float sK[NBUF][C * WS];  // K[p][i]
+  __shared__ float sLam[NBUF][C];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // ordered launches keep the dispatch order (consecutive blocks go to
-  // consecutive XCDs), so the longest sequences start first on every XCD
-  const int64_t vb = io.order ? static_cast<int64_t>(blockIdx.x) : xcd_block(nb8);
+  // ordered launches keep the dispatch order, so the longest sequences start
+  // first on every XCD; virtual blocks 2 p and 2 p + 1 (the two halves of a
+  // head, or two heads of a q/k group) go out 8 blocks apart, i.e. to the same
+  // XCD at about the same time, and share their W and K (K) through its L2
+  // (the grid is then a multiple of 16 blocks)
+  const int64_t bx = blockIdx.x;
+  const int64_t vb = io.order ? ((bx / 16) * 8 + bx % 8) * 2 + (bx / 8) % 2 : xcd_block(nb8);
   if (vb >= nblocks) return;
-  const int half = static_cast<int>(vb % 2);
-  const int h = static_cast<int>((vb / 2) % io.H_v);
-  int n = static_cast<int>(vb / (2 * io.H_v));
+  const int half = static_cast<int>(vb % NB);
+  const int h = static_cast<int>((vb / NB) % io.H_v);
+  int n = static_cast<int>(vb / (NB * io.H_v));
   if (n >= io.N) return;
   if (io.order) n = io.order[n];  // longest sequences first: their chains start earliest
   const int hq = h / (io.H_v / io.H_qk);
-  const int j = 64 * half + 16 * w + l16;  // this lane's column of d_v
+  const int j = 16 * NW * half + 16 * w + l16;  // this lane's column of d_v
   const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
   const int64_t nh = static_cast<int64_t>(n) * io.H_v + h;
 
@@ -571,21 +597,23 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
   }
   // buffer offsets (bytes): lane part in a VGPR, wave-uniform part in an SGPR
   const uint32_t fj = 4u * static_cast<uint32_t>(4 * g * D + j);  // (row 4 g, column j) of [.][D]
-  const int r0 = 8 * (tid >> 5), cq = tid & 31;  // this thread's rows r0 .. r0 + 7, column quad cq
+  const int r0 = NQ * (tid >> 5), cq = tid & 31;  // this thread's rows r0 .. r0 + NQ - 1, column quad cq
   const uint32_t fq = 4u * static_cast<uint32_t>(r0 * D + 4 * cq);
   const uint32_t kst = RESYNC ? static_cast<uint32_t>(io.H_qk) * D * 4u : 2 * D * 4u;  // key row stride
   const uint32_t fk = static_cast<uint32_t>(r0) * kst + 16u * cq;
 
-  // one chunk step's operands: W and K rows p = r0 + m, column quad cq; U in
-  // accumulator layout (p = 16 pb + 4 g + r, j); G
-  struct Ops {
-    float4 w[NQ], k[NQ];
-    float u[4][4];
-    float gv, glast;
-  };
-  // The loads come in NQ parts (part m: W and K rows r0 + m, two of the U
-  // values, and G with part 0) so that they can be issued between the
-  // matrix-core products of a chunk step.
+  // One chunk step's operands: W and K rows p = r0 + m, column quad cq; U in
+  // accumulator layout (p = 16 pb + 4 g + r, j); G.  Chunk c + 1's K is
+  // loaded at the start of chunk c's Delta products and goes to LDS when they
+  // end; chunk c + 2's W and G are loaded at the start of chunk c's S'
+  // products and go to LDS (W negated, with lam) when they end, i.e. at the
+  // start of chunk c + 1.  Each prefetch thus has a whole phase to arrive,
+  // only one of them is held in registers at a time, and with the two LDS
+  // buffers one barrier per chunk orders every write after the last read of
+  // its buffer and before the first read of its data.  Past the last chunk
+  // the prefetches reload the last chunk's operands into the spare buffer,
+  // which nothing reads: the loop body has no branches (a branch costs an
+  // instruction refetch that one wave per SIMD cannot hide).
   struct OpRes {
     brsrc_t rk, rw, ru;
     int64_t sh;
@@ -601,24 +629,41 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
     r.ru = make_rsrc(io.U + r.sh * CD, C * D * 4u);
     return r;
   };
-  auto load_part = [&](Ops& o, const OpRes& rs, int m) {
-    o.w[m] = ldbuf4(rs.rw, fq, static_cast<uint32_t>(m * D * 4));
-    o.k[m] = ldbuf4(rs.rk, fk + static_cast<uint32_t>(m) * kst, 0u);
+  float4 pw[NQ], pk[NQ];
+  float un[4][4];
+  float gvn = 0.0f, glastn = 0.0f;
+  auto load_w = [&](const OpRes& rs) {  // W rows r0 + m, and G (element lane of every wave)
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) pw[m] = ldbuf4(rs.rw, fq, static_cast<uint32_t>(m * D * 4));
+    gvn = io.G[rs.sh * C + lane];
+    glastn = io.G[rs.sh * C + C - 1];
+  };
+  auto load_k = [&](const OpRes& rs) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) pk[m] = ldbuf4(rs.rk, fk + static_cast<uint32_t>(m) * kst, 0u);
+  };
+  auto load_u = [&](const OpRes& rs, int m) {  // part m of 8: two of the U values
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int pb = m / 2, r = 2 * (m % 2) + e;
-      o.u[pb][r] = ldbuf(rs.ru, fj, static_cast<uint32_t>((16 * pb + r) * D * 4), static_cast<const float*>(nullptr));
-    }
-    if (m == 0) {
-      o.gv = tid < C ? io.G[rs.sh * C + tid] : 0.0f;
-      o.glast = io.G[rs.sh * C + C - 1];
+      un[pb][r] = ldbuf(rs.ru, fj, static_cast<uint32_t>((16 * pb + r) * D * 4), static_cast<const float*>(nullptr));
     }
   };
-  auto load_ops = [&](Ops& o, int64_t c) {
-    const OpRes rs = op_res(c);
+  // W and K go to LDS as loaded (no register transpose: a transpose of the
+  // prefetched quads would make the loads complete before the chunk computes)
+  auto put_w = [&](int b) {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) load_part(o, rs, m);
+    for (int m = 0; m < NQ; ++m) {  // stored negated: Delta adds (-W) S^T
+      const float4 wv = pw[m];
+      *reinterpret_cast<float4*>(&sW[b][(r0 + m) * WS + 4 * cq]) = float4{-wv.x, -wv.y, -wv.z, -wv.w};
+    }
+    sLam[b][lane] = expf(glastn - gvn);  // every wave writes the same row (no branch)
   };
+  auto put_k = [&](int b) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) *reinterpret_cast<float4*>(&sK[b][(r0 + m) * WS + 4 * cq]) = pk[m];
+  };
+  auto buf = [](int64_t c) { return NBUF == 1 ? 0 : static_cast<int>(c & 1); };
 
   // S^T tiles (i = 16 ib + 4 g + r, j)
   v4f st[8];
@@ -639,67 +684,67 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
       for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rd, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
   };
 
-  Ops nx;
-  if (nsteps > 0) load_ops(nx, 0);
+  float glast = 0.0f;  // G at the end of the current chunk
+  if (nsteps > 0) {    // chunk 0's operands to LDS; chunk 1's W and G in flight
+    const OpRes rs = op_res(0);
+    load_w(rs);
+    load_k(rs);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) load_u(rs, m);
+    put_w(0);
+    put_k(0);
+    glast = glastn;
+    if (nsteps > 1) load_w(op_res(1));
+  }
+  __syncthreads();
   for (int64_t c = 0; c < nsteps; ++c) {
     const int64_t fs = fslot0 + c;
-    __syncthreads();  // the previous step's LDS reads are done
-    // W and K go to LDS as loaded (no register transpose: a transpose of the
-    // prefetched quads would make the loads complete before this chunk computes)
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-      const float4 wv = nx.w[m];  // stored negated: Delta adds (-W) S^T
-      *reinterpret_cast<float4*>(sW + (r0 + m) * WS + 4 * cq) = float4{-wv.x, -wv.y, -wv.z, -wv.w};
-      *reinterpret_cast<float4*>(sK + (r0 + m) * WS + 4 * cq) = nx.k[m];
-    }
-    const float glast = nx.glast;
-    if (tid < C) sLam[tid] = expf(glast - nx.gv);
-    float u[4][4];
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) u[pb][r] = nx.u[pb][r];
-    // the next chunk's operands and this chunk's start state (a store) are
-    // issued between the Delta products below, a part per k block
+    const int b = buf(c), nb = buf(c + 1);
     const bool more = c + 1 < nsteps;
-    const OpRes nres = op_res(more ? c + 1 : c);
-    const brsrc_t rst = RESYNC ? make_rsrc(io.W, 0u)  // no chunk-start states in resync
-                               : make_rsrc(io.states + ((slot0 + c) * io.H_v + h) * DD, D * D * 4u);
-    __syncthreads();
     // ---- Delta tiles (p = 16 pb + 4 g + r, j) = U - W S^T, k = i
     // (the four tiles' chains are interleaved; each keeps its own k order)
     v4f dl[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dl[pb][r] = u[pb][r];
-    // A operands (-W) are read from LDS one k block ahead of their use
+      for (int r = 0; r < 4; ++r) dl[pb][r] = un[pb][r];
+    // A operands (-W) are read from LDS one k block ahead of their use; the
+    // first read goes ahead of the writes to the other buffer
     float4 a[2][4];
     auto read_w = [&](float4 (&x)[4], int ib) {
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb)
-        x[pb] = *reinterpret_cast<const float4*>(sW + (16 * pb + l16) * WS + 16 * ib + 4 * g);
+        x[pb] = *reinterpret_cast<const float4*>(&sW[b][(16 * pb + l16) * WS + 16 * ib + 4 * g]);
     };
     read_w(a[0], 0);
+    // chunk c + 1's W and lam (its buffer was last read in chunk c - 1)
+    if (NBUF == 2 || more) put_w(nb);
+    const float glast1 = more ? glastn : glast;
+    // chunk c + 1's K and U, and this chunk's start state (a store), are issued
+    // between the Delta products below
+    const OpRes nres = op_res(more ? c + 1 : c);
+    load_k(nres);
+    const brsrc_t rst = RESYNC ? make_rsrc(io.W, 0u)  // no chunk-start states in resync
+                               : make_rsrc(io.states + ((slot0 + c) * io.H_v + h) * DD, D * D * 4u);
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib) {
       const float4(&x)[4] = a[ib & 1];
       if (ib + 1 < 8) read_w(a[(ib + 1) & 1], ib + 1);
-      if (!RESYNC) {  // rows 16 ib + 4 g + r of the chunk-start state
-#pragma unroll
-        for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rst, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
-      }
-      if (more) load_part(nx, nres, ib);
       __builtin_amdgcn_sched_barrier(0);  // the reads issue before this block's products
+      // each k-step's four products, then a row of the chunk-start state
+      // (rows 16 ib + 4 g + r; dropped in resync), the U loads after the second
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].x, st[ib][0], dl[pb]);
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].y, st[ib][1], dl[pb]);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].z, st[ib][2], dl[pb]);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma4(x[pb].w, st[ib][3], dl[pb]);
-      __builtin_amdgcn_sched_barrier(0);  // at most one k block of reads in flight
+        for (int pb = 0; pb < 4; ++pb) {
+          const float xa = r == 0 ? x[pb].x : r == 1 ? x[pb].y : r == 2 ? x[pb].z : x[pb].w;
+          dl[pb] = mfma4(xa, st[ib][r], dl[pb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (!RESYNC) stbuf(st[ib][r], rst, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+        if (r == 1) load_u(nres, ib);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (MODE == kAll) {
       const brsrc_t rd = make_rsrc(io.Dl + (fs * io.H_v + h) * CD, C * D * 4u);
@@ -708,24 +753,33 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
 #pragma unroll
         for (int r = 0; r < 4; ++r) stbuf(dl[pb][r], rd, fj, static_cast<uint32_t>((16 * pb + r) * D * 4));
     }
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dl[pb][r] = dl[pb][r] * sLam[16 * pb + 4 * g + r];
-    // ---- S'^T tiles (i, j) = gam_C S^T + K^T (lam Delta), k = p
-    const float gam = expf(glast);
-#pragma unroll
-    for (int ib = 0; ib < 8; ++ib) st[ib] = gam * st[ib];
     // A operand K^T (i = 16 (4 h2 + q) + l16, p = 16 pb + 4 g + r), a column
-    // of K, read from LDS one group of four tiles ahead of its use
+    // of K, read from LDS one group of four tiles ahead of its use; the first
+    // read and lam go ahead of the writes to the other buffer
     float ak[2][4][4];
     auto read_k = [&](float (&x)[4][4], int pb, int h2) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[q][r] = sK[(16 * pb + 4 * g + r) * WS + 16 * (4 * h2 + q) + l16];
+        for (int r = 0; r < 4; ++r) x[q][r] = sK[b][(16 * pb + 4 * g + r) * WS + 16 * (4 * h2 + q) + l16];
     };
     read_k(ak[0], 0, 0);
+    float lam[4][4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lam[pb][r] = sLam[b][16 * pb + 4 * g + r];
+    if (NBUF == 2 || more) put_k(nb);  // chunk c + 1's K (its buffer was last read in chunk c - 1)
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dl[pb][r] = dl[pb][r] * lam[pb][r];
+    // ---- S'^T tiles (i, j) = gam_C S^T + K^T (lam Delta), k = p
+    const float gam = expf(glast);
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib) st[ib] = gam * st[ib];
+    // chunk c + 2's W and G are issued ahead of the products
+    load_w(op_res(c + 2 < nsteps ? c + 2 : c));
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
 #pragma unroll
@@ -741,6 +795,8 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanIO io, int64_t nblocks, i
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    glast = glast1;
+    __syncthreads();  // chunk c's buffers are free and chunk c + 1's are written
   }
 
   if (RESYNC) {
@@ -796,17 +852,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int l16 = lane & 15, g = lane >> 4;
-  const int h = blockIdx.y;
+  int64_t item;
+  int h;
+  wy_item(io.H_v / io.H_qk, item, h);
   const int hq = h / (io.H_v / io.H_qk);
   int64_t tok0, slot;
   int L = C;
   if (MODE == kResync) {
-    const int n = blockIdx.x;
+    if (item >= io.N) return;
+    const int n = static_cast<int>(item);
     if (io.pos[static_cast<int64_t>(n) * io.H_v + h] != 0) return;
     tok0 = static_cast<int64_t>(n) * C;
     slot = n;
   } else {
-    slot = blockIdx.x;
+    slot = item;
     if (slot >= io.cu_full[io.N]) return;
     const int n = find_seq(io.cu_full, io.N, slot);
     tok0 = static_cast<int64_t>(io.cu[n]) + static_cast<int64_t>(slot - io.cu_full[n]) * C;
@@ -3213,6 +3272,8 @@ constexpr int scan_tile() { return D == 128 ? kTile128 : D; }
 
 // Blocks of the persistent backward kernels: one per CU.
 constexpr int64_t kPersistentBlocks = 256;
+// Dynamic LDS that leaves room for one 4-wave k_scan_mfma block per CU (160 KB).
+constexpr unsigned kScanSoloLds = 24 * 1024;
 
 // Value heads per k_rec block: as many of the group as fit in 8 waves and
 // divide the group evenly (the group has at most 8 heads).
@@ -3227,7 +3288,8 @@ int rec_heads_per_block(int G) {
 template <int D, int C, typename TIn, int MODE>
 void launch_wy(const ChunkIO& io, int64_t items, int H_v, hipStream_t st) {
   if (items <= 0) return;
-  const dim3 grid(static_cast<unsigned>(items), H_v);
+  const int64_t G = H_v / io.H_qk;
+  const dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8 * G), io.H_qk);
   if constexpr (D == 128)
     hipLaunchKernelGGL((k_wy_mfma<C, TIn, MODE>), grid, dim3(256), 0, st, io);
   else
@@ -3241,10 +3303,20 @@ void launch_scan(const ScanIO& io, int64_t N, int H_v, hipStream_t st) {
   const int64_t blocks = N * H_v * (D / TILE);
   if (blocks <= 0) return;
   if constexpr (D == 128) {  // blocks of 64 columns of d_v
-    const int64_t mblocks = N * H_v * 2;
+    // Half a head per block of 4 waves, one block per CU (extra LDS keeps two
+    // off a CU), while they are no more than the CUs: each chain then has a
+    // SIMD per wave.  Past that, a head per block of 8 waves, which stages
+    // each chunk's W and K once for all 128 columns.
+    const bool wide = N * H_v * 2 > kPersistentBlocks;
+    const int64_t mblocks = N * H_v * (wide ? 1 : 2);
     const int64_t nb8 = (mblocks + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_scan_mfma<C, MODE>), dim3(static_cast<unsigned>(nb8)), dim3(256), 0, st,
-                       io, mblocks, nb8);
+    const int64_t grid = io.order ? (mblocks + 15) / 16 * 16 : nb8;
+    if (wide)
+      hipLaunchKernelGGL((k_scan_mfma<C, MODE, 8>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, st,
+                         io, mblocks, nb8);
+    else
+      hipLaunchKernelGGL((k_scan_mfma<C, MODE, 4>), dim3(static_cast<unsigned>(grid)), dim3(256),
+                         kScanSoloLds, st, io, mblocks, nb8);
   } else {
     hipLaunchKernelGGL((k_scan<D, C, TILE, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256),
                        0, st, io);
