@@ -86,6 +86,15 @@ __device__ __forceinline__ float ldbuf(brsrc_t r, uint32_t voff, uint32_t soff, 
   const uint16_t x = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
+// Four consecutive input elements as floats: 16 bytes (fp32) or 8 (bf16).
+__device__ __forceinline__ float4 ldbuf4in(brsrc_t r, uint32_t voff, uint32_t soff, const float*) {
+  return ldbuf4(r, voff, soff);
+}
+__device__ __forceinline__ float4 ldbuf4in(brsrc_t r, uint32_t voff, uint32_t soff, const bf16_t*) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return float4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u), __uint_as_float(x[1] << 16),
+                __uint_as_float(x[1] & 0xffff0000u)};
+}
 
 // Largest n in [0, N) with arr[n] <= x (arr non-decreasing, arr[0] = 0): the
 // sequence that owns slot x.  Uniform across the block.
@@ -882,39 +891,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const bool isW = w < 2;
   const int cbase = 64 * (w & 1);
   const TIn* v = static_cast<const TIn*>(io.v) + tok0 * io.H_v * D + static_cast<int64_t>(h) * D;
-  // right-hand-side sources of this wave's columns, (row 16 bi + 4 g + r,
-  // column cbase + 16 ct + l16): V straight from memory for the U waves (rows
-  // past a partial chunk's end are outside the buffer range and read 0), K from
-  // LDS for the W waves below
+  // Every column of W and U is solved on its own, so which lane holds which
+  // column is free: in a wave's tile ct, lane l16 holds column
+  // cbase + 4 l16 + ct, i.e. a lane's four tiles are four adjacent columns,
+  // read and written 16 (8) bytes at a time.  Right-hand-side sources, (row
+  // 16 bi + 4 g + r, that column): V straight from memory for the U waves
+  // (rows past a partial chunk's end are outside the buffer range and read
+  // 0), K from LDS for the W waves below.
+  const int col4 = cbase + 4 * l16;
   float rpre[4][4][4];
   if (!isW) {  // wave-uniform
     constexpr uint32_t ES = sizeof(TIn);
     const uint32_t rs = static_cast<uint32_t>(io.H_v) * D * ES;  // row stride, bytes
     const brsrc_t rv = make_rsrc(v, static_cast<uint32_t>(L - 1) * rs + D * ES);
-    const uint32_t vo = static_cast<uint32_t>(4 * g) * rs + static_cast<uint32_t>(cbase + l16) * ES;
+    const uint32_t vo = static_cast<uint32_t>(4 * g) * rs + static_cast<uint32_t>(col4) * ES;
     // A partial chunk (only in the all-chunks mode) relies on the range check
     // for its missing rows, so there the row is part of the lane offset (the
     // hardware range-checks the lane offset, not the scalar one); a full chunk
     // keeps the row in the scalar offset.  The branch is uniform per block.
-    if (MODE != kAll || L == C) {
+    const bool full = MODE != kAll || L == C;
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            rpre[bi][ct][r] = ldbuf(rv, vo, static_cast<uint32_t>(16 * bi + r) * rs + 16u * ct * ES,
-                                    static_cast<const TIn*>(nullptr));
-    } else {
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            rpre[bi][ct][r] = ldbuf(rv, vo + static_cast<uint32_t>(16 * bi + r) * rs + 16u * ct * ES, 0u,
-                                    static_cast<const TIn*>(nullptr));
-    }
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t ro = static_cast<uint32_t>(16 * bi + r) * rs;
+        const float4 x = ldbuf4in(rv, full ? vo : vo + ro, full ? ro : 0u, static_cast<const TIn*>(nullptr));
+        rpre[bi][0][r] = x.x;
+        rpre[bi][1][r] = x.y;
+        rpre[bi][2][r] = x.z;
+        rpre[bi][3][r] = x.w;
+      }
   }
   static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
 #pragma unroll
@@ -938,9 +944,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rpre[bi][ct][r] = sK[(16 * bi + 4 * g + r) * KS + cbase + 16 * ct + l16];
+      for (int r = 0; r < 4; ++r) {
+        const float4 x = *reinterpret_cast<const float4*>(sK + (16 * bi + 4 * g + r) * KS + col4);
+        rpre[bi][0][r] = x.x;
+        rpre[bi][1][r] = x.y;
+        rpre[bi][2][r] = x.z;
+        rpre[bi][3][r] = x.w;
+      }
   }
   if (tid == 0) {  // running sum of g, p ascending
     float acc = 0.0f;
@@ -1060,12 +1070,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       for (int ct = 0; ct < 4; ++ct) acc[ct] = yv[ct];
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      Y[bi][ct] = acc[ct];
+    for (int ct = 0; ct < 4; ++ct) Y[bi][ct] = acc[ct];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        out[static_cast<int64_t>(16 * bi + 4 * g + r) * D + cbase + 16 * ct + l16] = acc[ct][r];
-    }
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<float4*>(out + static_cast<int64_t>(16 * bi + 4 * g + r) * D + col4) =
+          float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
   }
   if (tid < C) io.G[(slot * io.H_v + h) * C + tid] = sG[tid];
 }
