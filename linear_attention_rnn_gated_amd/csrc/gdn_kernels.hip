@@ -2373,9 +2373,13 @@ __global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
 // group g is the B operand of the k-step that lane group g supplies as
 // k = 16 ib + 4 g + r, so dDelta (k = i) takes the state straight from
 // registers, and the update (k = p) takes dDelta and gam dO, held the same way,
-// straight from registers too.  Per chunk, K, Q and W (rows p) sit in LDS
-// and the next chunk's copies are fetched into registers while the current
-// one computes.
+// straight from registers too.  Per chunk, K, Q and W (rows p) sit in LDS.
+// K is read only by the dDelta products and Q, W only by the update, so each
+// is refilled while the other is read: the previous chunk's K is loaded
+// during this chunk's dDelta products and written once they end; its Q, W
+// and G are loaded during the update and written once it ends.  Two barriers
+// per chunk, one prefetch in registers at a time, and no branch in the loop
+// (past chunk 0 the prefetches reload chunk 0 into buffers nothing reads).
 template <int C>
 __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
   constexpr int D = 128, KS = D + 4, NQ = C * D / 4 / 512;  // float4 per thread
@@ -2408,14 +2412,7 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
   const uint32_t fw = 4u * static_cast<uint32_t>(r0 * D + 4 * cq);
   const uint32_t ostride = static_cast<uint32_t>(io.H_v) * D * 4u;  // dO row stride
   const uint32_t fo = 4u * static_cast<uint32_t>(j) + static_cast<uint32_t>(4 * g) * ostride;
-  // chunk operands: this thread's rows p = r0 + m and column quad cq
-  struct Ops {
-    float4 k[NQ], q[NQ], wv[NQ];
-    float gv, glast;  // G[tid] (tid < C) and G[C - 1]
-  };
   auto rows_of = [&](int64_t c) { return static_cast<int>(Lseq - c * C < C ? Lseq - c * C : C); };
-  // The loads come in NQ parts (part m: K, Q and W rows r0 + m, and G with
-  // part 0) so that they can be issued between the matrix-core products.
   struct OpRes {
     brsrc_t rq, rw;
     int64_t sh;
@@ -2429,20 +2426,38 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     r.rw = make_rsrc(io.W + r.sh * CD, C * D * 4u);
     return r;
   };
-  auto load_part = [&](Ops& o, const OpRes& rs, int m) {
-    const uint32_t mq = fq + static_cast<uint32_t>(m * 2 * D * 4);
-    o.k[m] = ldbuf4(rs.rq, mq, 0u);
-    o.q[m] = ldbuf4(rs.rq, mq + D * 4u, 0u);
-    o.wv[m] = ldbuf4(rs.rw, fw, static_cast<uint32_t>(m * D * 4));  // padded rows of W are 0
-    if (m == 0) {
-      o.gv = tid < C ? io.G[rs.sh * C + tid] : 0.0f;
-      o.glast = io.G[rs.sh * C + C - 1];
-    }
-  };
-  auto load_ops = [&](Ops& o, int64_t c) {
-    const OpRes rs = op_res(c);
+  // chunk operands, this thread's rows p = r0 + m and column quad cq
+  float4 pk[NQ], pq[NQ], pw[NQ];
+  float gvn = 0.0f, glastn = 0.0f;  // G[lane] and G[C - 1]
+  auto load_k = [&](const OpRes& rs) {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) load_part(o, rs, m);
+    for (int m = 0; m < NQ; ++m) pk[m] = ldbuf4(rs.rq, fq + static_cast<uint32_t>(m * 2 * D * 4), 0u);
+  };
+  auto load_qw = [&](const OpRes& rs) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      pq[m] = ldbuf4(rs.rq, fq + static_cast<uint32_t>(m * 2 * D * 4) + D * 4u, 0u);
+      pw[m] = ldbuf4(rs.rw, fw, static_cast<uint32_t>(m * D * 4));  // padded rows of W are 0
+    }
+    gvn = io.G[rs.sh * C + lane];
+    glastn = io.G[rs.sh * C + C - 1];
+  };
+  // K, Q and W go to LDS as loaded (no register transpose: a transpose of the
+  // prefetched quads would make the loads complete before the chunk computes)
+  auto put_k = [&]() {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) *reinterpret_cast<float4*>(sK + (r0 + m) * KS + 4 * cq) = pk[m];
+  };
+  auto put_qw = [&]() {  // W stored negated: the update adds (-W^T) dDelta
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      *reinterpret_cast<float4*>(sQ + (r0 + m) * KS + 4 * cq) = pq[m];
+      const float4 wv = pw[m];
+      *reinterpret_cast<float4*>(sW + (r0 + m) * KS + 4 * cq) = float4{-wv.x, -wv.y, -wv.z, -wv.w};
+    }
+    // every wave writes the same values (no branch)
+    sLam[lane] = expf(glastn - gvn);
+    sGam[lane] = expf(gvn);
   };
   // E and dO of a chunk in accumulator layout: (p = 16 pb + 4 g + r, j)
   auto load_ed = [&](float (&e)[4][4], float (&d)[4][4], int64_t c) {
@@ -2472,39 +2487,22 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
         st[ib][r] = ldbuf(rh, fj, static_cast<uint32_t>((16 * ib + r) * D * 4), static_cast<const float*>(nullptr));
   }
 
-  Ops nx;
-  if (nchunks > 0) load_ops(nx, nchunks - 1);
+  float glast = 0.0f;  // G at the end of the current chunk
+  if (nchunks > 0) {   // the last chunk's operands
+    const OpRes rs = op_res(nchunks - 1);
+    load_k(rs);
+    load_qw(rs);
+    put_k();
+    put_qw();
+    glast = glastn;
+  }
+  __syncthreads();
   for (int64_t c = nchunks - 1; c >= 0; --c) {
     const int64_t sh = (slot0 + c) * io.H_v + h;
     const int rows = rows_of(c);
-    __syncthreads();  // the previous chunk's LDS reads are done
-    // K, Q and W go to LDS as loaded (no register transpose: a transpose of the
-    // prefetched quads would make the loads complete before this chunk computes)
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-      *reinterpret_cast<float4*>(sK + (r0 + m) * KS + 4 * cq) = nx.k[m];
-      *reinterpret_cast<float4*>(sQ + (r0 + m) * KS + 4 * cq) = nx.q[m];
-      const float4 wv = nx.wv[m];  // stored negated: the update adds (-W^T) dDelta
-      *reinterpret_cast<float4*>(sW + (r0 + m) * KS + 4 * cq) = float4{-wv.x, -wv.y, -wv.z, -wv.w};
-    }
-    const float gcur = nx.gv, glast = nx.glast;
-    float ec[4][4], dc[4][4];  // land while dDelta is computed
-    load_ed(ec, dc, c);
-    if (tid < C) {
-      sLam[tid] = expf(glast - gcur);
-      sGam[tid] = expf(gcur);
-    }
-    // the next chunk's operands and this chunk's incoming state gradient (a
-    // store) are issued between the dDelta products below, a part per k block
-    const bool more = c > 0;
-    const OpRes nres = op_res(more ? c - 1 : c);
-    const brsrc_t rs = make_rsrc(io.dstates + sh * DD, D * D * 4u);
-    __syncthreads();  // sGam, sLam ready
-    // dDelta tiles (p = 16 pb + 4 g + r, j): k = i from the state registers
-    v4f dd[4];
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) dd[pb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    // A operands (K) are read from LDS one k block ahead of their use
+    const OpRes nres = op_res(c > 0 ? c - 1 : c);  // the next chunk (c - 1), or chunk 0 again
+    // dDelta tiles (p = 16 pb + 4 g + r, j): k = i from the state registers.
+    // A operands (K) are read from LDS one k block ahead of their use.
     float4 a[2][4];
     auto read_k = [&](float4 (&x)[4], int ib) {
 #pragma unroll
@@ -2512,24 +2510,45 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
         x[pb] = *reinterpret_cast<const float4*>(sK + (16 * pb + l16) * KS + 16 * ib + 4 * g);
     };
     read_k(a[0], 0);
+    float ec[4][4], dc[4][4];  // land while dDelta is computed
+    load_ed(ec, dc, c);
+    load_k(nres);
+    // the incoming state gradient (a store) between the dDelta products
+    const brsrc_t rs = make_rsrc(io.dstates + sh * DD, D * D * 4u);
+    v4f dd[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) dd[pb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib) {
       const float4(&x)[4] = a[ib & 1];
       if (ib + 1 < 8) read_k(a[(ib + 1) & 1], ib + 1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rs, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
-      if (more && ib < NQ) load_part(nx, nres, ib);
       __builtin_amdgcn_sched_barrier(0);  // the reads issue before this block's products
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].x, st[ib][0], dd[pb]);
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].y, st[ib][1], dd[pb]);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].z, st[ib][2], dd[pb]);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma4(x[pb].w, st[ib][3], dd[pb]);
-      __builtin_amdgcn_sched_barrier(0);  // at most one k block of reads in flight
+        for (int pb = 0; pb < 4; ++pb) {
+          const float xa = r == 0 ? x[pb].x : r == 1 ? x[pb].y : r == 2 ? x[pb].z : x[pb].w;
+          dd[pb] = mfma4(xa, st[ib][r], dd[pb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        stbuf(st[ib][r], rs, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    __syncthreads();  // every wave has read this chunk's K; sGam, sLam, Q, W are written
+    // A operand Q^T or -W^T (i = 16 (4 h2 + q) + l16, p = 16 pb + 4 g + r), a
+    // column of Q or -W, read from LDS one group of four tiles ahead of its use;
+    // the first read goes ahead of the next chunk's K
+    float aq[2][4][4];
+    auto read_qw = [&](float (&x)[4][4], int it) {
+      const float* src = (it < 8 ? sQ : sW) + (16 * ((it % 8) / 2) + 4 * g) * KS + 16 * (4 * (it % 2)) + l16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[q][r] = src[r * KS + 16 * q];
+    };
+    read_qw(aq[0], 0);
+    put_k();  // the next chunk's K
     const brsrc_t rd = make_rsrc(io.dD + sh * CD, C * D * 4u);
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
@@ -2550,17 +2569,7 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
       for (int r = 0; r < 4; ++r) dcv[pb][r] = dc[pb][r];
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib) st[ib] = gl * st[ib];
-    // A operand Q^T or -W^T (i = 16 (4 h2 + q) + l16, p = 16 pb + 4 g + r), a
-    // column of Q or -W, read from LDS one group of four tiles ahead of its use
-    float aq[2][4][4];
-    auto read_qw = [&](float (&x)[4][4], int it) {
-      const float* src = (it < 8 ? sQ : sW) + (16 * ((it % 8) / 2) + 4 * g) * KS + 16 * (4 * (it % 2)) + l16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[q][r] = src[r * KS + 16 * q];
-    };
-    read_qw(aq[0], 0);
+    load_qw(nres);  // the next chunk's Q, W and G, issued ahead of the products
 #pragma unroll
     for (int it = 0; it < 16; ++it) {  // Q^T (gam dO), then -W^T dDelta; (pb, h2) per op
       const int op = it / 8, pb = (it % 8) / 2, h2 = it % 2;
@@ -2574,6 +2583,9 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
         for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(x[q][r], bv[r], st[4 * h2 + q]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __syncthreads();  // every wave has read this chunk's Q, W, sGam and sLam
+    put_qw();         // the next chunk's
+    glast = glastn;
   }
   const brsrc_t rh0 = make_rsrc(io.dh0 + nh * DD, D * D * 4u);
 #pragma unroll
