@@ -2621,7 +2621,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   __shared__ __attribute__((aligned(16))) float sZ[C * CS];    // Z, later dA
   __shared__ __attribute__((aligned(16))) float sK[C * KS];
   __shared__ __attribute__((aligned(16))) float sY[2 * C * KS];  // dO | Delta, then Q, then Y
-  __shared__ float sG[C], sB[C], sGam[C], sLam[C], sdB[C], skd[C];
+  __shared__ float sG[C], sB[C], sGam[C], sdB[C];
+  __shared__ __attribute__((aligned(16))) float sLam[C], skd[C];
   __shared__ __attribute__((aligned(16))) float sdG[C];
   static_assert(C * YS <= 2 * C * KS, "Y must fit");
   float* sO = sY;
@@ -2810,8 +2811,18 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   }
   __syncthreads();  // Q, QK, Z reads done; Y may overwrite Q
   if (tid == 0) {
+    // rows q < L in ascending order; both rows are read 16 bytes at a time
+    // first, and rows past L keep sacc (a select, not a shorter loop)
     float sacc = sGam[C - 1] * MdM;
-    for (int q = 0; q < L; ++q) sacc = fmaf(sLam[q], skd[q], sacc);
+#pragma unroll
+    for (int q4 = 0; q4 < C / 4; ++q4) {
+      const float4 lm = *reinterpret_cast<const float4*>(sLam + 4 * q4);
+      const float4 kd = *reinterpret_cast<const float4*>(skd + 4 * q4);
+      sacc = 4 * q4 < L ? fmaf(lm.x, kd.x, sacc) : sacc;
+      sacc = 4 * q4 + 1 < L ? fmaf(lm.y, kd.y, sacc) : sacc;
+      sacc = 4 * q4 + 2 < L ? fmaf(lm.z, kd.z, sacc) : sacc;
+      sacc = 4 * q4 + 3 < L ? fmaf(lm.w, kd.w, sacc) : sacc;
+    }
     sdG[L - 1] = sdG[L - 1] + sacc;
   }
   // ---- back substitution (I + A)^T Y = [-SdD | dDelta], A_pr = beta_p KG_pr,
