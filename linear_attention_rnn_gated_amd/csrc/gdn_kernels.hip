@@ -1555,10 +1555,12 @@ __device__ __forceinline__ void st_grad(void* base, int64_t i, float x, int bf16
   }
 }
 
-// Chunk item of a backward kernel: slot = blockIdx.x over every chunk.
+// Chunk item of a backward kernel over every chunk and value head, grid
+// (8 G ceil(chunks / 8), H_qk) grouped as the chunk factors' (the value heads
+// of a q/k group, which read the same q-hat and k-hat rows, 8 blocks apart).
 template <int C>
-__device__ __forceinline__ bool bwd_item(const BwdIO& io, int64_t& slot, int64_t& tok0, int& L) {
-  slot = blockIdx.x;
+__device__ __forceinline__ bool bwd_item(const BwdIO& io, int64_t& slot, int& h, int64_t& tok0, int& L) {
+  wy_item(io.H_v / io.H_qk, slot, h);
   if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return false;
   const int n = find_seq(io.cu_chunks, io.N, slot);
   tok0 = static_cast<int64_t>(io.cu[n]) + (slot - io.cu_chunks[n]) * C;
@@ -1577,9 +1579,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdIO io) {
   __shared__ float sP[C][C + 1];
   __shared__ float sG[C];
   int64_t slot, tok0;
-  int L;
-  if (!bwd_item<C>(io, slot, tok0, L)) return;
-  const int tid = threadIdx.x, h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  int L, h;
+  if (!bwd_item<C>(io, slot, h, tok0, L)) return;
+  const int tid = threadIdx.x, hq = h / (io.H_v / io.H_qk);
   const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
   for (int e = tid; e < C * D; e += NT) {
     const int p = e / D, i = e % D;
@@ -1702,9 +1704,9 @@ __global__ __launch_bounds__(256) void k_bwd_mm(BwdIO io) {
   __shared__ float sM[D][D + 1];
   __shared__ float sY[C][D + 1];
   int64_t slot, tok0;
-  int L;
-  if (!bwd_item<C>(io, slot, tok0, L)) return;
-  const int tid = threadIdx.x, h = blockIdx.y;
+  int L, h;
+  if (!bwd_item<C>(io, slot, h, tok0, L)) return;
+  const int tid = threadIdx.x;
   const int64_t DD = static_cast<int64_t>(D) * D;
   const int64_t CD = static_cast<int64_t>(C) * D;
   const int64_t sh = slot * io.H_v + h;
@@ -1763,9 +1765,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdIO io) {
   static_assert(C * DP + 2 * C * CP >= C * 2 * D, "Y must fit in the Q/QK/Z region");
 
   int64_t slot, tok0;
-  int L;
-  if (!bwd_item<C>(io, slot, tok0, L)) return;
-  const int tid = threadIdx.x, h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  int L, h;
+  if (!bwd_item<C>(io, slot, h, tok0, L)) return;
+  const int tid = threadIdx.x, hq = h / (io.H_v / io.H_qk);
   const int64_t DD = static_cast<int64_t>(D) * D;
   const int64_t CD = static_cast<int64_t>(C) * D;
   const int64_t sh = slot * io.H_v + h;
@@ -2032,11 +2034,11 @@ __global__ __launch_bounds__(256) void k_bwd_prep_m(BwdIO io) {
   float* PT = lds + C * S1;    // [C][S2]
   static_assert(C * S2 <= C * S1, "LDS reuse");
   int64_t slot, tok0;
-  int L;
-  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  int L, h;
+  if (!bwd_item<C>(io, slot, h, tok0, L)) return;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  const int hq = h / (io.H_v / io.H_qk);
   const int64_t sh = slot * io.H_v + h;
   const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
   static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
@@ -2114,11 +2116,11 @@ __global__ __launch_bounds__(512) void k_chunk_o_m(BwdIO io) {
   __shared__ __attribute__((aligned(16))) float sP[C * S2];
   __shared__ float sG[C], sGam[C];
   int64_t slot, tok0;
-  int L;
-  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  int L, h;
+  if (!bwd_item<C>(io, slot, h, tok0, L)) return;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
-  const int h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  const int hq = h / (io.H_v / io.H_qk);
   const int64_t sh = slot * io.H_v + h;
   const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
   const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
@@ -2390,7 +2392,11 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
   __shared__ float sGam[C], sLam[C];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t nh = blockIdx.x;
+  // (sequence, head) pairs 2 p, 2 p + 1 (two heads of a q/k group when the
+  // group has two) go out 8 blocks apart, to one XCD at about the same time,
+  // and share the q-hat and k-hat rows through its L2 (grid: 16 | blocks)
+  const int64_t bx = blockIdx.x;
+  const int64_t nh = ((bx / 16) * 8 + bx % 8) * 2 + (bx / 8) % 2;
   const int n = static_cast<int>(nh / io.H_v), h = static_cast<int>(nh % io.H_v);
   if (n >= io.N) return;
   const int hq = h / (io.H_v / io.H_qk);
@@ -2629,11 +2635,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   float* sD = sY + C * KS;
   float* sQ = sY;
   int64_t slot, tok0;
-  int L;
-  if (!bwd_item<C>(io, slot, tok0, L)) return;
+  int L, h;
+  if (!bwd_item<C>(io, slot, h, tok0, L)) return;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
-  const int h = blockIdx.y, hq = h / (io.H_v / io.H_qk);
+  const int hq = h / (io.H_v / io.H_qk);
   const int64_t CD = static_cast<int64_t>(C) * D;
   const int64_t sh = slot * io.H_v + h;
   const int64_t vs = static_cast<int64_t>(io.H_v) * D;
@@ -3316,6 +3322,13 @@ int rec_heads_per_block(int G) {
   return hpb < G ? hpb : G;
 }
 
+// Grid of the kernels over every chunk and value head (see wy_item).
+dim3 chunk_grid(int64_t chunks, const gdn_shape_t* s) {
+  const int64_t G = s->H_v / s->H_qk;
+  const int64_t c = chunks > 0 ? chunks : 1;
+  return dim3(static_cast<unsigned>((c + 7) / 8 * 8 * G), static_cast<unsigned>(s->H_qk));
+}
+
 // The chunk factors: matrix-core kernel at d = 128, the VALU kernel at d = 16.
 template <int D, int C, typename TIn, int MODE>
 void launch_wy(const ChunkIO& io, int64_t items, int H_v, hipStream_t st) {
@@ -3642,7 +3655,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
       b.dqv = o;  // k_chunk_o's output
       b.N = N; b.H_qk = s->H_qk; b.H_v = s->H_v; b.T = cnt.T; b.max_state_slot = L.state_slots;
       Timed t_("k_chunk_o", st);
-      hipLaunchKernelGGL((k_chunk_o_m<C>), dim3(static_cast<unsigned>(cnt.chunks), s->H_v),
+      hipLaunchKernelGGL((k_chunk_o_m<C>), chunk_grid(cnt.chunks, s),
                          dim3(512), 0, st, b);
     }
   } else if (cnt.chunks > 0) {
@@ -3673,7 +3686,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   b.grad_bf16 = grad_bf16;
   b.N = N; b.H_qk = s->H_qk; b.H_v = s->H_v; b.l2 = s->qk_l2norm; b.scale = s->scale;
   b.T = cnt.T; b.max_state_slot = L.state_slots;
-  const dim3 cgrid(static_cast<unsigned>(cnt.chunks > 0 ? cnt.chunks : 1), s->H_v);
+  const dim3 cgrid = chunk_grid(cnt.chunks, s);
   if (cnt.chunks > 0) {
     Timed t_("k_bwd_prep", st);
     if constexpr (D == 128)
@@ -3684,7 +3697,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   if (sblocks > 0) {
     Timed t_("k_bwd_scan", st);
     if constexpr (D == 128) {
-      hipLaunchKernelGGL((k_bwd_scan_m<C>), dim3(static_cast<unsigned>(N * s->H_v)), dim3(512), 0,
+      hipLaunchKernelGGL((k_bwd_scan_m<C>), dim3(static_cast<unsigned>((N * s->H_v + 15) / 16 * 16)), dim3(512), 0,
                          st, b);
     } else {
       hipLaunchKernelGGL((k_bwd_scan<D, C, TILE>), dim3(static_cast<unsigned>(sblocks)),
@@ -3765,7 +3778,7 @@ int launch_prefill_chunked(const gdn_shape_t* s, int32_t N, const gdn::Counts& c
       b.dqv = o;
       b.N = N; b.H_qk = s->H_qk; b.H_v = s->H_v; b.T = cnt.T; b.max_state_slot = L.state_slots;
       Timed t_("k_chunk_o", st);
-      hipLaunchKernelGGL((k_chunk_o_m<C>), dim3(static_cast<unsigned>(cnt.chunks), s->H_v),
+      hipLaunchKernelGGL((k_chunk_o_m<C>), chunk_grid(cnt.chunks, s),
                          dim3(512), 0, st, b);
     }
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
