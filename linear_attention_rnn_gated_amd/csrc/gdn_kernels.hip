@@ -899,6 +899,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // (rows past a partial chunk's end are outside the buffer range and read
   // 0), K from LDS for the W waves below.
   const int col4 = cbase + 4 * l16;
+  // K (and beta, g) are loaded first and V last: loads complete in order, so
+  // the K staging below waits for K alone and V lands during the Gram products
+  float bx = 0.0f, gx = 0.0f;
+  if (tid < C) {
+    const int pc = tid < L ? tid : L - 1;
+    bx = io.beta[(tok0 + pc) * io.H_v + h];
+    gx = io.g[(tok0 + pc) * io.H_v + h];
+  }
+  constexpr int NK = (C * (D / 4)) / 256;
+  static_assert(NK * 256 == C * (D / 4), "whole rounds");
+  float4 kx[NK];
+#pragma unroll
+  for (int e_ = 0; e_ < NK; ++e_) {
+    const int e = tid + 256 * e_;
+    const int p = e / (D / 4), i4 = e % (D / 4);
+    const int pc = p < L ? p : L - 1;
+    kx[e_] = *reinterpret_cast<const float4*>(krow + pc * kst + 4 * i4);
+  }
   float rpre[4][4][4];
   if (!isW) {  // wave-uniform
     constexpr uint32_t ES = sizeof(TIn);
@@ -922,20 +940,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         rpre[bi][3][r] = x.w;
       }
   }
-  static_assert((C * (D / 4)) % 256 == 0, "whole rounds");
 #pragma unroll
-  for (int e_ = 0; e_ < (C * (D / 4)) / 256; ++e_) {
+  for (int e_ = 0; e_ < NK; ++e_) {
     const int e = tid + 256 * e_;
     const int p = e / (D / 4), i4 = e % (D / 4);
-    const int pc = p < L ? p : L - 1;
-    const float4 x = *reinterpret_cast<const float4*>(krow + pc * kst + 4 * i4);
-    *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) =
-        sel4(p < L, x, float4{0.0f, 0.0f, 0.0f, 0.0f});
+    *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) = sel4(p < L, kx[e_], float4{0.0f, 0.0f, 0.0f, 0.0f});
   }
   if (tid < C) {
-    const int pc = tid < L ? tid : L - 1;
-    const float bx = io.beta[(tok0 + pc) * io.H_v + h];
-    const float gx = io.g[(tok0 + pc) * io.H_v + h];
     sB[tid] = tid < L ? bx : 0.0f;
     sBG[tid] = tid < L ? gx : 0.0f;  // raw g for now
   }
