@@ -1159,11 +1159,15 @@ __device__ __forceinline__ void load_block(OpBlock& x, cfloat_p kq, cfloat_p kn,
 // touches the next token's query line and the key line two tokens ahead
 // (p0, p1; folded into `sink` one block later, so the next block's wait
 // retires them): the following tokens' operand loads then hit the scalar
-// cache.  The reads stay inside the prep buffer's two spare token rows.
-template <int DK, int D>  // DK: elements of the row this lane holds; D: head dimension
+// cache.  With SPREAD (four waves share the stream: two value heads, two
+// row parts) each of them touches only the lines of block toff / RB, once
+// per token: every line is still touched, with a quarter of the requests to
+// the scalar cache that all the waves share.  The reads stay inside the prep
+// buffer's two spare token rows.
+template <int DK, int D, bool SPREAD>  // DK: elements of the row this lane holds; D: head dimension
 __device__ __forceinline__ void r_token_pass(float (&s)[DK], cfloat_p kq, cfloat_p kn, float alpha,
                                              float delta, float& o, float& an, uint32_t& p0,
-                                             uint32_t& p1, uint32_t& sink) {
+                                             uint32_t& p1, uint32_t& sink, int toff) {
   constexpr int NB = DK / RB;
   static_assert(DK % RB == 0, "row part must be whole operand blocks");
 #pragma unroll
@@ -1177,9 +1181,11 @@ __device__ __forceinline__ void r_token_pass(float (&s)[DK], cfloat_p kq, cfloat
       an = fmaf(s[i], x.n[0], an);
     }
     __builtin_amdgcn_sched_barrier(0);
-    sink ^= p0 ^ p1;
-    p0 = __float_as_uint(kq[2 * D + D + b * RB]);
-    p1 = __float_as_uint(kq[4 * D + b * RB]);
+    if (!SPREAD || b == 0) {  // (SPREAD: the waves sharing the stream split its lines)
+      sink ^= p0 ^ p1;
+      p0 = __float_as_uint(kq[2 * D + D + (SPREAD ? toff : b * RB)]);
+      p1 = __float_as_uint(kq[4 * D + (SPREAD ? toff : b * RB)]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 1; r < RB; ++r) {
@@ -1233,7 +1239,7 @@ struct RowSplit {
 // same key/query stream share a CU and its scalar cache; blockIdx.z continues
 // a group of more heads.  Wave (head, row part, d_k part) = index within the
 // block in that order, d_k part fastest.
-template <int D, int C, typename TIn>
+template <int D, int C, typename TIn, bool SPREAD>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k_rec(RecIO io, int hpb) {
   using RS = RowSplit<D>;
   constexpr int DK = RS::DK, KS = RS::KS, NH = RS::NH;
@@ -1251,6 +1257,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   const int G = io.H_v / io.H_qk;
   const int h = blockIdx.y * G + wv / RS::WPH;
   const int wp = wl / KS;  // (head, row part) pair within the block
+  const int toff = SPREAD ? (wp & 3) * RB : 0;  // the touch lines of this wave (SPREAD)
   const int lane = threadIdx.x & 63;
   const int j = rh * 64 + lane;
   const bool act = D % 64 == 0 || j < D;
@@ -1342,7 +1349,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     const float delta = b * (vj - u);
     cfloat_p kn = kq + 2 * D;  // past the chunk's end on its last token: read, never used
     float o = 0.0f, an = 0.0f;
-    r_token_pass<DK, D>(s, kq, kn, alpha, delta, o, an, pp0, pp1, psink);
+    r_token_pass<DK, D, SPREAD>(s, kq, kn, alpha, delta, o, an, pp0, pp1, psink, toff);
     if constexpr (KS == 2) {
       const int par = t & 1;  // a slot is rewritten two barriers after it was read
       xa[par][wl][lane] = an;
@@ -3340,6 +3347,14 @@ dim3 chunk_grid(int64_t chunks, const gdn_shape_t* s) {
   return dim3(static_cast<unsigned>((c + 7) / 8 * 8 * G), static_cast<unsigned>(s->H_qk));
 }
 
+// Whether the waves of a token-step block that share a key/query stream are
+// four (two value heads, two row parts at d = 128, one operand block each),
+// so that they can split the prefetch touches.
+template <int D>
+bool rec_spread(int hpb) {
+  return D == 128 && RowSplit<D>::NH * hpb == 4 && RowSplit<D>::DK / RB == 4;
+}
+
 // The chunk factors: matrix-core kernel at d = 128, the VALU kernel at d = 16.
 template <int D, int C, typename TIn, int MODE>
 void launch_wy(const ChunkIO& io, int64_t items, int H_v, hipStream_t st) {
@@ -3460,8 +3475,11 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     Timed t_("k_rec", st);
     const int G = s->H_v / s->H_qk;
     const int hpb = rec_heads_per_block<D>(G);
-    hipLaunchKernelGGL((k_rec<D, C, TIn>), dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb),
-                       dim3(64 * RowSplit<D>::WPH * hpb), 0, st, io, hpb);
+    const dim3 rgrid(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb), rblock(64 * RowSplit<D>::WPH * hpb);
+    if (rec_spread<D>(hpb))
+      hipLaunchKernelGGL((k_rec<D, C, TIn, true>), rgrid, rblock, 0, st, io, hpb);
+    else
+      hipLaunchKernelGGL((k_rec<D, C, TIn, false>), rgrid, rblock, 0, st, io, hpb);
   }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -3677,8 +3695,11 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     Timed t_("k_rec", st);
     const int G = s->H_v / s->H_qk;
     const int hpb = rec_heads_per_block<D>(G);
-    hipLaunchKernelGGL((k_rec<D, C, TIn>), dim3(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb),
-                       dim3(64 * RowSplit<D>::WPH * hpb), 0, st, io, hpb);
+    const dim3 rgrid(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb), rblock(64 * RowSplit<D>::WPH * hpb);
+    if (rec_spread<D>(hpb))
+      hipLaunchKernelGGL((k_rec<D, C, TIn, true>), rgrid, rblock, 0, st, io, hpb);
+    else
+      hipLaunchKernelGGL((k_rec<D, C, TIn, false>), rgrid, rblock, 0, st, io, hpb);
   }
   // backward
   BwdIO b{};
