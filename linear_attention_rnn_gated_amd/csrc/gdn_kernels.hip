@@ -189,11 +189,30 @@ __global__ void k_order(const int32_t* __restrict__ cu, int N, int32_t* __restri
 // consecutive (token, q/k head) vectors, one at a time with the lanes and
 // arithmetic of l2norm_wave, after loading all of them.
 constexpr int kPrepVecs = 4;
+// (g, beta) of each value head in token order, gb[h][t] = (g[t][h], beta[t][h]):
+// the token step then reads a token's pair with one 8-byte scalar load, eight
+// tokens to a cache line (in [t][h] order each token's pair is a new line for
+// every wave of the head).  Null: not written.
+struct GbArgs {
+  const float* g;
+  const float* beta;
+  float* gb;
+  int H_v;
+};
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void k_prep(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                               float* __restrict__ qk, int64_t T, int H_qk,
-                                              float scale, int l2, PlanArgs plan) {
+                                              float scale, int l2, PlanArgs plan, GbArgs gb) {
   if (plan.cu && blockIdx.x == 0 && threadIdx.x == 0) plan_counts(plan);
+  if (gb.gb) {
+    const int64_t n = T * gb.H_v;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+         e += static_cast<int64_t>(gridDim.x) * 256) {
+      const int64_t t = e / gb.H_v;
+      const int64_t h = e - t * gb.H_v;
+      *reinterpret_cast<float2*>(gb.gb + (h * T + t) * 2) = float2{gb.g[e], gb.beta[e]};
+    }
+  }
   const int64_t nvec = T * H_qk;
   const int64_t vec0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepVecs;
   if (vec0 >= nvec) return;
@@ -1204,6 +1223,7 @@ struct RecIO {
   const void* v;
   const float* beta;
   const float* g;
+  const float* gb;   // (g, beta) per value head in token order [H_v][T][2]
   const int32_t* cu;
   const int32_t* cu_chunks;
   const float* states;
@@ -1271,13 +1291,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   const int L = static_cast<int>(end - tok0 < C ? end - tok0 : C);
   const int64_t DD = static_cast<int64_t>(D) * D;
   const int vs = io.H_v * D;  // < 2^20 (host-checked)
-  const int bs = io.H_v;
   const int i0 = kh * DK;     // first d_k element of this wave
   // Token operands of the chunk: g and beta as wave-uniform scalar loads, v
   // and o through buffer resources over the chunk's rows (lane offset in a
   // VGPR, token offset in an SGPR).
-  cfloat_p gt = as_const(io.g + tok0 * io.H_v + h);
-  cfloat_p bt = as_const(io.beta + tok0 * io.H_v + h);
+  cfloat_p gbt = as_const(io.gb + (static_cast<int64_t>(h) * io.T + tok0) * 2);
   float* obase = io.o + (tok0 * io.H_v + h) * D;
   const uint32_t otok = static_cast<uint32_t>(vs) * 4u;
   const brsrc_t orr = make_rsrc(obase, static_cast<uint32_t>(L - 1) * otok + D * 4u);
@@ -1316,14 +1334,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   // g, beta and v are loaded one token ahead; the last token reloads itself
   // rather than reading past the chunk
   uint32_t pp0 = 0, pp1 = 0, psink = 0;
-  float gn = gt[0], bn = bt[0], vn = ldin(&sv[wp][0][lane]);
+  float gn = gbt[0], bn = gbt[1], vn = ldin(&sv[wp][0][lane]);
   for (int t = 0; t < L; ++t) {
     const float alpha = expf(gn);
     const float b = bn;
     const float vj = vn;
     const int tn = t + 1 < L ? t + 1 : t;
-    gn = gt[tn * bs];
-    bn = bt[tn * bs];
+    gn = gbt[2 * tn];
+    bn = gbt[2 * tn + 1];
     if constexpr (SC < C) {
       // the second half: every wave read its last first-half row (token SC - 1)
       // one token ahead, before the previous token's exchange barrier
@@ -3154,6 +3172,7 @@ struct ContIO {
   void* v_ext;
   float* b_ext;
   float* g_ext;
+  float* gb;              // (g, beta) of the extended batch per value head, token order
   const float* o_ext;
   float* o;
   int N, H_qk, H_v, C, l2;
@@ -3222,8 +3241,10 @@ __global__ __launch_bounds__(256) void k_cont_gather(ContIO io) {
     if (l < D) vd[l] = vs[l];
     if (D > 64) vd[l + 64] = vs[l + 64];
     if (l == 0) {
-      io.b_ext[e * io.H_v + h] = bin[brow * io.H_v + h];
-      io.g_ext[e * io.H_v + h] = gin[brow * io.H_v + h];
+      const float bx = bin[brow * io.H_v + h], gx = gin[brow * io.H_v + h];
+      io.b_ext[e * io.H_v + h] = bx;
+      io.g_ext[e * io.H_v + h] = gx;
+      *reinterpret_cast<float2*>(io.gb + (static_cast<int64_t>(h) * io.T_ext + e) * 2) = float2{gx, bx};
     }
   }
 }
@@ -3413,7 +3434,7 @@ const int32_t* scan_order(const int32_t* cu, int32_t N, int H_v, const gdn::Layo
 template <int D, typename TIn>
 void launch_plan_prep(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, const int32_t* cu,
                       const void* q, const void* k, float* qk, int32_t* cu_chunks, int32_t* cu_full,
-                      hipStream_t st) {
+                      GbArgs gb, hipStream_t st) {
   const int64_t nvec = cnt.T * s->H_qk;
   if (nvec <= 0) {
     Timed t_("k_plan", st);
@@ -3423,7 +3444,7 @@ void launch_plan_prep(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, c
   Timed t_("k_prep", st);
   hipLaunchKernelGGL((k_prep<D, TIn>), dim3(static_cast<unsigned>(prep_blocks(nvec))), dim3(256), 0, st,
                      static_cast<const TIn*>(q), static_cast<const TIn*>(k), qk, cnt.T, s->H_qk,
-                     s->scale, s->qk_l2norm, PlanArgs{cu, N, s->C, cu_chunks, cu_full});
+                     s->scale, s->qk_l2norm, PlanArgs{cu, N, s->C, cu_chunks, cu_full}, gb);
 }
 
 template <int D, int C, typename TIn>
@@ -3441,7 +3462,9 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   float* Gs = reinterpret_cast<float*>(ws + L.G);
   float* states = reinterpret_cast<float*>(ws + L.states);
 
-  if (!gathered) launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, st);
+  float* gbp = reinterpret_cast<float*>(ws + L.gb);
+  if (!gathered)
+    launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, GbArgs{g, beta, gbp, s->H_v}, st);
   if (cnt.full > 0) {
     ChunkIO io{};
     io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_full;
@@ -3465,7 +3488,7 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   }
   if (cnt.chunks > 0) {
     RecIO io{};
-    io.qk = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu;
+    io.qk = qk; io.v = v; io.beta = beta; io.g = g; io.gb = gbp; io.cu = cu;
     io.cu_chunks = cu_chunks; io.states = states; io.o = o; io.hT = hT;
     if (cache) {
       io.S_run = cache->S_run; io.kbuf = cache->kbuf; io.vbuf = cache->vbuf;
@@ -3498,6 +3521,7 @@ int launch_prefill_continue(const gdn_shape_t* s, int32_t N, const gdn::Counts& 
   io.v_ext = ws + L.v_ext;
   io.b_ext = reinterpret_cast<float*>(ws + L.b_ext);
   io.g_ext = reinterpret_cast<float*>(ws + L.g_ext);
+  io.gb = reinterpret_cast<float*>(ws + L.gb);
   io.o_ext = reinterpret_cast<float*>(ws + L.o_ext);
   io.o = o;
   io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.C = C; io.l2 = s->qk_l2norm;
@@ -3655,7 +3679,8 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   float* Gs = reinterpret_cast<float*>(ws + L.G);
   float* states = reinterpret_cast<float*>(ws + L.states);
   float* Dl = reinterpret_cast<float*>(ws + L.Dl);
-  launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, st);
+  float* gbp = reinterpret_cast<float*>(ws + L.gb);
+  launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, GbArgs{g, beta, gbp, s->H_v}, st);
   if (cnt.chunks > 0) {
     ChunkIO io{};
     io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_chunks;
@@ -3689,7 +3714,7 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     }
   } else if (cnt.chunks > 0) {
     RecIO io{};
-    io.qk = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu;
+    io.qk = qk; io.v = v; io.beta = beta; io.g = g; io.gb = gbp; io.cu = cu;
     io.cu_chunks = cu_chunks; io.states = states; io.o = o; io.hT = hT;
     io.N = N; io.H_qk = s->H_qk; io.H_v = s->H_v; io.T = cnt.T; io.max_state_slot = L.state_slots;
     Timed t_("k_rec", st);
@@ -3784,7 +3809,7 @@ int launch_prefill_chunked(const gdn_shape_t* s, int32_t N, const gdn::Counts& c
     float* Gs = reinterpret_cast<float*>(ws + L.G);
     float* states = reinterpret_cast<float*>(ws + L.states);
     float* Dl = reinterpret_cast<float*>(ws + L.Dl);
-    launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, st);
+    launch_plan_prep<D, TIn>(s, N, cnt, cu, q, k, qk, cu_chunks, cu_full, GbArgs{}, st);
     if (cnt.chunks > 0) {
       ChunkIO io{};
       io.khat = qk; io.v = v; io.beta = beta; io.g = g; io.cu = cu; io.cu_full = cu_chunks;

@@ -79,6 +79,7 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
   L.G = take(&cur, wu_slots * Hv * C * f);
   L.states = take(&cur, L.state_slots * Hv * d * d * f);
   L.order = take(&cur, static_cast<size_t>(N) * sizeof(int32_t) + 1);
+  if (op != GDN_OP_PREFILL_CHUNKED) L.gb = take(&cur, T * Hv * 2 * f);  // read by the token step
   if (op == GDN_OP_PREFILL_CHUNKED) L.Dl = take(&cur, L.state_slots * Hv * C * d * f);
   if (op == GDN_OP_FWD_BWD) {
     const size_t cd = L.state_slots * Hv * C * d * f;

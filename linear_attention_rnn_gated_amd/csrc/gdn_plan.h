@@ -39,6 +39,7 @@ struct Layout {
   size_t G = 0;          // f32 [full_slots, H_v, C]
   size_t states = 0;     // f32 [state_slots, H_v, d, d]  chunk-start states
   size_t order = 0;      // int32 [N]  sequences longest first (chunk scan)
+  size_t gb = 0;         // f32 [H_v, T, 2]  (g, beta) of each value head in token order
   // trainer forward + backward only (W, U, G then use chunk slots)
   size_t Dl = 0;         // f32 [state_slots, H_v, C, d]  Delta = U - W S^T
   size_t E = 0;          // f32 [state_slots, H_v, C, d]  P^T dO
