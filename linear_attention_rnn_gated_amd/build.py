@@ -26,6 +26,9 @@ FLAGS = [
     "-shared",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the 4-wave chunk scan otherwise
+    # splits its accumulators into AGPRs and copies them back every chunk
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
     "-Wno-unused-function",
 ]
