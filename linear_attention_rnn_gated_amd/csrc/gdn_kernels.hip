@@ -559,36 +559,148 @@ __device__ __forceinline__ int64_t xcd_block(int64_t nb8) {
   return (b % 8) * (nb8 / 8) + b / 8;
 }
 
+// Matrix-core products of fp32 operands from bf16 parts.  A value x is
+// written as three bf16 parts, x = hi + mid + lo exactly: hi is x rounded to
+// nearest bf16; the residual x - hi is exact in fp32 (hi is within a factor
+// two of x) and has at most 16 significant bits; mid is that residual rounded
+// to nearest, and what is left has at most 8 significant bits, so lo holds it
+// exactly (for |x| above about 2^-110; smaller parts meet the bf16 range).
+// |mid| <= 2^-8 |x| and |lo| <= 2^-16 |x|, so of the nine part products of
+// a b the six kept,
+//   ah bh, ah bm, ah bl, am bh, am bm, al bh,
+// leave out three whose sum is below 2^-23 |a b| and of either sign.  Each
+// part product is exact in fp32; v_mfma_f32_16x16x32_bf16 sums them into an
+// fp32 accumulator.  Parts are packed two per 32-bit word, the lower element
+// in the low half, and a lane's eight elements of one part fill four words.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+struct Parts {
+  u32x4_t p[3];  // hi, mid, lo
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = pack_bf16(x0, x1);
+  const float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xffff0000u);
+  m = pack_bf16(r0, r1);
+  const float s0 = r0 - __uint_as_float(m << 16), s1 = r1 - __uint_as_float(m & 0xffff0000u);
+  l = pack_bf16(s0, s1);  // exact
+}
+// parts of x[0..7] and of y[0..7], stage by stage over all sixteen values
+// (neighbouring instructions are then independent)
+__device__ __forceinline__ void split8x2(const float (&x)[8], const float (&y)[8], Parts& px, Parts& py) {
+  float v[16], r[16];
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = x[k], v[8 + k] = y[k];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h[k] = pack_bf16(v[2 * k], v[2 * k + 1]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    r[2 * k] = v[2 * k] - __uint_as_float(h[k] << 16);
+    r[2 * k + 1] = v[2 * k + 1] - __uint_as_float(h[k] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m[k] = pack_bf16(r[2 * k], r[2 * k + 1]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    r[2 * k] = r[2 * k] - __uint_as_float(m[k] << 16);
+    r[2 * k + 1] = r[2 * k + 1] - __uint_as_float(m[k] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) l[k] = pack_bf16(r[2 * k], r[2 * k + 1]);  // exact
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    px.p[0][k] = h[k], px.p[1][k] = m[k], px.p[2][k] = l[k];
+    py.p[0][k] = h[4 + k], py.p[1][k] = m[4 + k], py.p[2][k] = l[4 + k];
+  }
+}
+// parts of x[0..7]
+__device__ __forceinline__ Parts split8(const float (&x)[8]) {
+  Parts r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t h, m, l;
+    split_pair(x[2 * k], x[2 * k + 1], h, m, l);
+    r.p[0][k] = h, r.p[1][k] = m, r.p[2][k] = l;
+  }
+  return r;
+}
+// parts of the eight values {x[0..3], y[0..3]} (two accumulator tiles)
+__device__ __forceinline__ Parts split8(v4f x, v4f y) {
+  const float v[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return split8(v);
+}
+// v_mfma_f32_16x16x32_bf16: lane l supplies A[l % 16][8 (l / 16) + e] and
+// B[8 (l / 16) + e][l % 16] for e = 0..7, and holds D[4 (l / 16) + r][l % 16]
+// in accumulator register r (the same output layout as mfma4).
+__device__ __forceinline__ v4f mfma_bf(u32x4_t a, u32x4_t b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// Scheduling pattern for a region of NM products: its NR LDS reads first, then
+// each product followed by up to three VALU instructions.
+template <int NM, int NR>
+__device__ __forceinline__ void mfma_valu_pattern() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+  }
+}
+
 // B, part 2 on the matrix cores (d = 128, C = 64): the chunk-state scan
 //   Delta = U - W S^T,   S' = gam_C S + sum_p lam_p Delta_p k_p^T
 // (gam_C = exp(G_C), lam_p = exp(G_C - G_p)), sequential over the chunks of a
-// sequence.  A block of NW waves (4 or 8) owns 16 NW columns j of d_v of one
-// (sequence, head); wave w holds S^T (rows i of d_k, its 16 columns j) as
-// eight 16 x 16 accumulator tiles.  Every column is computed the same way
-// whatever the block width; eight waves stage each chunk's W and K once for
-// the whole head.  In that layout accumulator register r of lane group g
-// is the B operand of the k-step in which lane group g supplies
-// k = 16 b + 4 g + r, so both contractions take their B operand straight from
-// registers: Delta (k = i) from the state, S' (k = p) from lam * Delta.
-// Summation orders: Delta starts from U and adds the k-steps (ib = 0..7,
-// r = 0..3); S' starts from gam_C S and adds the k-steps (pb = 0..3,
-// r = 0..3).  W and K (rows p) of a chunk sit in LDS; the next
-// chunk's W, K, U and G are fetched into registers while the current chunk
-// computes.  Decode resync runs this same kernel on the chunk buffers.
+// sequence, with fp32 operands as bf16 parts (above).  A block of NW waves (4
+// or 8) owns 16 NW columns j of d_v of one (sequence, head); wave w holds S^T
+// (rows i of d_k, its 16 columns j) as eight 16 x 16 accumulator tiles.
+// Every column is computed the same way whatever the block width.
+//
+// Contraction order.  A k block of 32 (kb) is spread over the lanes so that
+// both products take their B operand from accumulator tiles: lane group g
+// supplies, as element e, k = 32 kb + 16 (e / 4) + 4 g + e % 4, which is
+// register e % 4 of tile 2 kb + e / 4 of the state (Delta, k = i) or of
+// lam * Delta (S', k = p).  The A operands (W rows p, columns i; K^T rows i,
+// columns p) sit in LDS as parts in that same element order, so a lane reads
+// each part of its eight elements as one 16-byte word.  Summation orders:
+// Delta starts from -U and adds, for kb = 0..3, the six part products in the
+// order listed above (it is kept negated; S' takes lam * Delta from
+// (-lam) * (-Delta)); S' starts from gam_C S and adds, for the two k blocks of
+// p, the same six.
+//
+// Staging.  W and lam of chunk c + 1 are loaded during chunk c's Delta products
+// and written to LDS (as parts) during its S' products; K of chunk c + 1 is
+// loaded during chunk c's S' products and written during chunk c + 1's Delta
+// products.  The W and K^T buffers are then each written while the other is
+// read, with two barriers per chunk, and every load has a whole phase to
+// arrive.  Past the last chunk the loads reload the last chunk's operands,
+// which nothing reads: the loop body has no branches.  Decode resync runs
+// this same kernel on the chunk buffers.
 template <int C, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4))) void k_scan_mfma(ScanIO io,
                                                                                             int64_t nblocks,
                                                                                             int64_t nb8) {
-  constexpr int D = 128, WS = D + 4, NQ = C * D / 4 / (64 * NW);  // float4 of W (of K) per thread
-  constexpr int NB = D / (16 * NW);                                // blocks per (sequence, head)
+  constexpr int D = 128;
+  // 32-bit words per LDS row: 16 (W) or 8 (K^T) groups of three 16-byte
+  // parts, plus 16 bytes (rows l and l + 1 of a read then start 4 banks apart)
+  constexpr int WR = 16 * 12 + 4, KR = 8 * 12 + 4;
+  constexpr int NB = D / (16 * NW);  // blocks per (sequence, head)
+  constexpr int NR = 16 / NW;        // W rows per thread (one group of 8 columns each)
+  constexpr int KC = 16 / NW;        // K^T rows (key columns i) per thread (one group of 8 keys each)
+  constexpr int KCS = D / KC;        // threads per key group
   static_assert(C == 64 && (NW == 4 || NW == 8), "tiling assumes C = 64, D = 128");
   constexpr bool RESYNC = MODE == kResync;
-  // W, K and lam of chunk c sit in buffer c % NBUF (two buffers: the next
-  // chunk's operands go in while this chunk's are read; resync runs one step)
-  constexpr int NBUF = RESYNC ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) float sW[NBUF][C * WS];  // W[p][i]
-  __shared__ __attribute__((aligned(16))) float sK[NBUF][C * WS];  // K[p][i]
-  __shared__ float sLam[NBUF][C];
+  __shared__ __attribute__((aligned(16))) uint32_t sW[C * WR];  // W[p][group of i][part][8]
+  __shared__ __attribute__((aligned(16))) uint32_t sK[D * KR];  // K^T[i][group of p][part][8]
+  __shared__ float sLam[C];                                     // -lam_p
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // ordered launches keep the dispatch order, so the longest sequences start
@@ -625,23 +737,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
   }
   // buffer offsets (bytes): lane part in a VGPR, wave-uniform part in an SGPR
   const uint32_t fj = 4u * static_cast<uint32_t>(4 * g * D + j);  // (row 4 g, column j) of [.][D]
-  const int r0 = NQ * (tid >> 5), cq = tid & 31;  // this thread's rows r0 .. r0 + NQ - 1, column quad cq
-  const uint32_t fq = 4u * static_cast<uint32_t>(r0 * D + 4 * cq);
   const uint32_t kst = RESYNC ? static_cast<uint32_t>(io.H_qk) * D * 4u : 2 * D * 4u;  // key row stride
-  const uint32_t fk = static_cast<uint32_t>(r0) * kst + 16u * cq;
-
-  // One chunk step's operands: W and K rows p = r0 + m, column quad cq; U in
-  // accumulator layout (p = 16 pb + 4 g + r, j); G.  Chunk c + 1's K is
-  // loaded at the start of chunk c's Delta products and goes to LDS when they
-  // end; chunk c + 2's W and G are loaded at the start of chunk c's S'
-  // products and go to LDS (W negated, with lam) when they end, i.e. at the
-  // start of chunk c + 1.  Each prefetch thus has a whole phase to arrive,
-  // only one of them is held in registers at a time, and with the two LDS
-  // buffers one barrier per chunk orders every write after the last read of
-  // its buffer and before the first read of its data.  Past the last chunk
-  // the prefetches reload the last chunk's operands into the spare buffer,
-  // which nothing reads: the loop body has no branches (a branch costs an
-  // instruction refetch that one wave per SIMD cannot hide).
+  // W staging: rows wr0 .. wr0 + NR - 1, column group wg (columns 32 (wg / 4)
+  // + 4 (wg % 4) + 0..3 and + 16 + 0..3, elements 0..7 of the group)
+  const int wg = tid & 15, wr0 = (tid >> 4) * NR;
+  const uint32_t fw = 4u * static_cast<uint32_t>(wr0 * D + 32 * (wg >> 2) + 4 * (wg & 3));
+  // K staging: key group kg (keys p = 32 (kg / 4) + 16 (e / 4) + 4 (kg % 4) +
+  // e % 4 for e = 0..7) at columns kc + KCS c, c < KC (consecutive lanes take
+  // consecutive columns: coalesced loads, conflict-free LDS writes)
+  const int kg = tid / KCS, kc = tid % KCS;
+  const uint32_t fk = static_cast<uint32_t>(32 * (kg >> 2) + 4 * (kg & 3)) * kst + 4u * kc;
   struct OpRes {
     brsrc_t rk, rw, ru;
     int64_t sh;
@@ -657,18 +762,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
     r.ru = make_rsrc(io.U + r.sh * CD, C * D * 4u);
     return r;
   };
-  float4 pw[NQ], pk[NQ];
+  float pw[NR][8], pk[8][KC];
   float un[4][4];
   float gvn = 0.0f, glastn = 0.0f;
-  auto load_w = [&](const OpRes& rs) {  // W rows r0 + m, and G (element lane of every wave)
+  auto load_w = [&](const OpRes& rs) {  // W rows wr0 + m, and G (element lane of every wave)
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) pw[m] = ldbuf4(rs.rw, fq, static_cast<uint32_t>(m * D * 4));
+    for (int m = 0; m < NR; ++m)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const float4 x = ldbuf4(rs.rw, fw, static_cast<uint32_t>(m * D * 4 + 64 * hf));
+        pw[m][4 * hf] = x.x, pw[m][4 * hf + 1] = x.y, pw[m][4 * hf + 2] = x.z, pw[m][4 * hf + 3] = x.w;
+      }
     gvn = io.G[rs.sh * C + lane];
     glastn = io.G[rs.sh * C + C - 1];
   };
   auto load_k = [&](const OpRes& rs) {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) pk[m] = ldbuf4(rs.rk, fk + static_cast<uint32_t>(m) * kst, 0u);
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        pk[e][c] = ldbuf(rs.rk, fk, static_cast<uint32_t>(16 * (e >> 2) + (e & 3)) * kst + 4u * KCS * c,
+                         static_cast<const float*>(nullptr));
   };
   auto load_u = [&](const OpRes& rs, int m) {  // part m of 8: two of the U values
 #pragma unroll
@@ -677,21 +791,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
       un[pb][r] = ldbuf(rs.ru, fj, static_cast<uint32_t>((16 * pb + r) * D * 4), static_cast<const float*>(nullptr));
     }
   };
-  // W and K go to LDS as loaded (no register transpose: a transpose of the
-  // prefetched quads would make the loads complete before the chunk computes)
-  auto put_w = [&](int b) {
+  auto put_w = [&](int m) {  // W parts of row wr0 + m
+    const Parts x = split8(pw[m]);
+    uint32_t* d = &sW[(wr0 + m) * WR + 12 * wg];
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) {  // stored negated: Delta adds (-W) S^T
-      const float4 wv = pw[m];
-      *reinterpret_cast<float4*>(&sW[b][(r0 + m) * WS + 4 * cq]) = float4{-wv.x, -wv.y, -wv.z, -wv.w};
-    }
-    sLam[b][lane] = expf(glastn - gvn);  // every wave writes the same row (no branch)
+    for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4_t*>(d + 4 * q) = x.p[q];
   };
-  auto put_k = [&](int b) {
+  auto put_lam = [&]() { sLam[lane] = -expf(glastn - gvn); };  // every wave writes the row: no branch
+  auto put_k = [&](int c, const Parts& y) {  // K^T parts of key column kc + KCS c
+    uint32_t* d = &sK[(kc + KCS * c) * KR + 12 * kg];
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) *reinterpret_cast<float4*>(&sK[b][(r0 + m) * WS + 4 * cq]) = pk[m];
+    for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4_t*>(d + 4 * q) = y.p[q];
   };
-  auto buf = [](int64_t c) { return NBUF == 1 ? 0 : static_cast<int>(c & 1); };
+  auto k_col = [&](float (&x)[8], int c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = pk[e][c];
+  };
+  auto put_w_parts = [&](int m, const Parts& x) {  // W parts of row wr0 + m
+    uint32_t* d = &sW[(wr0 + m) * WR + 12 * wg];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4_t*>(d + 4 * q) = x.p[q];
+  };
+  auto tiles8 = [](float (&x)[8], v4f a, v4f b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = a[e], x[4 + e] = b[e];
+  };
 
   // S^T tiles (i = 16 ib + 4 g + r, j)
   v4f st[8];
@@ -713,118 +837,177 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
   };
 
   float glast = 0.0f;  // G at the end of the current chunk
-  if (nsteps > 0) {    // chunk 0's operands to LDS; chunk 1's W and G in flight
+  if (nsteps > 0) {    // chunk 0's W and lam to LDS, its K and U in registers
     const OpRes rs = op_res(0);
     load_w(rs);
     load_k(rs);
 #pragma unroll
     for (int m = 0; m < 8; ++m) load_u(rs, m);
-    put_w(0);
-    put_k(0);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) put_w(m);
+    put_lam();
     glast = glastn;
-    if (nsteps > 1) load_w(op_res(1));
   }
+  v4f dl[4];  // -Delta tiles (p = 16 pb + 4 g + r, j), started from -U
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[pb][r] = -un[pb][r];
+  Parts b = split8(st[0], st[1]);  // B parts of Delta's first k block
   __syncthreads();
-  for (int64_t c = 0; c < nsteps; ++c) {
-    const int64_t fs = fslot0 + c;
-    const int b = buf(c), nb = buf(c + 1);
-    const bool more = c + 1 < nsteps;
-    // ---- Delta tiles (p = 16 pb + 4 g + r, j) = U - W S^T, k = i
-    // (the four tiles' chains are interleaved; each keeps its own k order)
-    v4f dl[4];
+  // A operands: part q of W rows 16 pb + l16 in k block kb, of K^T rows
+  // 16 (4 h2 + t) + l16 in k block kp
+  auto read_w = [&](u32x4_t (&x)[4], int kb, int q) {
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
+      x[pb] = *reinterpret_cast<const u32x4_t*>(&sW[(16 * pb + l16) * WR + 12 * (4 * kb + g) + 4 * q]);
+  };
+  auto read_k = [&](u32x4_t (&x)[4], int kp, int h2, int q) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dl[pb][r] = un[pb][r];
-    // A operands (-W) are read from LDS one k block ahead of their use; the
-    // first read goes ahead of the writes to the other buffer
-    float4 a[2][4];
-    auto read_w = [&](float4 (&x)[4], int ib) {
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb)
-        x[pb] = *reinterpret_cast<const float4*>(&sW[b][(16 * pb + l16) * WS + 16 * ib + 4 * g]);
-    };
-    read_w(a[0], 0);
-    // chunk c + 1's W and lam (its buffer was last read in chunk c - 1)
-    if (NBUF == 2 || more) put_w(nb);
-    const float glast1 = more ? glastn : glast;
-    // chunk c + 1's K and U, and this chunk's start state (a store), are issued
-    // between the Delta products below
+    for (int t = 0; t < 4; ++t)
+      x[t] = *reinterpret_cast<const u32x4_t*>(&sK[(16 * (4 * h2 + t) + l16) * KR + 12 * (4 * kp + g) + 4 * q]);
+  };
+  // Each k block's products form one scheduling region with VALU work that
+  // does not depend on them (B parts of a later block, a share of the operand
+  // staging, the gam scaling of state tiles already used), one product to a
+  // few VALU instructions, so that the matrix core and the VALU run side by
+  // side.  Part 0 of a block's A operand is read one region ahead, parts 1
+  // and 2 at the start of their region (part 0's products cover them).
+  for (int64_t c = 0; c < nsteps; ++c) {
+    const int64_t fs = fslot0 + c;
+    const bool more = c + 1 < nsteps;
     const OpRes nres = op_res(more ? c + 1 : c);
-    load_k(nres);
     const brsrc_t rst = RESYNC ? make_rsrc(io.W, 0u)  // no chunk-start states in resync
                                : make_rsrc(io.states + ((slot0 + c) * io.H_v + h) * DD, D * D * 4u);
+    const float gam = expf(glast);
+    u32x4_t a0[4];
+    read_w(a0, 0, 0);
+    load_w(nres);  // chunk c + 1's W and G: to LDS during this chunk's S' products
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- -Delta = -U + W S^T, k = i (the four tiles' chains are
+    // interleaved; each keeps its own k order)
 #pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      const float4(&x)[4] = a[ib & 1];
-      if (ib + 1 < 8) read_w(a[(ib + 1) & 1], ib + 1);
-      __builtin_amdgcn_sched_barrier(0);  // the reads issue before this block's products
-      // each k-step's four products, then a row of the chunk-start state
-      // (rows 16 ib + 4 g + r; dropped in resync), the U loads after the second
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          const float xa = r == 0 ? x[pb].x : r == 1 ? x[pb].y : r == 2 ? x[pb].z : x[pb].w;
-          dl[pb] = mfma4(xa, st[ib][r], dl[pb]);
+    for (int kb = 0; kb < 4; ++kb) {
+      u32x4_t a1[4], a2[4], an[4];
+      read_w(a1, kb, 1);
+      read_w(a2, kb, 2);
+      if (kb + 1 < 4) read_w(an, kb + 1, 0);
+      // the next block's B parts and, on some blocks, a column of chunk c's
+      // K^T (its buffer was last read by chunk c - 1)
+      Parts bn = b;
+      if (kb % (4 / KC) == 0) {
+        float xk[8], xb[8];
+        k_col(xk, kb / (4 / KC));
+        Parts pk2;
+        if (kb + 1 < 4) {
+          tiles8(xb, st[2 * kb + 2], st[2 * kb + 3]);
+          split8x2(xb, xk, bn, pk2);
+        } else {
+          pk2 = split8(xk);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (!RESYNC) stbuf(st[ib][r], rst, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
-        if (r == 1) load_u(nres, ib);
-        __builtin_amdgcn_sched_barrier(0);
+        put_k(kb / (4 / KC), pk2);
+      } else if (kb + 1 < 4) {
+        bn = split8(st[2 * kb + 2], st[2 * kb + 3]);
       }
+      // tiles 2 kb, 2 kb + 1 of the chunk-start state (a store, dropped in
+      // resync), then scaled by gam_C for S'; two parts of chunk c + 1's U
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ib = 2 * kb + e / 4, r = e % 4;
+        if (!RESYNC) stbuf(st[ib][r], rst, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+      }
+      st[2 * kb] = gam * st[2 * kb];
+      st[2 * kb + 1] = gam * st[2 * kb + 1];
+      load_u(nres, 2 * kb);
+      load_u(nres, 2 * kb + 1);
+#pragma unroll
+      for (int bq = 0; bq < 3; ++bq)  // A part 0 with B parts 0..2, part 1 with 0..1, part 2 with 0
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma_bf(a0[pb], b.p[bq], dl[pb]);
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma_bf(a1[pb], b.p[bq], dl[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dl[pb] = mfma_bf(a2[pb], b.p[0], dl[pb]);
+      if (kb + 1 < 4) mfma_valu_pattern<24, 12>();
+      else mfma_valu_pattern<24, 8>();
+      __builtin_amdgcn_sched_barrier(0);
+      b = bn;
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) a0[pb] = an[pb];
     }
     if (MODE == kAll) {
       const brsrc_t rd = make_rsrc(io.Dl + (fs * io.H_v + h) * CD, C * D * 4u);
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) stbuf(dl[pb][r], rd, fj, static_cast<uint32_t>((16 * pb + r) * D * 4));
+        for (int r = 0; r < 4; ++r) stbuf(-dl[pb][r], rd, fj, static_cast<uint32_t>((16 * pb + r) * D * 4));
     }
-    // A operand K^T (i = 16 (4 h2 + q) + l16, p = 16 pb + 4 g + r), a column
-    // of K, read from LDS one group of four tiles ahead of its use; the first
-    // read and lam go ahead of the writes to the other buffer
-    float ak[2][4][4];
-    auto read_k = [&](float (&x)[4][4], int pb, int h2) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[q][r] = sK[b][(16 * pb + 4 * g + r) * WS + 16 * (4 * h2 + q) + l16];
-    };
-    read_k(ak[0], 0, 0);
-    float lam[4][4];
+    // lam * Delta = (-lam) * (-Delta)
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lam[pb][r] = sLam[b][16 * pb + 4 * g + r];
-    if (NBUF == 2 || more) put_k(nb);  // chunk c + 1's K (its buffer was last read in chunk c - 1)
+      for (int r = 0; r < 4; ++r) dl[pb][r] = dl[pb][r] * sLam[16 * pb + 4 * g + r];
+    __syncthreads();  // chunk c's K^T written; its W and lam read by every wave
+    // ---- S'^T (i, j) = gam_C S^T + K^T (lam Delta), k = p
+    read_k(a0, 0, 0, 0);
+    put_lam();  // chunk c + 1's (chunk c's was read before the barrier)
+    glast = more ? glastn : glast;
+    load_k(nres);  // chunk c + 1's K: to LDS during its Delta products
+    Parts b0 = b, b1 = b;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dl[pb][r] = dl[pb][r] * lam[pb][r];
-    // ---- S'^T tiles (i, j) = gam_C S^T + K^T (lam Delta), k = p
-    const float gam = expf(glast);
-#pragma unroll
-    for (int ib = 0; ib < 8; ++ib) st[ib] = gam * st[ib];
-    // chunk c + 2's W and G are issued ahead of the products
-    load_w(op_res(c + 2 < nsteps ? c + 2 : c));
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {  // two groups of four tiles
-        const int it = 2 * pb + h2;
-        const float(&x)[4][4] = ak[it & 1];
-        if (it + 1 < 8) read_k(ak[(it + 1) & 1], (it + 1) / 2, (it + 1) % 2);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(x[q][r], dl[pb][r], st[4 * h2 + q]);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int it = 0; it < 4; ++it) {  // k block kp, tiles 4 h2 .. 4 h2 + 3
+      const int kp = it / 2, h2 = it % 2;
+      u32x4_t a1[4], a2[4], an[4];
+      read_k(a1, kp, h2, 1);
+      read_k(a2, kp, h2, 2);
+      if (it + 1 < 4) read_k(an, (it + 1) / 2, (it + 1) % 2, 0);
+      // chunk c + 1's W rows (chunk c's was read before the barrier), with
+      // the second block's B parts, and the next chunk's first B parts
+      // (tiles 0..3 are final) and -U
+      if (it == 0) b0 = split8(dl[0], dl[1]);
+      const bool wrow = it % (4 / NR) == 0;
+      if (it == 1 || it == 3) {
+        float xb[8];
+        if (it == 1) tiles8(xb, dl[2], dl[3]);
+        else tiles8(xb, st[0], st[1]);
+        Parts& pb2 = it == 1 ? b1 : b;
+        if (wrow) {
+          Parts pw2;
+          split8x2(xb, pw[it / (4 / NR)], pb2, pw2);
+          put_w_parts(it / (4 / NR), pw2);
+        } else {
+          pb2 = split8(xb);
+        }
+      } else if (wrow) {
+        put_w(it / (4 / NR));
       }
+      if (it == 2) {
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dl[pb][r] = -un[pb][r];
+      }
+      const Parts& bb = kp == 0 ? b0 : b1;
+#pragma unroll
+      for (int bq = 0; bq < 3; ++bq)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) st[4 * h2 + t] = mfma_bf(a0[t], bb.p[bq], st[4 * h2 + t]);
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) st[4 * h2 + t] = mfma_bf(a1[t], bb.p[bq], st[4 * h2 + t]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) st[4 * h2 + t] = mfma_bf(a2[t], bb.p[0], st[4 * h2 + t]);
+      if (it + 1 < 4) mfma_valu_pattern<24, 12>();
+      else mfma_valu_pattern<24, 8>();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a0[t] = an[t];
     }
-    glast = glast1;
-    __syncthreads();  // chunk c's buffers are free and chunk c + 1's are written
+    __syncthreads();  // chunk c's K^T read; chunk c + 1's W and lam written
   }
 
   if (RESYNC) {
@@ -3349,8 +3532,6 @@ constexpr int scan_tile() { return D == 128 ? kTile128 : D; }
 
 // Blocks of the persistent backward kernels: one per CU.
 constexpr int64_t kPersistentBlocks = 256;
-// Dynamic LDS that leaves room for one 4-wave k_scan_mfma block per CU (160 KB).
-constexpr unsigned kScanSoloLds = 24 * 1024;
 
 // Value heads per k_rec block: as many of the group as fit in 8 waves and
 // divide the group evenly (the group has at most 8 heads).
@@ -3395,7 +3576,7 @@ void launch_scan(const ScanIO& io, int64_t N, int H_v, hipStream_t st) {
   const int64_t blocks = N * H_v * (D / TILE);
   if (blocks <= 0) return;
   if constexpr (D == 128) {  // blocks of 64 columns of d_v
-    // Half a head per block of 4 waves, one block per CU (extra LDS keeps two
+    // Half a head per block of 4 waves, one block per CU (its LDS keeps two
     // off a CU), while they are no more than the CUs: each chain then has a
     // SIMD per wave.  Past that, a head per block of 8 waves, which stages
     // each chunk's W and K once for all 128 columns.
@@ -3407,8 +3588,8 @@ void launch_scan(const ScanIO& io, int64_t N, int H_v, hipStream_t st) {
       hipLaunchKernelGGL((k_scan_mfma<C, MODE, 8>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, st,
                          io, mblocks, nb8);
     else
-      hipLaunchKernelGGL((k_scan_mfma<C, MODE, 4>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                         kScanSoloLds, st, io, mblocks, nb8);
+      hipLaunchKernelGGL((k_scan_mfma<C, MODE, 4>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                         io, mblocks, nb8);
   } else {
     hipLaunchKernelGGL((k_scan<D, C, TILE, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256),
                        0, st, io);
@@ -4225,8 +4406,8 @@ int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
 }
 
 const char* gdn_contract_id(void) {
-  return "gdn-cpr/v8;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
-         "B=mfma16x16x4-wy-blocked16-diaginv,mfma16x16x4-scan-regB;prep=wave-butterfly;src=" GDN_SOURCE_DIGEST;
+  return "gdn-cpr/v9;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
+         "B=mfma16x16x4-wy-blocked16-diaginv,bf16x3-mfma16x16x32-scan-regB;prep=wave-butterfly;src=" GDN_SOURCE_DIGEST;
 }
 
 int gdn_contract_check(const char* id) {
