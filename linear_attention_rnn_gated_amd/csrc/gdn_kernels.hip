@@ -74,6 +74,11 @@ __device__ __forceinline__ brsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ float ldbuf(brsrc_t r, uint32_t voff, uint32_t soff, const float*) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void stbuf4(v4f x, brsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(4))), x), r, voff, soff, 0);
+}
 __device__ __forceinline__ void stbuf(float x, brsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
 }
@@ -398,6 +403,12 @@ __global__ __launch_bounds__(256) void k_wy(ChunkIO io) {
 // start state, and the final state when the sequence ends on a chunk edge.
 // Resync: one step from cache S_chunk for each (sequence, head) with pos == 0,
 // writing S_chunk = S_run = result.
+// Row quads.  At d = 128 outside the all-chunks mode, the prefill's
+// chunk-start states [d][d] keep each run of four consecutive rows of a
+// column together: element (r, j) sits at ((r / 4) d + j) 4 + r % 4.  A lane
+// that holds rows 4 q .. 4 q + 3 of column j (the scan's accumulator layout,
+// the token step's row part) then moves them with one 16-byte access, and
+// consecutive columns are consecutive 16-byte words.
 struct ScanIO {
   const float* khat;     // prefill: prep keys; resync: cache kbuf
   const float* W;
@@ -545,7 +556,6 @@ __global__ __launch_bounds__(256) void k_scan(ScanIO io) {
 // Matrix-core helpers.  mfma4 is v_mfma_f32_16x16x4_f32 on one 16 x 16 tile:
 // lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], and holds
 // D[4 (l / 16) + r][l % 16] in accumulator register r.
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -737,6 +747,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
   }
   // buffer offsets (bytes): lane part in a VGPR, wave-uniform part in an SGPR
   const uint32_t fj = 4u * static_cast<uint32_t>(4 * g * D + j);  // (row 4 g, column j) of [.][D]
+  const uint32_t fq4 = 16u * static_cast<uint32_t>(g * D + j);     // (quad g, column j) in row quads
   const uint32_t kst = RESYNC ? static_cast<uint32_t>(io.H_qk) * D * 4u : 2 * D * 4u;  // key row stride
   // W staging: rows wr0 .. wr0 + NR - 1, column group wg (columns 32 (wg / 4)
   // + 4 (wg % 4) + 0..3 and + 16 + 0..3, elements 0..7 of the group)
@@ -835,6 +846,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
 #pragma unroll
       for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rd, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
   };
+  // a chunk-start state: row quads outside the all-chunks mode
+  auto store_start_tile = [&](const brsrc_t& rd, int ib) {
+    if constexpr (MODE != kAll) {
+      stbuf4(st[ib], rd, fq4, static_cast<uint32_t>(ib) * 4 * D * 16);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stbuf(st[ib][r], rd, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+    }
+  };
 
   float glast = 0.0f;  // G at the end of the current chunk
   if (nsteps > 0) {    // chunk 0's W and lam to LDS, its K and U in registers
@@ -910,14 +930,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
         bn = split8(st[2 * kb + 2], st[2 * kb + 3]);
       }
       // tiles 2 kb, 2 kb + 1 of the chunk-start state (a store, dropped in
-      // resync), then scaled by gam_C for S'; two parts of chunk c + 1's U
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ib = 2 * kb + e / 4, r = e % 4;
-        if (!RESYNC) stbuf(st[ib][r], rst, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+      // resync) and two parts of chunk c + 1's U.  The all-chunks mode then
+      // scales them by gam_C for S' here; the others store 16 bytes per lane
+      // and scale past the next barrier, so that no write of a wide store's
+      // data registers follows it closely.
+      if (!RESYNC) {
+        store_start_tile(rst, 2 * kb);
+        store_start_tile(rst, 2 * kb + 1);
       }
-      st[2 * kb] = gam * st[2 * kb];
-      st[2 * kb + 1] = gam * st[2 * kb + 1];
+      if constexpr (MODE == kAll) {
+        st[2 * kb] = gam * st[2 * kb];
+        st[2 * kb + 1] = gam * st[2 * kb + 1];
+      }
       load_u(nres, 2 * kb);
       load_u(nres, 2 * kb + 1);
 #pragma unroll
@@ -950,7 +974,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
 #pragma unroll
       for (int r = 0; r < 4; ++r) dl[pb][r] = dl[pb][r] * sLam[16 * pb + 4 * g + r];
     __syncthreads();  // chunk c's K^T written; its W and lam read by every wave
-    // ---- S'^T (i, j) = gam_C S^T + K^T (lam Delta), k = p
+    // ---- S'^T (i, j) = gam_C S^T + K^T (lam Delta), k = p (outside the
+    // all-chunks mode tiles 0..3 are scaled by gam_C here, tiles 4..7 beside
+    // the first products, into tiles 0..3)
+    if constexpr (MODE != kAll) {
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) st[ib] = gam * st[ib];
+    }
     read_k(a0, 0, 0, 0);
     put_lam();  // chunk c + 1's (chunk c's was read before the barrier)
     glast = more ? glastn : glast;
@@ -967,7 +997,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
       // chunk c + 1's W rows (chunk c's was read before the barrier), with
       // the second block's B parts, and the next chunk's first B parts
       // (tiles 0..3 are final) and -U
-      if (it == 0) b0 = split8(dl[0], dl[1]);
+      if (it == 0) {
+        b0 = split8(dl[0], dl[1]);
+        if constexpr (MODE != kAll) {
+#pragma unroll
+          for (int ib = 4; ib < 8; ++ib) st[ib] = gam * st[ib];
+        }
+      }
       const bool wrow = it % (4 / NR) == 0;
       if (it == 1 || it == 3) {
         float xb[8];
@@ -1021,7 +1057,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
     return;
   }
   if (tail) {
-    store_state(io.states + ((slot0 + nsteps) * io.H_v + h) * DD);  // tail chunk start
+    {  // tail chunk start
+      const brsrc_t rd = make_rsrc(io.states + ((slot0 + nsteps) * io.H_v + h) * DD, D * D * 4u);
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib) store_start_tile(rd, ib);
+    }
     if (io.S_chunk) store_state(io.S_chunk + nh * DD);
   } else {
     if (io.hT) store_state(io.hT + nh * DD);
@@ -1409,7 +1449,7 @@ struct RecIO {
   const float* gb;   // (g, beta) per value head in token order [H_v][T][2]
   const int32_t* cu;
   const int32_t* cu_chunks;
-  const float* states;
+  const float* states;  // prefill at d = 128: row quads
   float* o;
   float* hT;       // nullable
   // cache (nullable): the tail chunk leaves its running state and tokens
@@ -1442,7 +1482,7 @@ struct RowSplit {
 // same key/query stream share a CU and its scalar cache; blockIdx.z continues
 // a group of more heads.  Wave (head, row part, d_k part) = index within the
 // block in that order, d_k part fastest.
-template <int D, int C, typename TIn, bool SPREAD>
+template <int D, int C, typename TIn, bool SPREAD, bool QUAD>  // QUAD: states in row quads
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k_rec(RecIO io, int hpb) {
   using RS = RowSplit<D>;
   constexpr int DK = RS::DK, KS = RS::KS, NH = RS::NH;
@@ -1502,9 +1542,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   __syncthreads();
 
   float s[DK];
-  const float* st = io.states + (static_cast<int64_t>(slot) * io.H_v + h) * DD + jc;
+  const float* st = io.states + (static_cast<int64_t>(slot) * io.H_v + h) * DD;
+  if constexpr (QUAD) {  // rows i0 + 4 m .. + 3 of column jc in 16 bytes
 #pragma unroll
-  for (int i = 0; i < DK; ++i) s[i] = st[static_cast<int64_t>(i0 + i) * D];
+    for (int m = 0; m < DK / 4; ++m) {
+      const float4 x = *reinterpret_cast<const float4*>(st + (static_cast<int64_t>(i0 / 4 + m) * D + jc) * 4);
+      s[4 * m] = x.x, s[4 * m + 1] = x.y, s[4 * m + 2] = x.z, s[4 * m + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DK; ++i) s[i] = st[static_cast<int64_t>(i0 + i) * D + jc];
+  }
 
   // key (t) / query (t) / key (t+1) streams, 2*D floats per token
   cfloat_p kq = as_const(io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D + i0);
@@ -3681,9 +3729,9 @@ int launch_prefill(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     const int hpb = rec_heads_per_block<D>(G);
     const dim3 rgrid(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb), rblock(64 * RowSplit<D>::WPH * hpb);
     if (rec_spread<D>(hpb))
-      hipLaunchKernelGGL((k_rec<D, C, TIn, true>), rgrid, rblock, 0, st, io, hpb);
+      hipLaunchKernelGGL((k_rec<D, C, TIn, true, D == 128>), rgrid, rblock, 0, st, io, hpb);
     else
-      hipLaunchKernelGGL((k_rec<D, C, TIn, false>), rgrid, rblock, 0, st, io, hpb);
+      hipLaunchKernelGGL((k_rec<D, C, TIn, false, D == 128>), rgrid, rblock, 0, st, io, hpb);
   }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -3903,9 +3951,9 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     const int hpb = rec_heads_per_block<D>(G);
     const dim3 rgrid(static_cast<unsigned>(cnt.chunks), s->H_qk, G / hpb), rblock(64 * RowSplit<D>::WPH * hpb);
     if (rec_spread<D>(hpb))
-      hipLaunchKernelGGL((k_rec<D, C, TIn, true>), rgrid, rblock, 0, st, io, hpb);
+      hipLaunchKernelGGL((k_rec<D, C, TIn, true, false>), rgrid, rblock, 0, st, io, hpb);
     else
-      hipLaunchKernelGGL((k_rec<D, C, TIn, false>), rgrid, rblock, 0, st, io, hpb);
+      hipLaunchKernelGGL((k_rec<D, C, TIn, false, false>), rgrid, rblock, 0, st, io, hpb);
   }
   // backward
   BwdIO b{};
