@@ -754,10 +754,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
   const int wg = tid & 15, wr0 = (tid >> 4) * NR;
   const uint32_t fw = 4u * static_cast<uint32_t>(wr0 * D + 32 * (wg >> 2) + 4 * (wg & 3));
   // K staging: key group kg (keys p = 32 (kg / 4) + 16 (e / 4) + 4 (kg % 4) +
-  // e % 4 for e = 0..7) at columns kc + KCS c, c < KC (consecutive lanes take
-  // consecutive columns: coalesced loads, conflict-free LDS writes)
+  // e % 4 for e = 0..7) at columns KC kc .. KC kc + KC - 1, one 4 KC-byte load
+  // per key (consecutive lanes take consecutive columns: coalesced).  In LDS
+  // the group of row i sits at slot kg ^ ((i / 8) % 8): the writes (rows KC
+  // apart in consecutive lanes) and the A-operand reads are both free of bank
+  // conflicts.
   const int kg = tid / KCS, kc = tid % KCS;
-  const uint32_t fk = static_cast<uint32_t>(32 * (kg >> 2) + 4 * (kg & 3)) * kst + 4u * kc;
+  const uint32_t fk = static_cast<uint32_t>(32 * (kg >> 2) + 4 * (kg & 3)) * kst + 4u * KC * kc;
+  const int kslot = kg ^ (((KC * kc) >> 3) & 7);  // the same for the thread's KC rows
   struct OpRes {
     brsrc_t rk, rw, ru;
     int64_t sh;
@@ -789,11 +793,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
   };
   auto load_k = [&](const OpRes& rs) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-        pk[e][c] = ldbuf(rs.rk, fk, static_cast<uint32_t>(16 * (e >> 2) + (e & 3)) * kst + 4u * KCS * c,
-                         static_cast<const float*>(nullptr));
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t so = static_cast<uint32_t>(16 * (e >> 2) + (e & 3)) * kst;
+      if constexpr (KC == 4) {
+        const float4 x = ldbuf4(rs.rk, fk, so);
+        pk[e][0] = x.x, pk[e][1] = x.y, pk[e][2] = x.z, pk[e][3] = x.w;
+      } else {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs.rk, fk, so, 0);
+        pk[e][0] = __uint_as_float(x[0]), pk[e][1] = __uint_as_float(x[1]);
+      }
+    }
   };
   auto load_u = [&](const OpRes& rs, int m) {  // part m of 8: two of the U values
 #pragma unroll
@@ -809,8 +818,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
     for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4_t*>(d + 4 * q) = x.p[q];
   };
   auto put_lam = [&]() { sLam[lane] = -expf(glastn - gvn); };  // every wave writes the row: no branch
-  auto put_k = [&](int c, const Parts& y) {  // K^T parts of key column kc + KCS c
-    uint32_t* d = &sK[(kc + KCS * c) * KR + 12 * kg];
+  auto put_k = [&](int c, const Parts& y) {  // K^T parts of key column KC kc + c
+    uint32_t* d = &sK[(KC * kc + c) * KR + 12 * kslot];
 #pragma unroll
     for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4_t*>(d + 4 * q) = y.p[q];
   };
@@ -884,8 +893,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
   };
   auto read_k = [&](u32x4_t (&x)[4], int kp, int h2, int q) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      x[t] = *reinterpret_cast<const u32x4_t*>(&sK[(16 * (4 * h2 + t) + l16) * KR + 12 * (4 * kp + g) + 4 * q]);
+    for (int t = 0; t < 4; ++t) {
+      const int i = 16 * (4 * h2 + t) + l16;  // slot of group 4 kp + g in row i (see the K staging)
+      x[t] = *reinterpret_cast<const u32x4_t*>(&sK[i * KR + 12 * ((4 * kp + g) ^ ((i >> 3) & 7)) + 4 * q]);
+    }
   };
   // Each k block's products form one scheduling region with VALU work that
   // does not depend on them (B parts of a later block, a share of the operand
