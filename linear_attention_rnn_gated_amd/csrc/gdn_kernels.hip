@@ -911,6 +911,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
     const brsrc_t rst = RESYNC ? make_rsrc(io.W, 0u)  // no chunk-start states in resync
                                : make_rsrc(io.states + ((slot0 + c) * io.H_v + h) * DD, D * D * 4u);
     const float gam = expf(glast);
+    float nlam[4][4];
     u32x4_t a0[4];
     read_w(a0, 0, 0);
     load_w(nres);  // chunk c + 1's W and G: to LDS during this chunk's S' products
@@ -955,6 +956,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
       }
       load_u(nres, 2 * kb);
       load_u(nres, 2 * kb + 1);
+      if (kb == 3) {  // -lam of the chunk's rows, read beside the last block's products
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) nlam[pb][r] = sLam[16 * pb + 4 * g + r];
+      }
 #pragma unroll
       for (int bq = 0; bq < 3; ++bq)  // A part 0 with B parts 0..2, part 1 with 0..1, part 2 with 0
 #pragma unroll
@@ -983,7 +990,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dl[pb][r] = dl[pb][r] * sLam[16 * pb + 4 * g + r];
+      for (int r = 0; r < 4; ++r) dl[pb][r] = dl[pb][r] * nlam[pb][r];
     __syncthreads();  // chunk c's K^T written; its W and lam read by every wave
     // ---- S'^T (i, j) = gam_C S^T + K^T (lam Delta), k = p (outside the
     // all-chunks mode tiles 0..3 are scaled by gam_C here, tiles 4..7 beside
