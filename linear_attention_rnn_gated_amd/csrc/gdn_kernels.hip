@@ -686,8 +686,8 @@ __device__ __forceinline__ void mfma_valu_pattern() {
 // (-lam) * (-Delta)); S' starts from gam_C S and adds, for the two k blocks of
 // p, the same six.
 //
-// Staging.  W and lam of chunk c + 1 are loaded during chunk c's Delta products
-// and written to LDS (as parts) during its S' products; K of chunk c + 1 is
+// Staging.  W and G of chunk c + 1 are loaded at the end of chunk c - 1's S'
+// products and W goes to LDS (as parts) during chunk c's S' products; K of chunk c + 1 is
 // loaded during chunk c's S' products and written during chunk c + 1's Delta
 // products.  The W and K^T buffers are then each written while the other is
 // read, with two barriers per chunk, and every load has a whole phase to
@@ -876,6 +876,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
     for (int m = 0; m < NR; ++m) put_w(m);
     put_lam();
     glast = glastn;
+    load_w(op_res(nsteps > 1 ? 1 : 0));  // chunk 1's W and G: to LDS during chunk 0's S' products
   }
   v4f dl[4];  // -Delta tiles (p = 16 pb + 4 g + r, j), started from -U
 #pragma unroll
@@ -914,7 +915,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
     float nlam[4][4];
     u32x4_t a0[4];
     read_w(a0, 0, 0);
-    load_w(nres);  // chunk c + 1's W and G: to LDS during this chunk's S' products
     __builtin_amdgcn_sched_barrier(0);
     // ---- -Delta = -U + W S^T, k = i (the four tiles' chains are
     // interleaved; each keeps its own k order)
@@ -1061,6 +1061,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)
 #pragma unroll
       for (int t = 0; t < 4; ++t) a0[t] = an[t];
     }
+    // chunk c + 2's W and G, issued where the wave waits at the barrier anyway
+    // rather than among the products, where each memory instruction held up
+    // the products behind it (to LDS during chunk c + 1's S' products)
+    load_w(op_res(c + 2 < nsteps ? c + 2 : nsteps - 1));
     __syncthreads();  // chunk c's K^T read; chunk c + 1's W and lam written
   }
 
