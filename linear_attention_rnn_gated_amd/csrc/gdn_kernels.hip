@@ -133,6 +133,39 @@ __device__ __forceinline__ void l2norm_vals(float x0, float x1, float mul, int d
   y0 = x0 * mul;
   y1 = x1 * mul;
 }
+// The same normalisation at d = 128 with sixteen lanes per vector, so that a
+// lane loads and stores its elements 8 or 16 bytes at a time: lane lam of the
+// group holds elements 4 lam + i (lo) and 64 + 4 lam + i (hi), i = 0..3.  The
+// sums are those of l2norm_vals: leaf l = fmaf(x[l + 64], x[l + 64], x[l] x[l]),
+// then pairs (l, l ^ m) for m = 32, 16, 8, 4, 2, 1.  With l = 4 lam + i the
+// pairs for m = 32 .. 4 are lanes lam ^ 8 .. lam ^ 1 with the same i, and for
+// m = 2, 1 they are i ^ 2, i ^ 1 within the lane; a pair's sum does not depend
+// on which of the two adds, so every result has l2norm_vals' bits.
+__device__ __forceinline__ void l2norm_quads(float4& lo, float4& hi, float mul, int do_norm) {
+  if (do_norm) {
+    float e0 = fmaf(hi.x, hi.x, lo.x * lo.x), e1 = fmaf(hi.y, hi.y, lo.y * lo.y);
+    float e2 = fmaf(hi.z, hi.z, lo.z * lo.z), e3 = fmaf(hi.w, hi.w, lo.w * lo.w);
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) {
+      e0 += __shfl_xor(e0, m, 64);
+      e1 += __shfl_xor(e1, m, 64);
+      e2 += __shfl_xor(e2, m, 64);
+      e3 += __shfl_xor(e3, m, 64);
+    }
+    const float r = 1.0f / sqrtf(((e0 + e2) + (e1 + e3)) + gdn::kNormEps);
+    lo = float4{lo.x * r, lo.y * r, lo.z * r, lo.w * r};
+    hi = float4{hi.x * r, hi.y * r, hi.z * r, hi.w * r};
+  }
+  lo = float4{lo.x * mul, lo.y * mul, lo.z * mul, lo.w * mul};
+  hi = float4{hi.x * mul, hi.y * mul, hi.z * mul, hi.w * mul};
+}
+// Four consecutive input elements as floats (16 bytes fp32, 8 bytes bf16).
+__device__ __forceinline__ float4 ld4in(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4in(const bf16_t* p) {
+  const uint2 x = *reinterpret_cast<const uint2*>(p);
+  return float4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u), __uint_as_float(x.y << 16),
+                __uint_as_float(x.y & 0xffff0000u)};
+}
 template <int D, typename TIn>
 __device__ __forceinline__ void l2norm_wave(const TIn* __restrict__ x, float mul, int do_norm,
                                             float& y0, float& y1) {
@@ -191,8 +224,9 @@ __global__ void k_order(const int32_t* __restrict__ cu, int N, int32_t* __restri
 // interleaved: qk[hq][t][0][:] = k-hat, qk[hq][t][1][:] = q-hat.  A chunk's
 // key/query stream for one head is then a single contiguous run, read by
 // k_rec as wave-uniform scalar loads.  Each wave normalises kPrepVecs
-// consecutive (token, q/k head) vectors, one at a time with the lanes and
-// arithmetic of l2norm_wave, after loading all of them.
+// consecutive (token, q/k head) vectors, after loading all of them: at
+// d = 128 four at a time with l2norm_quads, else one at a time with the lanes
+// and arithmetic of l2norm_wave.
 constexpr int kPrepVecs = 4;
 // (g, beta) of each value head in token order, gb[h][t] = (g[t][h], beta[t][h]):
 // the token step then reads a token's pair with one 8-byte scalar load, eight
@@ -222,6 +256,41 @@ __global__ __launch_bounds__(256) void k_prep(const TIn* __restrict__ q, const T
   const int64_t vec0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepVecs;
   if (vec0 >= nvec) return;
   const int l = threadIdx.x & 63;
+  if constexpr (D == 128) {
+    static_assert(kPrepVecs % 4 == 0, "whole lane groups");
+    constexpr int NR = kPrepVecs / 4;  // rounds of four vectors
+    const int lg = l >> 4, lam = l & 15;
+    float4 klo[NR], khi[NR], qlo[NR], qhi[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int64_t vr = vec0 + 4 * r + lg;
+      const int64_t vec = vr < nvec ? vr : nvec - 1;  // t * H_qk + hq
+      klo[r] = ld4in(k + vec * D + 4 * lam);
+      khi[r] = ld4in(k + vec * D + 64 + 4 * lam);
+      qlo[r] = ld4in(q + vec * D + 4 * lam);
+      qhi[r] = ld4in(q + vec * D + 64 + 4 * lam);
+    }
+    // (token, head) of vec0 once per wave; the lane's vector is a few past it
+    const int64_t t0 = vec0 / H_qk;
+    const int h0 = static_cast<int>(vec0 - t0 * H_qk);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int64_t vec = vec0 + 4 * r + lg;
+      l2norm_quads(klo[r], khi[r], 1.0f, l2);  // every lane: the shuffles read all of them
+      l2norm_quads(qlo[r], qhi[r], scale, l2);
+      if (vec < nvec) {
+        const int off = h0 + 4 * r + lg;  // < H_qk + kPrepVecs
+        const int64_t t = t0 + off / H_qk;
+        const int hq = off % H_qk;
+        float* out = qk + (static_cast<int64_t>(hq) * T + t) * 2 * D;
+        *reinterpret_cast<float4*>(out + 4 * lam) = klo[r];
+        *reinterpret_cast<float4*>(out + 64 + 4 * lam) = khi[r];
+        *reinterpret_cast<float4*>(out + D + 4 * lam) = qlo[r];
+        *reinterpret_cast<float4*>(out + D + 64 + 4 * lam) = qhi[r];
+      }
+    }
+    return;
+  }
   float k0[kPrepVecs], k1[kPrepVecs], q0[kPrepVecs], q1[kPrepVecs];
 #pragma unroll
   for (int v = 0; v < kPrepVecs; ++v) {
