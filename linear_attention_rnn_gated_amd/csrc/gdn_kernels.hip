@@ -2565,165 +2565,6 @@ __global__ __launch_bounds__(512) void k_chunk_o_m(BwdIO io) {
     }
 }
 
-// Chunk item `it` of the persistent backward kernels: items are (chunk slot,
-// value head) pairs, head fastest.  False if the item has no tokens.
-template <int C>
-__device__ __forceinline__ bool bwd_item_at(const BwdIO& io, int64_t it, int64_t& slot, int& h,
-                                            int64_t& tok0, int& L) {
-  slot = it / io.H_v;
-  h = static_cast<int>(it % io.H_v);
-  if (slot >= io.cu_chunks[io.N] || slot >= io.max_state_slot) return false;
-  const int n = find_seq(io.cu_chunks, io.N, slot);
-  tok0 = static_cast<int64_t>(io.cu[n]) + (slot - io.cu_chunks[n]) * C;
-  const int64_t end = io.cu[n + 1];
-  if (tok0 < 0 || end > io.T || tok0 >= end) return false;
-  L = static_cast<int>(end - tok0 < C ? end - tok0 : C);
-  return true;
-}
-
-// The three state products of a chunk on the matrix cores, and <S, dS'>:
-//   SdO[p][n] = sum_k dO[p][k] S[n][k]      SdD[p][n] = sum_k dDelta[p][k] S[n][k]
-//   DsD[p][n] = sum_k Delta[p][k] dS'[n][k]  MdM = sum_{n,k} S[n][k] dS'[n][k]
-// with S, dS' in their stored layout.  Persistent blocks of 8 waves walk the
-// (chunk, head) items.  The three C x D operands of an item sit in LDS (the
-// next item's are fetched into registers while the current one computes);
-// wave w streams rows 16 w .. 16 w + 15 of S and dS' from memory once, each
-// row feeding four 16-row tiles of every product.  k runs in steps of 16:
-// lane group g supplies k = 16 s + 4 g + c at component c, so each load of a
-// lane group covers 64 contiguous bytes of a row.
-template <int C>
-__global__ __launch_bounds__(512) void k_bwd_mm_m(BwdIO io, int64_t nitems) {
-  constexpr int D = 128, S1 = D + 4, NY = 3 * C * (D / 4) / 512;  // float4 per thread
-  static_assert(C == 64 && NY * 512 == 3 * C * (D / 4), "tiling assumes C = 64, D = 128");
-  __shared__ __attribute__((aligned(16))) float sY[3 * C * S1];
-  __shared__ float red[8];
-  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t DD = static_cast<int64_t>(D) * D, CD = static_cast<int64_t>(C) * D;
-  const float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  // this thread's share of an item's operands: rows tid / 32 + 16 m, column
-  // quad tid % 32, of dO (m = 0..3), dDelta (m = 4..7) and Delta (m = 8..11)
-  auto load_y = [&](float4 (&y)[NY], int64_t it) {
-    int64_t slot, tok0;
-    int h, L;
-    const bool ok = bwd_item_at<C>(io, it, slot, h, tok0, L);
-    if (!ok) {  // read row 0 of item 0 (in bounds) and zero it below
-      slot = 0;
-      h = 0;
-      tok0 = 0;
-      L = 1;
-    }
-    const int64_t sh = slot * io.H_v + h;
-    const int pr = tid >> 5, q4 = tid & 31;
-    const float* o0 = io.dO + (tok0 * io.H_v + h) * D + 4 * q4;
-    const float* o1 = io.dD + sh * CD + 4 * q4;
-    const float* o2 = io.Dl + sh * CD + 4 * q4;
-    const int64_t ors = static_cast<int64_t>(io.H_v) * D;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int p = pr + 16 * m;
-      const int pc = p < L ? p : L - 1;
-      const bool keep = ok && p < L;
-      const float4 x0 = *reinterpret_cast<const float4*>(o0 + pc * ors);
-      const float4 x1 = *reinterpret_cast<const float4*>(o1 + pc * D);
-      const float4 x2 = *reinterpret_cast<const float4*>(o2 + pc * D);
-      y[m] = sel4(keep, x0, z4);
-      y[4 + m] = sel4(keep, x1, z4);
-      y[8 + m] = sel4(keep, x2, z4);
-    }
-  };
-  float4 ypre[NY];
-  int64_t it = blockIdx.x;
-  if (it < nitems) load_y(ypre, it);
-  for (; it < nitems; it += gridDim.x) {
-    int64_t slot, tok0;
-    int h, L;
-    const bool ok = bwd_item_at<C>(io, it, slot, h, tok0, L);
-    const int64_t sh = ok ? slot * io.H_v + h : 0;
-    const int n = 16 * w + l16;  // the X row this lane streams
-    const float* x1 = io.states + sh * DD + n * D + 4 * g;
-    const float* x2 = io.dstates + sh * DD + n * D + 4 * g;
-    // this lane's 16-byte pieces of its S and dS' rows, one per k step, loaded
-    // two steps ahead (the first two before the staging barriers)
-    float4 p1[D / 16], p2[D / 16];
-    if (ok) {
-#pragma unroll
-      for (int s4 = 0; s4 < 2; ++s4) {
-        p1[s4] = *reinterpret_cast<const float4*>(x1 + 16 * s4);
-        p2[s4] = *reinterpret_cast<const float4*>(x2 + 16 * s4);
-      }
-    }
-    __syncthreads();  // the previous item's LDS reads are done
-#pragma unroll
-    for (int m = 0; m < NY; ++m)
-      *reinterpret_cast<float4*>(sY + ((m / 4) * C + (tid >> 5) + 16 * (m % 4)) * S1 +
-                                 4 * (tid & 31)) = ypre[m];
-    __syncthreads();
-    if (it + gridDim.x < nitems) load_y(ypre, it + gridDim.x);
-    if (!ok) continue;  // uniform over the block
-    v4f acc[3][4];
-#pragma unroll
-    for (int pr = 0; pr < 3; ++pr)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[pr][mb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    float mdm = 0.0f;
-#pragma unroll
-    for (int s4 = 0; s4 < D / 16; ++s4) {
-      if (s4 + 2 < D / 16) {
-        p1[s4 + 2] = *reinterpret_cast<const float4*>(x1 + 16 * (s4 + 2));
-        p2[s4 + 2] = *reinterpret_cast<const float4*>(x2 + 16 * (s4 + 2));
-      }
-      const float4 c1 = p1[s4], c2 = p2[s4];
-      mdm = fmaf(c1.x, c2.x, mdm);
-      mdm = fmaf(c1.y, c2.y, mdm);
-      mdm = fmaf(c1.z, c2.z, mdm);
-      mdm = fmaf(c1.w, c2.w, mdm);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int ro = (16 * mb + l16) * S1 + 16 * s4 + 4 * g;
-        const float4 y0 = *reinterpret_cast<const float4*>(sY + ro);
-        const float4 y1 = *reinterpret_cast<const float4*>(sY + C * S1 + ro);
-        const float4 y2 = *reinterpret_cast<const float4*>(sY + 2 * C * S1 + ro);
-        acc[0][mb] = mfma4(y0.x, c1.x, acc[0][mb]);
-        acc[1][mb] = mfma4(y1.x, c1.x, acc[1][mb]);
-        acc[2][mb] = mfma4(y2.x, c2.x, acc[2][mb]);
-        acc[0][mb] = mfma4(y0.y, c1.y, acc[0][mb]);
-        acc[1][mb] = mfma4(y1.y, c1.y, acc[1][mb]);
-        acc[2][mb] = mfma4(y2.y, c2.y, acc[2][mb]);
-        acc[0][mb] = mfma4(y0.z, c1.z, acc[0][mb]);
-        acc[1][mb] = mfma4(y1.z, c1.z, acc[1][mb]);
-        acc[2][mb] = mfma4(y2.z, c2.z, acc[2][mb]);
-        acc[0][mb] = mfma4(y0.w, c1.w, acc[0][mb]);
-        acc[1][mb] = mfma4(y1.w, c1.w, acc[1][mb]);
-        acc[2][mb] = mfma4(y2.w, c2.w, acc[2][mb]);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep each step's loads two steps ahead
-    }
-    // products out through buffer stores: lane part (row 4 g, column n) in a
-    // VGPR, the row block and row in an SGPR
-    const uint32_t fo = 4u * static_cast<uint32_t>(4 * g * D + n);
-#pragma unroll
-    for (int pr = 0; pr < 3; ++pr) {
-      const brsrc_t ro = make_rsrc((pr == 0 ? io.SdO : pr == 1 ? io.SdD : io.DsD) + sh * CD, C * D * 4u);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) stbuf(acc[pr][mb][r], ro, fo, static_cast<uint32_t>((16 * mb + r) * D * 4));
-    }
-    // <S, dS'>: wave butterfly, then the 8 wave sums in ascending order
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mdm = mdm + __shfl_xor(mdm, off, 64);
-    if (lane == 0) red[w] = mdm;
-    __syncthreads();
-    if (tid == 0) {
-      float t = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) t = t + red[q];
-      io.MdM[sh] = t;
-    }
-  }
-}
-
 // Reverse scan of the state gradient on the matrix cores, one block of 8
 // waves per (sequence, value head):
 //   dDelta = E + diag(lam) K dS'^T,   dS = gam_last dS' + (gam dO)^T Q - dDelta^T W.
@@ -2975,16 +2816,29 @@ __device__ __forceinline__ float oct_sum(float x) {
 
 // Per chunk and value head, on the matrix cores: gradients of q-hat, k-hat
 // (per value head), v, beta and g.  Eight waves (two per SIMD) share the LDS
-// tiles; row reductions use 8 lanes per row.
+// tiles; row reductions use 8 lanes per row.  The chunk's three state
+// products and <S, dS'> are formed here first, from S and dS' streamed out of
+// memory once (so they never make a round trip through memory):
+//   SdO[p][n] = sum_k dO[p][k] S[n][k]      SdD[p][n] = sum_k dDelta[p][k] S[n][k]
+//   DsD[p][n] = sum_k Delta[p][k] dS'[n][k]  MdM = sum_{n,k} S[n][k] dS'[n][k]
+// with S, dS' in their stored layout: wave w streams rows n = 16 w + l16,
+// which are its own output columns, and k runs in steps of 16 with lane
+// group g supplying k = 16 s + 4 g + c at component c.
 template <int C, typename TIn>
 __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   constexpr int D = 128, CS = C + 4, KS = D + 4, YS = 2 * D + 4;
   static_assert(C == 64, "tiling assumes C = 64");
-  __shared__ __attribute__((aligned(16))) float sQK[C * CS];   // QK, later F = E2 + E2^T
-  __shared__ __attribute__((aligned(16))) float sKG[C * CS];   // (k_p . k_r) Gam_pr, r < p
-  __shared__ __attribute__((aligned(16))) float sZ[C * CS];    // Z, later dA
+  // QK (later F = E2 + E2^T), KG = (k_p . k_r) Gam_pr (r < p), Z (later dA);
+  // before them dDelta (the products' operand), then DsD (row reads)
+  __shared__ __attribute__((aligned(16))) float sX[3 * C * CS];
+  static_assert(C * KS <= 2 * C * CS, "dDelta and DsD fit below Z");
+  float* sQK = sX;
+  float* sKG = sX + C * CS;
+  float* sZ = sX + 2 * C * CS;
+  float* sdD = sX;
+  __shared__ float red[8];
   __shared__ __attribute__((aligned(16))) float sK[C * KS];
-  __shared__ __attribute__((aligned(16))) float sY[2 * C * KS];  // dO | Delta, then Q, then Y
+  __shared__ __attribute__((aligned(16))) float sY[2 * C * KS];  // dO | Delta, then Q | SdO, then Y
   __shared__ float sG[C], sB[C], sGam[C], sdB[C];
   __shared__ __attribute__((aligned(16))) float sLam[C], skd[C];
   __shared__ __attribute__((aligned(16))) float sdG[C];
@@ -3004,8 +2858,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   const float* kq = io.qk + (static_cast<int64_t>(hq) * io.T + tok0) * 2 * D;
   const float* dO = io.dO + (tok0 * io.H_v + h) * D;
   const float* Dl = io.Dl + sh * CD;
-  const float* SdO = io.SdO + sh * CD;
-  const float* DsD = io.DsD + sh * CD;
+  const float* dDl = io.dD + sh * CD;
   const float* Wc = io.W + sh * CD;
   const float* Uc = io.U + sh * CD;
   const float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -3028,14 +2881,111 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     const float4 k4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
     const float4 o4 = *reinterpret_cast<const float4*>(dO + pc * vs + 4 * i4);
     const float4 d4 = *reinterpret_cast<const float4*>(Dl + p * D + 4 * i4);
+    const float4 dd4 = *reinterpret_cast<const float4*>(dDl + p * D + 4 * i4);
     *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) = sel4(p < L, k4, z4);
     *reinterpret_cast<float4*>(sO + p * KS + 4 * i4) = sel4(p < L, o4, z4);
     *reinterpret_cast<float4*>(sD + p * KS + 4 * i4) = sel4(p < L, d4, z4);
+    *reinterpret_cast<float4*>(sdD + p * KS + 4 * i4) = sel4(p < L, dd4, z4);
+  }
+  // this lane's 16-byte pieces of its S and dS' rows, one per k step, loaded
+  // two steps ahead (the first two before the staging barrier)
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const float* xs1 = io.states + sh * DD + col * D + 4 * g;
+  const float* xs2 = io.dstates + sh * DD + col * D + 4 * g;
+  float4 p1[D / 16], p2[D / 16];
+#pragma unroll
+  for (int s4 = 0; s4 < 2; ++s4) {
+    p1[s4] = *reinterpret_cast<const float4*>(xs1 + 16 * s4);
+    p2[s4] = *reinterpret_cast<const float4*>(xs2 + 16 * s4);
   }
   __syncthreads();
-  // Operands of later phases are fetched ahead of their use, after the loads
-  // that the current phase waits for (memory counters retire in order): Q
-  // and, in accumulator layout (rows 16 mb + 4 g + r, column col), SdO and DsD.
+  const float glast = sG[C - 1];
+  if (tid < C) {
+    sGam[tid] = expf(sG[tid]);
+    sLam[tid] = expf(glast - sG[tid]);
+  }
+  // ---- the state products (accumulator layout: rows 16 mb + 4 g + r, column col)
+  v4f acc[3][4];  // SdO, SdD, DsD
+#pragma unroll
+  for (int pr = 0; pr < 3; ++pr)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[pr][mb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  float mdm = 0.0f;
+#pragma unroll
+  for (int s4 = 0; s4 < D / 16; ++s4) {
+    if (s4 + 2 < D / 16) {
+      p1[s4 + 2] = *reinterpret_cast<const float4*>(xs1 + 16 * (s4 + 2));
+      p2[s4 + 2] = *reinterpret_cast<const float4*>(xs2 + 16 * (s4 + 2));
+    }
+    const float4 c1 = p1[s4], c2 = p2[s4];
+    mdm = fmaf(c1.x, c2.x, mdm);
+    mdm = fmaf(c1.y, c2.y, mdm);
+    mdm = fmaf(c1.z, c2.z, mdm);
+    mdm = fmaf(c1.w, c2.w, mdm);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int ro = (16 * mb + l16) * KS + 16 * s4 + 4 * g;
+      const float4 y0 = *reinterpret_cast<const float4*>(sO + ro);
+      const float4 y1 = *reinterpret_cast<const float4*>(sdD + ro);
+      const float4 y2 = *reinterpret_cast<const float4*>(sD + ro);
+      acc[0][mb] = mfma4(y0.x, c1.x, acc[0][mb]);
+      acc[1][mb] = mfma4(y1.x, c1.x, acc[1][mb]);
+      acc[2][mb] = mfma4(y2.x, c2.x, acc[2][mb]);
+      acc[0][mb] = mfma4(y0.y, c1.y, acc[0][mb]);
+      acc[1][mb] = mfma4(y1.y, c1.y, acc[1][mb]);
+      acc[2][mb] = mfma4(y2.y, c2.y, acc[2][mb]);
+      acc[0][mb] = mfma4(y0.z, c1.z, acc[0][mb]);
+      acc[1][mb] = mfma4(y1.z, c1.z, acc[1][mb]);
+      acc[2][mb] = mfma4(y2.z, c2.z, acc[2][mb]);
+      acc[0][mb] = mfma4(y0.w, c1.w, acc[0][mb]);
+      acc[1][mb] = mfma4(y1.w, c1.w, acc[1][mb]);
+      acc[2][mb] = mfma4(y2.w, c2.w, acc[2][mb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep each step's loads two steps ahead
+  }
+  // <S, dS'>: wave butterfly, then the 8 wave sums in ascending order (tid 0)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mdm = mdm + __shfl_xor(mdm, off, 64);
+  if (lane == 0) red[w] = mdm;
+  // the right-hand side of the back substitution, columns col of -SdD and of
+  // dDelta: SdD from the products, dDelta from its LDS tile
+  float rh[4][2][4];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      rh[bi][0][r] = acc[1][bi][r];
+      rh[bi][1][r] = sdD[(16 * bi + 4 * g + r) * KS + col];
+    }
+  __syncthreads();  // the products' reads of dDelta are done: DsD takes its place
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sdD[(16 * mb + 4 * g + r) * KS + col] = acc[2][mb][r];
+  float MdM = 0.0f;  // thread 0's
+  if (tid == 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) MdM = MdM + red[q];
+  }
+  __syncthreads();
+  // the dG term through the state update, k . DsD per row (8 lanes per row,
+  // each a 16-element chain over its part)
+  {
+    const int pp = tid >> 3, part = tid & 7;
+    float kd = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = 16 * part + 4 * m;
+      const float4 rD = *reinterpret_cast<const float4*>(sdD + pp * KS + i);
+      kd = fmaf(sK[pp * KS + i], rD.x, kd);
+      kd = fmaf(sK[pp * KS + i + 1], rD.y, kd);
+      kd = fmaf(sK[pp * KS + i + 2], rD.z, kd);
+      kd = fmaf(sK[pp * KS + i + 3], rD.w, kd);
+    }
+    kd = oct_sum(kd);
+    if (part == 0) skd[pp] = pp < L ? kd : 0.0f;
+  }
+  // Operands of later phases are fetched ahead of their use: Q.
 #pragma unroll
   for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
     const int e = tid + 512 * e_;
@@ -3047,15 +2997,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pS[mb][r] = SdO[(16 * mb + 4 * g + r) * D + col];
-      pD[mb][r] = DsD[(16 * mb + 4 * g + r) * D + col];
+      pS[mb][r] = acc[0][mb][r];
+      pD[mb][r] = acc[2][mb][r];
     }
-  const float glast = sG[C - 1];
-  if (tid < C) {
-    sGam[tid] = expf(sG[tid]);
-    sLam[tid] = expf(glast - sG[tid]);
-  }
-  const float MdM = io.MdM[sh];
   // ---- Z = (dO Delta^T) . Gam, masked r <= p
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -3096,29 +3040,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     }
   }
   __syncthreads();
-  // fetched ahead: SdO and DsD as row segments (row tid / 8, 16 elements) for
-  // the dG terms, and the right-hand side of the back substitution (wave w:
-  // columns 32 w .. 32 w + 31 of [SdD | dDelta]); all inside the chunk's slabs
-  float4 rS[4], rD[4];
-  {
-    const int pp = tid >> 3, part = tid & 7;
+  // SdO into Delta's old place, for the row reads of the dG terms below
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      rS[m] = *reinterpret_cast<const float4*>(SdO + pp * D + 16 * part + 4 * m);
-      rD[m] = *reinterpret_cast<const float4*>(DsD + pp * D + 16 * part + 4 * m);
-    }
-  }
-  float rh[4][2][4];
-  {
-    const int col0 = 32 * w;
-    const float* rhs = w < 4 ? io.SdD + sh * CD + col0 : io.dD + sh * CD + (col0 - D);
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rh[bi][ct][r] = rhs[(16 * bi + 4 * g + r) * D + 16 * ct + l16];
-  }
+    for (int r = 0; r < 4; ++r) sD[(16 * mb + 4 * g + r) * KS + col] = pS[mb][r];
   // ---- dq-hat = gam SdO + Z K  and  dk-hat (partial) = lam DsD + Z^T Q; wave w
   // owns columns i = 16 w + l16, all four row blocks
   v4f dk[4];
@@ -3140,21 +3066,19 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
       if (pp < L) io.dqv[(tok0 + pp) * vs + static_cast<int64_t>(h) * D + col] = aq[r];
     }
   }
+  __syncthreads();  // the SdO tile is written
   // ---- dG terms through O and the state update (8 lanes per row)
   {
     const int pp = tid >> 3, part = tid & 7;
-    float qs = 0.0f, kd = 0.0f, zq = 0.0f;
+    float qs = 0.0f, zq = 0.0f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int i = 16 * part + 4 * m;
-      qs = fmaf(sQ[pp * KS + i], rS[m].x, qs);
-      kd = fmaf(sK[pp * KS + i], rD[m].x, kd);
-      qs = fmaf(sQ[pp * KS + i + 1], rS[m].y, qs);
-      kd = fmaf(sK[pp * KS + i + 1], rD[m].y, kd);
-      qs = fmaf(sQ[pp * KS + i + 2], rS[m].z, qs);
-      kd = fmaf(sK[pp * KS + i + 2], rD[m].z, kd);
-      qs = fmaf(sQ[pp * KS + i + 3], rS[m].w, qs);
-      kd = fmaf(sK[pp * KS + i + 3], rD[m].w, kd);
+      const float4 rS = *reinterpret_cast<const float4*>(sD + pp * KS + i);
+      qs = fmaf(sQ[pp * KS + i], rS.x, qs);
+      qs = fmaf(sQ[pp * KS + i + 1], rS.y, qs);
+      qs = fmaf(sQ[pp * KS + i + 2], rS.z, qs);
+      qs = fmaf(sQ[pp * KS + i + 3], rS.w, qs);
     }
 #pragma unroll
     for (int r = 8 * part; r < 8 * part + 8; ++r) {
@@ -3166,14 +3090,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
       zq = r != pp ? t : zq;
     }
     qs = oct_sum(qs);
-    kd = oct_sum(kd);
     zq = oct_sum(zq);
-    if (part == 0) {
-      skd[pp] = pp < L ? kd : 0.0f;
-      sdG[pp] = pp < L ? (sGam[pp] * qs - sLam[pp] * kd) + zq : 0.0f;
-    }
+    if (part == 0) sdG[pp] = pp < L ? (sGam[pp] * qs - sLam[pp] * skd[pp]) + zq : 0.0f;
   }
-  __syncthreads();  // Q, QK, Z reads done; Y may overwrite Q
+  __syncthreads();  // Q, SdO, QK, Z reads done; Y may overwrite them
   if (tid == 0) {
     // rows q < L in ascending order; both rows are read 16 bytes at a time
     // first, and rows past L keep sacc (a select, not a shorter loop)
@@ -3190,7 +3110,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     sdG[L - 1] = sdG[L - 1] + sacc;
   }
   // ---- back substitution (I + A)^T Y = [-SdD | dDelta], A_pr = beta_p KG_pr,
-  // blocked by 16 rows from the bottom; wave w owns columns 32 w .. 32 w + 31
+  // blocked by 16 rows from the bottom; wave w owns columns col of -SdD (tile
+  // ct = 0) and of dDelta (ct = 1); every column is solved on its own
   // W and U rows of this wave's first dA tile, fetched while the back
   // substitution runs (the wave with no first tile fetches a valid row block)
   float4 pw[D / 16], pu[D / 16];
@@ -3214,8 +3135,6 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     for (int i = 0; i < 16; ++i) pv[i] = ldin(vin + i);
   }
   {
-    const int col0 = 32 * w;
-    const float sgn = w < 4 ? -1.0f : 1.0f;
     v4f Y[4][2];
 #pragma unroll
     for (int bi = 3; bi >= 0; --bi) {
@@ -3225,7 +3144,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int pp = 16 * bi + 4 * g + r;
-          const float x = sgn * rh[bi][ct][r];
+          const float x = (ct == 0 ? -1.0f : 1.0f) * rh[bi][ct][r];
           acc[ct][r] = pp < L ? x : 0.0f;
         }
 #pragma unroll
@@ -3258,7 +3177,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
       for (int ct = 0; ct < 2; ++ct) {
         Y[bi][ct] = acc[ct];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sY[(16 * bi + 4 * g + r) * YS + col0 + 16 * ct + l16] = acc[ct][r];
+        for (int r = 0; r < 4; ++r) sY[(16 * bi + 4 * g + r) * YS + ct * D + col] = acc[ct][r];
       }
     }
   }
@@ -4082,16 +4001,9 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     }
   }
   if (cnt.chunks > 0) {
-    {
+    if constexpr (D != 128) {  // (at d = 128 the chunk kernel forms the state products itself)
       Timed t_("k_bwd_mm", st);
-      if constexpr (D == 128) {
-        const int64_t nitems = cnt.chunks * s->H_v;
-        const int64_t nblk = nitems < kPersistentBlocks ? nitems : kPersistentBlocks;
-        hipLaunchKernelGGL((k_bwd_mm_m<C>), dim3(static_cast<unsigned>(nblk)), dim3(512), 0, st, b,
-                           nitems);
-      }
-      else
-        hipLaunchKernelGGL((k_bwd_mm<D, C>), cgrid, dim3(256), 0, st, b);
+      hipLaunchKernelGGL((k_bwd_mm<D, C>), cgrid, dim3(256), 0, st, b);
     }
     {
       Timed t_("k_bwd_chunk", st);
