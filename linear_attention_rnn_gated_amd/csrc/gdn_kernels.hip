@@ -3972,10 +3972,12 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
   b.E = reinterpret_cast<float*>(ws + L.E);
   b.dstates = reinterpret_cast<float*>(ws + L.dstates);
   b.dD = reinterpret_cast<float*>(ws + L.dD);
-  b.SdO = reinterpret_cast<float*>(ws + L.SdO);
-  b.DsD = reinterpret_cast<float*>(ws + L.DsD);
-  b.SdD = reinterpret_cast<float*>(ws + L.SdD);
-  b.MdM = reinterpret_cast<float*>(ws + L.MdM);
+  if (L.SdO) {  // (not allocated at d = 128)
+    b.SdO = reinterpret_cast<float*>(ws + L.SdO);
+    b.DsD = reinterpret_cast<float*>(ws + L.DsD);
+    b.SdD = reinterpret_cast<float*>(ws + L.SdD);
+    b.MdM = reinterpret_cast<float*>(ws + L.MdM);
+  }
   b.dqv = reinterpret_cast<float*>(ws + L.dqv);
   b.dkv = reinterpret_cast<float*>(ws + L.dkv);
   b.dv = dv; b.dbeta = dbeta; b.dg = dg; b.dq = dq; b.dk = dk; b.dh0 = dh0;

@@ -87,10 +87,12 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
     L.E = take(&cur, cd);
     L.dstates = take(&cur, L.state_slots * Hv * d * d * f);
     L.dD = take(&cur, cd);
-    L.SdO = take(&cur, cd);
-    L.DsD = take(&cur, cd);
-    L.SdD = take(&cur, cd);
-    L.MdM = take(&cur, L.state_slots * Hv * f);
+    if (d != 128) {  // at d = 128 the backward chunk kernel forms these itself
+      L.SdO = take(&cur, cd);
+      L.DsD = take(&cur, cd);
+      L.SdD = take(&cur, cd);
+      L.MdM = take(&cur, L.state_slots * Hv * f);
+    }
     L.dqv = take(&cur, T * Hv * d * f);
     L.dkv = take(&cur, T * Hv * d * f);
   }
