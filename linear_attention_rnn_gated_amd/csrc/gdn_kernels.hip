@@ -2567,27 +2567,36 @@ __global__ __launch_bounds__(512) void k_chunk_o_m(BwdIO io) {
 
 // Reverse scan of the state gradient on the matrix cores, one block of 8
 // waves per (sequence, value head):
-//   dDelta = E + diag(lam) K dS'^T,   dS = gam_last dS' + (gam dO)^T Q - dDelta^T W.
-// The state gradient is held transposed (rows i of d_k, columns j of d_v) in
+//   dDelta = E + diag(lam) K dS'^T,   dS = gam_last dS' + (gam dO)^T Q - dDelta^T W,
+// with fp32 operands as bf16 parts (as in the chunk scan).  The state
+// gradient is held transposed (rows i of d_k, columns j of d_v) in
 // accumulator layout: wave w owns columns j = 16 w .. 16 w + 15 as eight
-// 16 x 16 tiles (ib = 0..7).  In that layout accumulator register r of lane
-// group g is the B operand of the k-step that lane group g supplies as
-// k = 16 ib + 4 g + r, so dDelta (k = i) takes the state straight from
-// registers, and the update (k = p) takes dDelta and gam dO, held the same way,
-// straight from registers too.  Per chunk, K, Q and W (rows p) sit in LDS.
-// K is read only by the dDelta products and Q, W only by the update, so each
-// is refilled while the other is read: the previous chunk's K is loaded
-// during this chunk's dDelta products and written once they end; its Q, W
-// and G are loaded during the update and written once it ends.  Two barriers
-// per chunk, one prefetch in registers at a time, and no branch in the loop
-// (past chunk 0 the prefetches reload chunk 0 into buffers nothing reads).
+// 16 x 16 tiles (ib = 0..7).  A k block of 32 is spread over the lanes as in
+// the chunk scan (lane group g supplies element e as k = 32 kb + 16 (e / 4) +
+// 4 g + e % 4, register e % 4 of tile 2 kb + e / 4), so dDelta (k = i) takes
+// the state, and the update (k = p) takes gam dO and dDelta, straight from
+// accumulator tiles split into parts.  Summation orders: dDelta's products
+// start from 0 and add, for kb = 0..3, the six part products (then
+// fmaf(lam, ., E)); the update starts from gam_last dS' and adds the six
+// part products of Q^T (gam dO) for the two k blocks of p, then those of
+// (-W^T) dDelta.  (Two waves share a SIMD, so a block's A operand is read at
+// the start of its region: the other wave's products cover the reads.)  Per chunk, K (rows p, groups of i), and Q^T and -W^T (rows
+// i, groups of p; group slots XOR-swizzled by row as in the chunk scan) sit
+// in LDS as parts.  K is read only by the dDelta products and Q, W only by
+// the update, so each is written while the other is read: the previous
+// chunk's K is loaded during this chunk's dDelta products and split into LDS
+// beside the update's; its Q, W and G are loaded during the update and split
+// into LDS beside the next chunk's dDelta products.  Each k block's products
+// are one scheduling region with that VALU work.  Two barriers per chunk and
+// no branch in the loop (past chunk 0 the loads reload chunk 0).
 template <int C>
 __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
-  constexpr int D = 128, KS = D + 4, NQ = C * D / 4 / 512;  // float4 per thread
-  static_assert(C == 64 && NQ == 4, "tiling assumes C = 64, D = 128");
-  __shared__ __attribute__((aligned(16))) float sK[C * KS];  // K[p][i]
-  __shared__ __attribute__((aligned(16))) float sQ[C * KS];  // Q[p][i]
-  __shared__ __attribute__((aligned(16))) float sW[C * KS];  // W[p][i]
+  constexpr int D = 128;
+  constexpr int WR = 16 * 12 + 4, KR = 8 * 12 + 4;  // words per LDS row (parts + 16 bytes)
+  static_assert(C == 64, "tiling assumes C = 64, D = 128");
+  __shared__ __attribute__((aligned(16))) uint32_t sK[C * WR];  // K[p][group of i][part][8]
+  __shared__ __attribute__((aligned(16))) uint32_t sQ[D * KR];  // Q^T[i][slot of p group][part][8]
+  __shared__ __attribute__((aligned(16))) uint32_t sW[D * KR];  // -W^T, the same way
   __shared__ float sGam[C], sLam[C];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2612,11 +2621,17 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
   // SGPR.  Rows past a partial chunk's end are outside the range of the
   // chunk's K/Q and dO resources (range-checked lane offsets) and read 0.
   const uint32_t fj = 4u * static_cast<uint32_t>(4 * g * D + j);   // (p or i = 4 g, j) of [.][D]
-  const int r0 = 4 * (tid >> 5), cq = tid & 31;  // this thread's rows r0 .. r0 + 3, column quad cq
-  const uint32_t fq = 4u * static_cast<uint32_t>(r0 * 2 * D + 4 * cq);
-  const uint32_t fw = 4u * static_cast<uint32_t>(r0 * D + 4 * cq);
   const uint32_t ostride = static_cast<uint32_t>(io.H_v) * D * 4u;  // dO row stride
   const uint32_t fo = 4u * static_cast<uint32_t>(j) + static_cast<uint32_t>(4 * g) * ostride;
+  // K staging: rows kr0, kr0 + 1, column group kgp (columns 32 (kgp / 4) +
+  // 4 (kgp % 4) + 0..3 and + 16 + 0..3)
+  const int kgp = tid & 15, kr0 = (tid >> 4) * 2;
+  const uint32_t fk = 4u * static_cast<uint32_t>(kr0 * 2 * D + 32 * (kgp >> 2) + 4 * (kgp & 3));
+  // Q and W staging: key group qg (keys p = 32 (qg / 4) + 16 (e / 4) +
+  // 4 (qg % 4) + e % 4), columns 2 qc, 2 qc + 1 (8 bytes per key: coalesced)
+  const int qg = tid >> 6, qc = tid & 63;
+  const int qslot = qg ^ (((2 * qc) >> 3) & 7);  // the same for both columns
+  const int qp0 = 32 * (qg >> 2) + 4 * (qg & 3);
   auto rows_of = [&](int64_t c) { return static_cast<int>(Lseq - c * C < C ? Lseq - c * C : C); };
   struct OpRes {
     brsrc_t rq, rw;
@@ -2631,38 +2646,51 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
     r.rw = make_rsrc(io.W + r.sh * CD, C * D * 4u);
     return r;
   };
-  // chunk operands, this thread's rows p = r0 + m and column quad cq
-  float4 pk[NQ], pq[NQ], pw[NQ];
+  float pk[2][8], pq[8][2], pw[8][2];
   float gvn = 0.0f, glastn = 0.0f;  // G[lane] and G[C - 1]
   auto load_k = [&](const OpRes& rs) {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) pk[m] = ldbuf4(rs.rq, fq + static_cast<uint32_t>(m * 2 * D * 4), 0u);
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const float4 x = ldbuf4(rs.rq, fk + static_cast<uint32_t>(m * 2 * D * 4 + 64 * hf), 0u);
+        pk[m][4 * hf] = x.x, pk[m][4 * hf + 1] = x.y, pk[m][4 * hf + 2] = x.z, pk[m][4 * hf + 3] = x.w;
+      }
   };
   auto load_qw = [&](const OpRes& rs) {
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-      pq[m] = ldbuf4(rs.rq, fq + static_cast<uint32_t>(m * 2 * D * 4) + D * 4u, 0u);
-      pw[m] = ldbuf4(rs.rw, fw, static_cast<uint32_t>(m * D * 4));  // padded rows of W are 0
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t p = static_cast<uint32_t>(qp0 + 16 * (e >> 2) + (e & 3));
+      const auto xq = __builtin_amdgcn_raw_buffer_load_b64(rs.rq, (p * 2 * D + D + 2 * qc) * 4u, 0u, 0);
+      const auto xw = __builtin_amdgcn_raw_buffer_load_b64(rs.rw, (p * D + 2 * qc) * 4u, 0u, 0);  // padded rows of W are 0
+      pq[e][0] = __uint_as_float(xq[0]), pq[e][1] = __uint_as_float(xq[1]);
+      pw[e][0] = __uint_as_float(xw[0]), pw[e][1] = __uint_as_float(xw[1]);
     }
     gvn = io.G[rs.sh * C + lane];
     glastn = io.G[rs.sh * C + C - 1];
   };
-  // K, Q and W go to LDS as loaded (no register transpose: a transpose of the
-  // prefetched quads would make the loads complete before the chunk computes)
-  auto put_k = [&]() {
+  auto put_k = [&](int m, const Parts& y) {  // row kr0 + m
+    uint32_t* d = &sK[(kr0 + m) * WR + 12 * kgp];
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) *reinterpret_cast<float4*>(sK + (r0 + m) * KS + 4 * cq) = pk[m];
+    for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4_t*>(d + 4 * q) = y.p[q];
   };
-  auto put_qw = [&]() {  // W stored negated: the update adds (-W^T) dDelta
+  auto put_t = [&](uint32_t* base, int c, const Parts& y) {  // column 2 qc + c of Q^T or -W^T
+    uint32_t* d = &base[(2 * qc + c) * KR + 12 * qslot];
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-      *reinterpret_cast<float4*>(sQ + (r0 + m) * KS + 4 * cq) = pq[m];
-      const float4 wv = pw[m];
-      *reinterpret_cast<float4*>(sW + (r0 + m) * KS + 4 * cq) = float4{-wv.x, -wv.y, -wv.z, -wv.w};
-    }
-    // every wave writes the same values (no branch)
-    sLam[lane] = expf(glastn - gvn);
-    sGam[lane] = expf(gvn);
+    for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4_t*>(d + 4 * q) = y.p[q];
+  };
+  auto col = [](float (&x)[8], const float (&src)[8][2], int c, bool neg) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = neg ? -src[e][c] : src[e][c];
+  };
+  auto put_gl = [&]() {  // every wave writes the same values (no branch)
+    // the lane index is re-derived here so that the two LDS addresses are
+    // formed where they are used instead of being kept (and spilled) across
+    // the loop
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    sLam[l] = expf(glastn - gvn);
+    sGam[l] = expf(gvn);
   };
   // E and dO of a chunk in accumulator layout: (p = 16 pb + 4 g + r, j)
   auto load_ed = [&](float (&e)[4][4], float (&d)[4][4], int64_t c) {
@@ -2680,6 +2708,24 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
                          static_cast<const float*>(nullptr));
       }
   };
+  auto tiles8 = [](float (&x)[8], v4f a, v4f b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = a[e], x[4 + e] = b[e];
+  };
+  // A operands: part q of K rows 16 pb + l16 in k block kb; of Q^T or -W^T
+  // rows 16 (4 h2 + t) + l16 in k block kp
+  auto read_k = [&](u32x4_t (&x)[4], int kb, int q) {
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+      x[pb] = *reinterpret_cast<const u32x4_t*>(&sK[(16 * pb + l16) * WR + 12 * (4 * kb + g) + 4 * q]);
+  };
+  auto read_t = [&](u32x4_t (&x)[4], const uint32_t* base, int kp, int h2, int q) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = 16 * (4 * h2 + t) + l16;
+      x[t] = *reinterpret_cast<const u32x4_t*>(&base[i * KR + 12 * ((4 * kp + g) ^ ((i >> 3) & 7)) + 4 * q]);
+    }
+  };
 
   // state gradient dS'^T tiles: (i = 16 ib + 4 g + r, j)
   v4f st[8];
@@ -2693,67 +2739,70 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
   }
 
   float glast = 0.0f;  // G at the end of the current chunk
-  if (nchunks > 0) {   // the last chunk's operands
+  if (nchunks > 0) {   // the last chunk's K to LDS; its Q, W and G in registers
     const OpRes rs = op_res(nchunks - 1);
     load_k(rs);
     load_qw(rs);
-    put_k();
-    put_qw();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) put_k(m, split8(pk[m]));
     glast = glastn;
   }
+  Parts b = split8(st[0], st[1]);  // B parts of dDelta's first k block
   __syncthreads();
   for (int64_t c = nchunks - 1; c >= 0; --c) {
     const int64_t sh = (slot0 + c) * io.H_v + h;
     const int rows = rows_of(c);
     const OpRes nres = op_res(c > 0 ? c - 1 : c);  // the next chunk (c - 1), or chunk 0 again
-    // dDelta tiles (p = 16 pb + 4 g + r, j): k = i from the state registers.
-    // A operands (K) are read from LDS one k block ahead of their use.
-    float4 a[2][4];
-    auto read_k = [&](float4 (&x)[4], int ib) {
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb)
-        x[pb] = *reinterpret_cast<const float4*>(sK + (16 * pb + l16) * KS + 16 * ib + 4 * g);
-    };
-    read_k(a[0], 0);
+    put_gl();  // this chunk's lam and gam (the previous ones were read before the last barrier)
     float ec[4][4], dc[4][4];  // land while dDelta is computed
     load_ed(ec, dc, c);
-    load_k(nres);
-    // the incoming state gradient (a store) between the dDelta products
     const brsrc_t rs = make_rsrc(io.dstates + sh * DD, D * D * 4u);
     v4f dd[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) dd[pb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- dDelta tiles (p = 16 pb + 4 g + r, j): k = i; beside them this
+    // chunk's Q and -W go to LDS as parts, a column per block
 #pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      const float4(&x)[4] = a[ib & 1];
-      if (ib + 1 < 8) read_k(a[(ib + 1) & 1], ib + 1);
-      __builtin_amdgcn_sched_barrier(0);  // the reads issue before this block's products
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          const float xa = r == 0 ? x[pb].x : r == 1 ? x[pb].y : r == 2 ? x[pb].z : x[pb].w;
-          dd[pb] = mfma4(xa, st[ib][r], dd[pb]);
+    for (int kb = 0; kb < 4; ++kb) {
+      u32x4_t a0[4], a1[4], a2[4];
+      read_k(a0, kb, 0);
+      read_k(a1, kb, 1);
+      read_k(a2, kb, 2);
+      Parts bn = b, pt;
+      {
+        float xt[8];
+        col(xt, kb < 2 ? pq : pw, kb & 1, kb >= 2);
+        if (kb + 1 < 4) {
+          float xb[8];
+          tiles8(xb, st[2 * kb + 2], st[2 * kb + 3]);
+          split8x2(xb, xt, bn, pt);
+        } else {
+          pt = split8(xt);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        stbuf(st[ib][r], rs, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
-        __builtin_amdgcn_sched_barrier(0);
+        put_t(kb < 2 ? sQ : sW, kb & 1, pt);
       }
+      // the incoming state gradient (a store), tiles 2 kb and 2 kb + 1
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ib = 2 * kb + e / 4, r = e % 4;
+        stbuf(st[ib][r], rs, fj, static_cast<uint32_t>((16 * ib + r) * D * 4));
+      }
+#pragma unroll
+      for (int bq = 0; bq < 3; ++bq)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma_bf(a0[pb], b.p[bq], dd[pb]);
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma_bf(a1[pb], b.p[bq], dd[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) dd[pb] = mfma_bf(a2[pb], b.p[0], dd[pb]);
+      mfma_valu_pattern<24, 12>();
+      __builtin_amdgcn_sched_barrier(0);
+      b = bn;
     }
-    __syncthreads();  // every wave has read this chunk's K; sGam, sLam, Q, W are written
-    // A operand Q^T or -W^T (i = 16 (4 h2 + q) + l16, p = 16 pb + 4 g + r), a
-    // column of Q or -W, read from LDS one group of four tiles ahead of its use;
-    // the first read goes ahead of the next chunk's K
-    float aq[2][4][4];
-    auto read_qw = [&](float (&x)[4][4], int it) {
-      const float* src = (it < 8 ? sQ : sW) + (16 * ((it % 8) / 2) + 4 * g) * KS + 16 * (4 * (it % 2)) + l16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[q][r] = src[r * KS + 16 * q];
-    };
-    read_qw(aq[0], 0);
-    put_k();  // the next chunk's K
+    __syncthreads();  // every wave has read this chunk's K; Q, W, sGam and sLam are written
     const brsrc_t rd = make_rsrc(io.dD + sh * CD, C * D * 4u);
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb)
@@ -2765,32 +2814,52 @@ __global__ __launch_bounds__(512) void k_bwd_scan_m(BwdIO io) {
         stbuf(dd[pb][r], rd, fj, static_cast<uint32_t>((16 * pb + r) * D * 4));
         dc[pb][r] = sGam[p] * dc[pb][r];  // gam dO
       }
-    // dS^T = gam_last dS'^T + Q^T (gam dO) - W^T dDelta: k = p from registers
+    // ---- dS^T = gam_last dS'^T + Q^T (gam dO) - W^T dDelta: k = p from
+    // registers; beside the products the next chunk's K goes to LDS as parts
     const float gl = expf(glast);
-    v4f dcv[4];
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dcv[pb][r] = dc[pb][r];
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib) st[ib] = gl * st[ib];
-    load_qw(nres);  // the next chunk's Q, W and G, issued ahead of the products
+    load_k(nres);  // the next chunk's K: to LDS beside these products
+    Parts bq0 = b, bq1 = b, bw0 = b, bw1 = b;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {  // Q^T (gam dO), then -W^T dDelta; (pb, h2) per op
-      const int op = it / 8, pb = (it % 8) / 2, h2 = it % 2;
-      const float(&x)[4][4] = aq[it & 1];
-      if (it + 1 < 16) read_qw(aq[(it + 1) & 1], it + 1);
+    for (int it = 0; it < 8; ++it) {  // op (Q, then W), k block kp, tiles 4 h2 .. 4 h2 + 3
+      const int op = it / 4, kp = (it / 2) % 2, h2 = it % 2;
+      const uint32_t* src = op == 0 ? sQ : sW;
+      u32x4_t a0[4], a1[4], a2[4];
+      read_t(a0, src, kp, h2, 0);
+      read_t(a1, src, kp, h2, 1);
+      read_t(a2, src, kp, h2, 2);
+      if (it == 0) {
+        float x[8], y[8];
+        tiles8(x, v4f{dc[0][0], dc[0][1], dc[0][2], dc[0][3]}, v4f{dc[1][0], dc[1][1], dc[1][2], dc[1][3]});
+        tiles8(y, v4f{dc[2][0], dc[2][1], dc[2][2], dc[2][3]}, v4f{dc[3][0], dc[3][1], dc[3][2], dc[3][3]});
+        split8x2(x, y, bq0, bq1);
+      }
+      if (it == 3 || it == 4) {  // dDelta's k block it - 3 with the next chunk's K row it - 3
+        float x[8];
+        tiles8(x, dd[2 * (it - 3)], dd[2 * (it - 3) + 1]);
+        split8x2(x, pk[it - 3], it == 3 ? bw0 : bw1, b);
+        put_k(it - 3, b);
+      }
+      if (it == 7) b = split8(st[0], st[1]);  // the next chunk's first B parts (tiles 0..3 are final)
+      const Parts& bb = op == 0 ? (kp == 0 ? bq0 : bq1) : (kp == 0 ? bw0 : bw1);
+#pragma unroll
+      for (int bq = 0; bq < 3; ++bq)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) st[4 * h2 + t] = mfma_bf(a0[t], bb.p[bq], st[4 * h2 + t]);
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) st[4 * h2 + t] = mfma_bf(a1[t], bb.p[bq], st[4 * h2 + t]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) st[4 * h2 + t] = mfma_bf(a2[t], bb.p[0], st[4 * h2 + t]);
+      mfma_valu_pattern<24, 12>();
       __builtin_amdgcn_sched_barrier(0);
-      const v4f bv = op == 0 ? dcv[pb] : dd[pb];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st[4 * h2 + q] = mfma4(x[q][r], bv[r], st[4 * h2 + q]);
-      __builtin_amdgcn_sched_barrier(0);
+      if (it == 3) load_qw(nres);  // the next chunk's Q, W and G: to LDS beside its dDelta products
     }
-    __syncthreads();  // every wave has read this chunk's Q, W, sGam and sLam
-    put_qw();         // the next chunk's
     glast = glastn;
+    __syncthreads();  // every wave has read this chunk's Q, W, sGam and sLam; the next K is written
   }
   const brsrc_t rh0 = make_rsrc(io.dh0 + nh * DD, D * D * 4u);
 #pragma unroll
@@ -4459,8 +4528,9 @@ int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
 }
 
 const char* gdn_contract_id(void) {
-  return "gdn-cpr/v9;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
-         "B=mfma16x16x4-wy-blocked16-diaginv,bf16x3-mfma16x16x32-scan-regB;prep=wave-butterfly;src=" GDN_SOURCE_DIGEST;
+  return "gdn-cpr/v10;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
+         "B=mfma16x16x4-wy-blocked16-diaginv,bf16x3-mfma16x16x32-scan-regB;prep=wave-butterfly;"
+         "bwd-scan=bf16x3-mfma16x16x32;src=" GDN_SOURCE_DIGEST;
 }
 
 int gdn_contract_check(const char* id) {
