@@ -2891,30 +2891,50 @@ __device__ __forceinline__ float oct_sum(float x) {
 //   SdO[p][n] = sum_k dO[p][k] S[n][k]      SdD[p][n] = sum_k dDelta[p][k] S[n][k]
 //   DsD[p][n] = sum_k Delta[p][k] dS'[n][k]  MdM = sum_{n,k} S[n][k] dS'[n][k]
 // with S, dS' in their stored layout: wave w streams rows n = 16 w + l16,
-// which are its own output columns, and k runs in steps of 16 with lane
-// group g supplying k = 16 s + 4 g + c at component c.
+// which are its own output columns.  These products and Z = dO Delta^T take
+// their fp32 operands as three bf16 parts on v_mfma_f32_16x16x32_bf16 (the six
+// part products of the chunk scan, in the same order), k = 32 kb + 8 g + e for
+// element e of lane group g: dO, Delta and dDelta are split once into LDS
+// (row p, group k / 8, part, eight elements in 16 bytes), a wave's S and dS'
+// rows in registers.
+__device__ __forceinline__ v4f mfma_six(const Parts& a, const Parts& b, v4f c) {
+  c = mfma_bf(a.p[0], b.p[0], c);
+  c = mfma_bf(a.p[0], b.p[1], c);
+  c = mfma_bf(a.p[0], b.p[2], c);
+  c = mfma_bf(a.p[1], b.p[0], c);
+  c = mfma_bf(a.p[1], b.p[1], c);
+  return mfma_bf(a.p[2], b.p[0], c);
+}
 template <int C, typename TIn>
 __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   constexpr int D = 128, CS = C + 4, KS = D + 4, YS = 2 * D + 4;
   static_assert(C == 64, "tiling assumes C = 64");
-  // QK (later F = E2 + E2^T), KG = (k_p . k_r) Gam_pr (r < p), Z (later dA);
-  // before them dDelta (the products' operand), then DsD (row reads)
-  __shared__ __attribute__((aligned(16))) float sX[3 * C * CS];
-  static_assert(C * KS <= 2 * C * CS, "dDelta and DsD fit below Z");
-  float* sQK = sX;
-  float* sKG = sX + C * CS;
-  float* sZ = sX + 2 * C * CS;
-  float* sdD = sX;
+  // One LDS pool (words):
+  //   Z [0, C CS), QK (later F = E2 + E2^T), KG = (k_p . k_r) Gam_pr (r < p),
+  //   K [3 C CS, + C KS), Y [3 C CS + C KS, + 2 C KS): Q | R, then Y;
+  // R holds DsD, then SdO, for row reads.  Before the Z phase ends the pool
+  // holds the parts of dDelta, dO and Delta from word 0 (PT words each).
+  constexpr int PR = 16 * 12 + 4;  // words per parts row: 16 groups x 3 parts x 16 bytes, + 16 bytes
+  constexpr int PT = C * PR;
+  constexpr int oQK = C * CS, oKG = 2 * C * CS, oK = 3 * C * CS, oY = oK + C * KS;
+  constexpr int NPOOL = oY + 2 * C * KS;
+  static_assert(3 * PT <= NPOOL && C * YS <= 2 * C * KS, "pool layout");
+  static_assert(C * CS <= PT, "Z is written over dDelta's parts only");
+  __shared__ __attribute__((aligned(16))) float pool[NPOOL];
+  uint32_t* const pdD = reinterpret_cast<uint32_t*>(pool);
+  uint32_t* const pdO = pdD + PT;
+  uint32_t* const pDl = pdD + 2 * PT;
+  float* const sZ = pool;
+  float* const sQK = pool + oQK;
+  float* const sKG = pool + oKG;
+  float* const sK = pool + oK;
+  float* const sY = pool + oY;
+  float* const sQ = sY;
+  float* const sR = sY + C * KS;
   __shared__ float red[8];
-  __shared__ __attribute__((aligned(16))) float sK[C * KS];
-  __shared__ __attribute__((aligned(16))) float sY[2 * C * KS];  // dO | Delta, then Q | SdO, then Y
   __shared__ float sG[C], sB[C], sGam[C], sdB[C];
   __shared__ __attribute__((aligned(16))) float sLam[C], skd[C];
   __shared__ __attribute__((aligned(16))) float sdG[C];
-  static_assert(C * YS <= 2 * C * KS, "Y must fit");
-  float* sO = sY;
-  float* sD = sY + C * KS;
-  float* sQ = sY;
   int64_t slot, tok0;
   int L, h;
   if (!bwd_item<C>(io, slot, h, tok0, L)) return;
@@ -2940,33 +2960,50 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     const float bx = io.beta[(tok0 + crow(tid)) * io.H_v + h];
     sB[tid] = tid < L ? bx : 0.0f;
   }
-  static_assert((C * (D / 4)) % 512 == 0, "whole rounds");
-  constexpr int NR = (C * (D / 4)) / 512;  // float4 of a C x D tile per thread
-  float4 pq[NR];
+  // dO, Delta, dDelta split into parts: thread t takes (row, group) pairs t and
+  // t + 512, row = pair / 16, eight elements from k = 8 (pair % 16); rows past
+  // the chunk's end are 0
+  {
+    float4 x[3][2][2];
 #pragma unroll
-  for (int e_ = 0; e_ < NR; ++e_) {
-    const int e = tid + 512 * e_;
-    const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
-    const float4 k4 = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
-    const float4 o4 = *reinterpret_cast<const float4*>(dO + pc * vs + 4 * i4);
-    const float4 d4 = *reinterpret_cast<const float4*>(Dl + p * D + 4 * i4);
-    const float4 dd4 = *reinterpret_cast<const float4*>(dDl + p * D + 4 * i4);
-    *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) = sel4(p < L, k4, z4);
-    *reinterpret_cast<float4*>(sO + p * KS + 4 * i4) = sel4(p < L, o4, z4);
-    *reinterpret_cast<float4*>(sD + p * KS + 4 * i4) = sel4(p < L, d4, z4);
-    *reinterpret_cast<float4*>(sdD + p * KS + 4 * i4) = sel4(p < L, dd4, z4);
+    for (int j = 0; j < 2; ++j) {
+      const int pair = tid + 512 * j, p = pair >> 4, q = pair & 15, pc = crow(p);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        x[0][j][hf] = *reinterpret_cast<const float4*>(dDl + p * D + 8 * q + 4 * hf);
+        x[1][j][hf] = *reinterpret_cast<const float4*>(dO + pc * vs + 8 * q + 4 * hf);
+        x[2][j][hf] = *reinterpret_cast<const float4*>(Dl + p * D + 8 * q + 4 * hf);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pair = tid + 512 * j, p = pair >> 4, q = pair & 15;
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        const float4 a = sel4(p < L, x[m][j][0], z4), b = sel4(p < L, x[m][j][1], z4);
+        const Parts y = split8(v4f{a.x, a.y, a.z, a.w}, v4f{b.x, b.y, b.z, b.w});
+        uint32_t* d = pdD + m * PT + p * PR + 12 * q;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) *reinterpret_cast<u32x4_t*>(d + 4 * t) = y.p[t];
+      }
+    }
   }
-  // this lane's 16-byte pieces of its S and dS' rows, one per k step, loaded
-  // two steps ahead (the first two before the staging barrier)
+  // this lane's S and dS' row pieces (k = 32 kb + 8 g .. + 7), one k block ahead
   const int64_t DD = static_cast<int64_t>(D) * D;
-  const float* xs1 = io.states + sh * DD + col * D + 4 * g;
-  const float* xs2 = io.dstates + sh * DD + col * D + 4 * g;
-  float4 p1[D / 16], p2[D / 16];
+  const float* xs1 = io.states + sh * DD + col * D + 8 * g;
+  const float* xs2 = io.dstates + sh * DD + col * D + 8 * g;
+  float4 c1[2], c2[2], n1[2], n2[2];
 #pragma unroll
-  for (int s4 = 0; s4 < 2; ++s4) {
-    p1[s4] = *reinterpret_cast<const float4*>(xs1 + 16 * s4);
-    p2[s4] = *reinterpret_cast<const float4*>(xs2 + 16 * s4);
+  for (int hf = 0; hf < 2; ++hf) {
+    c1[hf] = *reinterpret_cast<const float4*>(xs1 + 4 * hf);
+    c2[hf] = *reinterpret_cast<const float4*>(xs2 + 4 * hf);
   }
+  // dDelta's column col, the back substitution's right-hand side for tile 1
+  float rh[4][2][4];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rh[bi][1][r] = dDl[(16 * bi + 4 * g + r) * D + col];
   __syncthreads();
   const float glast = sG[C - 1];
   if (tid < C) {
@@ -2981,100 +3018,92 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
     for (int mb = 0; mb < 4; ++mb) acc[pr][mb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   float mdm = 0.0f;
 #pragma unroll
-  for (int s4 = 0; s4 < D / 16; ++s4) {
-    if (s4 + 2 < D / 16) {
-      p1[s4 + 2] = *reinterpret_cast<const float4*>(xs1 + 16 * (s4 + 2));
-      p2[s4 + 2] = *reinterpret_cast<const float4*>(xs2 + 16 * (s4 + 2));
+  for (int kb = 0; kb < 4; ++kb) {
+    if (kb + 1 < 4) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        n1[hf] = *reinterpret_cast<const float4*>(xs1 + 32 * (kb + 1) + 4 * hf);
+        n2[hf] = *reinterpret_cast<const float4*>(xs2 + 32 * (kb + 1) + 4 * hf);
+      }
     }
-    const float4 c1 = p1[s4], c2 = p2[s4];
-    mdm = fmaf(c1.x, c2.x, mdm);
-    mdm = fmaf(c1.y, c2.y, mdm);
-    mdm = fmaf(c1.z, c2.z, mdm);
-    mdm = fmaf(c1.w, c2.w, mdm);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      mdm = fmaf(c1[hf].x, c2[hf].x, mdm);
+      mdm = fmaf(c1[hf].y, c2[hf].y, mdm);
+      mdm = fmaf(c1[hf].z, c2[hf].z, mdm);
+      mdm = fmaf(c1[hf].w, c2[hf].w, mdm);
+    }
+    const Parts b1 = split8(v4f{c1[0].x, c1[0].y, c1[0].z, c1[0].w}, v4f{c1[1].x, c1[1].y, c1[1].z, c1[1].w});
+    const Parts b2 = split8(v4f{c2[0].x, c2[0].y, c2[0].z, c2[0].w}, v4f{c2[1].x, c2[1].y, c2[1].z, c2[1].w});
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int ro = (16 * mb + l16) * KS + 16 * s4 + 4 * g;
-      const float4 y0 = *reinterpret_cast<const float4*>(sO + ro);
-      const float4 y1 = *reinterpret_cast<const float4*>(sdD + ro);
-      const float4 y2 = *reinterpret_cast<const float4*>(sD + ro);
-      acc[0][mb] = mfma4(y0.x, c1.x, acc[0][mb]);
-      acc[1][mb] = mfma4(y1.x, c1.x, acc[1][mb]);
-      acc[2][mb] = mfma4(y2.x, c2.x, acc[2][mb]);
-      acc[0][mb] = mfma4(y0.y, c1.y, acc[0][mb]);
-      acc[1][mb] = mfma4(y1.y, c1.y, acc[1][mb]);
-      acc[2][mb] = mfma4(y2.y, c2.y, acc[2][mb]);
-      acc[0][mb] = mfma4(y0.z, c1.z, acc[0][mb]);
-      acc[1][mb] = mfma4(y1.z, c1.z, acc[1][mb]);
-      acc[2][mb] = mfma4(y2.z, c2.z, acc[2][mb]);
-      acc[0][mb] = mfma4(y0.w, c1.w, acc[0][mb]);
-      acc[1][mb] = mfma4(y1.w, c1.w, acc[1][mb]);
-      acc[2][mb] = mfma4(y2.w, c2.w, acc[2][mb]);
+      const int ro = (16 * mb + l16) * PR + 12 * (4 * kb + g);
+      Parts a0, a1, a2;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        a0.p[t] = *reinterpret_cast<const u32x4_t*>(pdO + ro + 4 * t);
+        a1.p[t] = *reinterpret_cast<const u32x4_t*>(pdD + ro + 4 * t);
+        a2.p[t] = *reinterpret_cast<const u32x4_t*>(pDl + ro + 4 * t);
+      }
+      acc[0][mb] = mfma_six(a0, b1, acc[0][mb]);
+      acc[1][mb] = mfma_six(a1, b1, acc[1][mb]);
+      acc[2][mb] = mfma_six(a2, b2, acc[2][mb]);
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep each step's loads two steps ahead
+    if (kb + 1 < 4) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) c1[hf] = n1[hf], c2[hf] = n2[hf];
+    }
   }
   // <S, dS'>: wave butterfly, then the 8 wave sums in ascending order (tid 0)
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mdm = mdm + __shfl_xor(mdm, off, 64);
   if (lane == 0) red[w] = mdm;
-  // the right-hand side of the back substitution, columns col of -SdD and of
-  // dDelta: SdD from the products, dDelta from its LDS tile
-  float rh[4][2][4];
-#pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      rh[bi][0][r] = acc[1][bi][r];
-      rh[bi][1][r] = sdD[(16 * bi + 4 * g + r) * KS + col];
-    }
-  __syncthreads();  // the products' reads of dDelta are done: DsD takes its place
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sdD[(16 * mb + 4 * g + r) * KS + col] = acc[2][mb][r];
-  float MdM = 0.0f;  // thread 0's
-  if (tid == 0) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) MdM = MdM + red[q];
-  }
-  __syncthreads();
-  // the dG term through the state update, k . DsD per row (8 lanes per row,
-  // each a 16-element chain over its part)
-  {
-    const int pp = tid >> 3, part = tid & 7;
-    float kd = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int i = 16 * part + 4 * m;
-      const float4 rD = *reinterpret_cast<const float4*>(sdD + pp * KS + i);
-      kd = fmaf(sK[pp * KS + i], rD.x, kd);
-      kd = fmaf(sK[pp * KS + i + 1], rD.y, kd);
-      kd = fmaf(sK[pp * KS + i + 2], rD.z, kd);
-      kd = fmaf(sK[pp * KS + i + 3], rD.w, kd);
-    }
-    kd = oct_sum(kd);
-    if (part == 0) skd[pp] = pp < L ? kd : 0.0f;
-  }
-  // Operands of later phases are fetched ahead of their use: Q.
-#pragma unroll
-  for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
-    const int e = tid + 512 * e_;
-    const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
-    pq[e_] = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
-  }
+  // -SdD's column col: the back substitution's right-hand side for tile 0
   float pS[4][4], pD[4][4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       pS[mb][r] = acc[0][mb][r];
+      rh[mb][0][r] = acc[1][mb][r];
       pD[mb][r] = acc[2][mb][r];
     }
+  // Q and K, fetched during the Z products and written once dO's and Delta's
+  // parts are dead
+  static_assert((C * (D / 4)) % 512 == 0, "whole rounds");
+  constexpr int NR = (C * (D / 4)) / 512;  // float4 of a C x D tile per thread
+  float4 pq[NR], pk[NR];
+#pragma unroll
+  for (int e_ = 0; e_ < NR; ++e_) {
+    const int e = tid + 512 * e_;
+    const int p = e / (D / 4), i4 = e % (D / 4), pc = crow(p);
+    pk[e_] = *reinterpret_cast<const float4*>(kq + pc * 2 * D + 4 * i4);
+    pq[e_] = *reinterpret_cast<const float4*>(kq + pc * 2 * D + D + 4 * i4);
+  }
+  __syncthreads();  // dDelta's parts are dead: Z takes their place
+  float MdM = 0.0f;  // thread 0's
+  if (tid == 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) MdM = MdM + red[q];
+  }
   // ---- Z = (dO Delta^T) . Gam, masked r <= p
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int nb = tnb0 + 2 * t;
     v4f dp = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (nb <= tmb) dp = mma_nt<D>(dp, sO + (16 * tmb + l16) * KS, sD + (16 * nb + l16) * KS, g);
+    if (nb <= tmb) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int ra = (16 * tmb + l16) * PR + 12 * (4 * kb + g), rb = (16 * nb + l16) * PR + 12 * (4 * kb + g);
+        Parts a, b;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          a.p[q] = *reinterpret_cast<const u32x4_t*>(pdO + ra + 4 * q);
+          b.p[q] = *reinterpret_cast<const u32x4_t*>(pDl + rb + 4 * q);
+        }
+        dp = mfma_six(a, b, dp);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int pp = 16 * tmb + 4 * g + r, qq = 16 * nb + l16;
@@ -3084,12 +3113,34 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
   }
   __syncthreads();  // dO and Delta are dead
 #pragma unroll
-  for (int e_ = 0; e_ < (C * (D / 4)) / 512; ++e_) {
+  for (int e_ = 0; e_ < NR; ++e_) {
     const int e = tid + 512 * e_;
     const int p = e / (D / 4), i4 = e % (D / 4);
+    *reinterpret_cast<float4*>(sK + p * KS + 4 * i4) = sel4(p < L, pk[e_], z4);
     *reinterpret_cast<float4*>(sQ + p * KS + 4 * i4) = sel4(p < L, pq[e_], z4);
   }
+  // DsD for the row reads of the dG term through the state update
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sR[(16 * mb + 4 * g + r) * KS + col] = pD[mb][r];
   __syncthreads();
+  // k . DsD per row (8 lanes per row, each a 16-element chain over its part)
+  {
+    const int pp = tid >> 3, part = tid & 7;
+    float kd = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = 16 * part + 4 * m;
+      const float4 rD = *reinterpret_cast<const float4*>(sR + pp * KS + i);
+      kd = fmaf(sK[pp * KS + i], rD.x, kd);
+      kd = fmaf(sK[pp * KS + i + 1], rD.y, kd);
+      kd = fmaf(sK[pp * KS + i + 2], rD.z, kd);
+      kd = fmaf(sK[pp * KS + i + 3], rD.w, kd);
+    }
+    kd = oct_sum(kd);
+    if (part == 0) skd[pp] = pp < L ? kd : 0.0f;
+  }
   // ---- QK (r <= p) and KK Gam (r < p)
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -3108,12 +3159,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
       sKG[pp * CS + qq] = (in && qq < pp) ? kk[r] * gam : 0.0f;
     }
   }
-  __syncthreads();
-  // SdO into Delta's old place, for the row reads of the dG terms below
+  __syncthreads();  // the DsD row reads are done
+  // SdO, for the row reads of the dG terms below
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sD[(16 * mb + 4 * g + r) * KS + col] = pS[mb][r];
+    for (int r = 0; r < 4; ++r) sR[(16 * mb + 4 * g + r) * KS + col] = pS[mb][r];
   // ---- dq-hat = gam SdO + Z K  and  dk-hat (partial) = lam DsD + Z^T Q; wave w
   // owns columns i = 16 w + l16, all four row blocks
   v4f dk[4];
@@ -3143,7 +3194,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int i = 16 * part + 4 * m;
-      const float4 rS = *reinterpret_cast<const float4*>(sD + pp * KS + i);
+      const float4 rS = *reinterpret_cast<const float4*>(sR + pp * KS + i);
       qs = fmaf(sQ[pp * KS + i], rS.x, qs);
       qs = fmaf(sQ[pp * KS + i + 1], rS.y, qs);
       qs = fmaf(sQ[pp * KS + i + 2], rS.z, qs);
@@ -4528,9 +4579,9 @@ int gdn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
 }
 
 const char* gdn_contract_id(void) {
-  return "gdn-cpr/v10;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
+  return "gdn-cpr/v11;eps=1e-6;claims=d16C16,d128C64;R=lane-row,dk-halves-at-d128,fmaf-asc,o-after-update;"
          "B=mfma16x16x4-wy-blocked16-diaginv,bf16x3-mfma16x16x32-scan-regB;prep=wave-butterfly;"
-         "bwd-scan=bf16x3-mfma16x16x32;src=" GDN_SOURCE_DIGEST;
+         "bwd=bf16x3-mfma16x16x32-scan-stateproducts-Z;src=" GDN_SOURCE_DIGEST;
 }
 
 int gdn_contract_check(const char* id) {
