@@ -1584,6 +1584,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   // staged half a chunk at a time so that three blocks fit a CU's LDS
   constexpr int SC = (sizeof(TIn) == 4 && D == 128) ? C / 2 : C;
   __shared__ TIn sv[NW][SC][64];
+  __shared__ float2 sgb[8][C];  // (g, beta) of the block's heads, token order
   const int slot = blockIdx.x;
   const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wv = blockIdx.z * hpb * RS::WPH + wl;
@@ -1606,10 +1607,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   const int64_t DD = static_cast<int64_t>(D) * D;
   const int vs = io.H_v * D;  // < 2^20 (host-checked)
   const int i0 = kh * DK;     // first d_k element of this wave
-  // Token operands of the chunk: g and beta as wave-uniform scalar loads, v
-  // and o through buffer resources over the chunk's rows (lane offset in a
+  // Token operands of the chunk: g and beta from LDS (one broadcast read per
+  // token, so that the scalar cache serves only the key/query stream), v from
+  // LDS, o through a buffer resource over the chunk's rows (lane offset in a
   // VGPR, token offset in an SGPR).
-  cfloat_p gbt = as_const(io.gb + (static_cast<int64_t>(h) * io.T + tok0) * 2);
   float* obase = io.o + (tok0 * io.H_v + h) * D;
   const uint32_t otok = static_cast<uint32_t>(vs) * 4u;
   const brsrc_t orr = make_rsrc(obase, static_cast<uint32_t>(L - 1) * otok + D * 4u);
@@ -1629,8 +1630,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
       sv[q][tt][ll] = row < D ? vin[(tok0 + tc) * io.H_v * D + static_cast<int64_t>(hb + q / NH) * D + row]
                               : TIn(0);
     }
+    for (int e = threadIdx.x; e < hpb * C; e += blockDim.x) {
+      const int hh = e / C, tt = e % C;
+      const int tc = tt < L ? tt : L - 1;
+      sgb[hh][tt] = *reinterpret_cast<const float2*>(io.gb + ((static_cast<int64_t>(hb + hh) * io.T) + tok0 + tc) * 2);
+    }
   }
   __syncthreads();
+  const int hl = wl / RS::WPH;  // the wave's head within the block
 
   float s[DK];
   const float* st = io.states + (static_cast<int64_t>(slot) * io.H_v + h) * DD;
@@ -1656,14 +1663,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   // g, beta and v are loaded one token ahead; the last token reloads itself
   // rather than reading past the chunk
   uint32_t pp0 = 0, pp1 = 0, psink = 0;
-  float gn = gbt[0], bn = gbt[1], vn = ldin(&sv[wp][0][lane]);
+  float gn = sgb[hl][0].x, bn = sgb[hl][0].y, vn = ldin(&sv[wp][0][lane]);
   for (int t = 0; t < L; ++t) {
     const float alpha = expf(gn);
     const float b = bn;
     const float vj = vn;
     const int tn = t + 1 < L ? t + 1 : t;
-    gn = gbt[2 * tn];
-    bn = gbt[2 * tn + 1];
+    {
+      const float2 x = sgb[hl][tn];
+      gn = x.x;
+      bn = x.y;
+    }
     if constexpr (SC < C) {
       // the second half: every wave read its last first-half row (token SC - 1)
       // one token ahead, before the previous token's exchange barrier
