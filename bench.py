@@ -486,8 +486,8 @@ def bench_fwd_bwd(args, B, torch, make_inputs):
     step()
     ms_step, prof = wall_then_profile(
         step, args.train_steps, 1,
-        ["k_prep", "k_wy", "k_scan", "k_rec", "k_bwd_prep", "k_bwd_scan", "k_bwd_mm",
-         "k_bwd_chunk", "k_bwd_qk"], B, torch)
+        ["k_prep", "k_wy", "k_scan", "k_rec", "k_bwd_prep", "k_bwd_scan", "k_bwd_chunk", "k_bwd_qk"],
+        B, torch)
     per = {name: round(1e3 * ms / max(n, 1), 1) for name, (ms, n) in prof.items()}
 
     def native_step():  # native-mixed baseline: chunk-form forward outputs
