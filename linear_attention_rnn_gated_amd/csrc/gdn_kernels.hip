@@ -1892,10 +1892,10 @@ struct BwdIO {
   float* E;               // [slot][H_v][C][D] P^T dO
   float* dstates;         // [slot][H_v][D][D] gradient of each chunk's end state
   float* dD;              // [slot][H_v][C][D] dDelta, then dX_u
+  // d = 16 only (the d = 128 chunk kernel forms these itself; null there):
   float* SdO;             // [slot][H_v][C][D] S^T dO_p
   float* DsD;             // [slot][H_v][C][D] dS'^T Delta_p
   float* SdD;             // [slot][H_v][C][D] S^T dDelta_p, then dX_w
-  float* MdM;             // [slot][H_v] <S, dS'> of each chunk (matrix-core path)
   float* dqv;             // [T][H_v][D] per value head
   float* dkv;             // [T][H_v][D]
   void* dv;               // [T][H_v][D], fp32 or (grad_bf16) bf16
@@ -4106,7 +4106,6 @@ int launch_fwd_bwd(const gdn_shape_t* s, int32_t N, const gdn::Counts& cnt, cons
     b.SdO = reinterpret_cast<float*>(ws + L.SdO);
     b.DsD = reinterpret_cast<float*>(ws + L.DsD);
     b.SdD = reinterpret_cast<float*>(ws + L.SdD);
-    b.MdM = reinterpret_cast<float*>(ws + L.MdM);
   }
   b.dqv = reinterpret_cast<float*>(ws + L.dqv);
   b.dkv = reinterpret_cast<float*>(ws + L.dkv);

@@ -91,7 +91,6 @@ Layout layout(const gdn_shape_t* s, int32_t N, int64_t T, int op) {
       L.SdO = take(&cur, cd);
       L.DsD = take(&cur, cd);
       L.SdD = take(&cur, cd);
-      L.MdM = take(&cur, L.state_slots * Hv * f);
     }
     L.dqv = take(&cur, T * Hv * d * f);
     L.dkv = take(&cur, T * Hv * d * f);

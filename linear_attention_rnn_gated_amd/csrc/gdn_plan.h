@@ -48,7 +48,6 @@ struct Layout {
   size_t SdO = 0;        // f32 [state_slots, H_v, C, d]
   size_t DsD = 0;        // f32 [state_slots, H_v, C, d]
   size_t SdD = 0;        // f32 [state_slots, H_v, C, d]  then dX_w
-  size_t MdM = 0;        // f32 [state_slots, H_v]  <S, dS'> per chunk
   size_t dqv = 0;        // f32 [T, H_v, d]  per value head dq-hat
   size_t dkv = 0;        // f32 [T, H_v, d]  per value head dk-hat
   // prefill continuation only: the extended batch (buffered + new tokens of

@@ -59,7 +59,7 @@ int main() {
       // in the order layout() hands them out
       const size_t regions[] = {L.cu_chunks, L.cu_full, L.qk,  L.W,      L.U,    L.G,     L.states,
                                 L.order,     L.Dl,      L.E,   L.dstates, L.dD,  L.SdO,   L.DsD,
-                                L.SdD,       L.MdM,     L.dqv, L.dkv,    L.cu_ext, L.v_ext, L.b_ext,
+                                L.SdD,       L.dqv,     L.dkv, L.cu_ext, L.v_ext, L.b_ext,
                                 L.g_ext,     L.o_ext};
       // offsets are aligned, inside the workspace (an empty region may sit at
       // its end) and never decrease (empty regions share an offset)
