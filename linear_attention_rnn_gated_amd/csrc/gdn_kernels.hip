@@ -3670,8 +3670,11 @@ struct Profiler {
       pool.pop_back();
       return e;
     }
+    // timing-only events: no system-scope fence (no cache writeback and
+    // invalidation around the timed launches); they are read only after the
+    // caller has synchronised the device
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
   }
 };
