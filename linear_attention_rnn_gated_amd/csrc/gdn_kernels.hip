@@ -3264,6 +3264,34 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) pv[i] = ldin(vin + i);
   }
+  // T_b = (I + A_bb)^-1 for the four diagonal 16 x 16 blocks: wave b < 4
+  // inverts block b by forward substitution on the identity (pivots 0..14 in
+  // order; a pivot's coefficients for rows at or above it are the masked
+  // tile's zeros), holding T[4 g + r][l16] in register r, and leaves it in Z's
+  // place (free until dA) for every wave: block bi's rows are then
+  // Y_bi = T_bi^T (right-hand side - sum_bj A_bj,bi^T Y_bj) on the matrix cores
+  float* const sT = sZ;  // [4][16][16]
+  if (w < 4) {  // wave-uniform
+    const int tb = w;
+    v4f t;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[r] = 4 * g + r == l16 ? 1.0f : 0.0f;
+#pragma unroll
+    for (int pp = 0; pp < 15; ++pp) {
+      float a[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * tb + 4 * g + r;
+        a[r] = sB[row] * sKG[row * CS + 16 * tb + pp];
+      }
+      const float y = __shfl(t[pp & 3], l16 + 16 * (pp >> 2), 64);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] = fmaf(-a[r], y, t[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sT[tb * 256 + (4 * g + r) * 16 + l16] = t[r];
+  }
+  __syncthreads();
   {
     v4f Y[4][2];
 #pragma unroll
@@ -3286,21 +3314,18 @@ __global__ __launch_bounds__(512) void k_bwd_chunk_m(BwdIO io) {
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) acc[ct] = mfma4(a, Y[bj][ct][s4], acc[ct]);
         }
-      // row pp (solved) is subtracted from the rows above it; the coefficients
-      // of rows at or below pp are the zeros of the masked Gram tile, so those
-      // rows keep their values (up to the sign of a zero).  Row 0 updates nothing.
+      // Y_bi = T_bi^T acc: k-step s takes T[4 g + s][l16] (lane group g) and
+      // acc row 4 g + s, which this lane holds in register s
+      {
+        float tA[4];
 #pragma unroll
-      for (int pp = 15; pp >= 1; --pp) {
-        const int gp = pp >> 2, rp = pp & 3;
-        const int prow = 16 * bi + pp;
-        float a[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = sB[prow] * sKG[prow * CS + 16 * bi + 4 * g + r];
+        for (int s2 = 0; s2 < 4; ++s2) tA[s2] = sT[bi * 256 + (4 * g + s2) * 16 + l16];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const float y = __shfl(acc[ct][rp], l16 + 16 * gp, 64);
+          v4f y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ct][r] = fmaf(-a[r], y, acc[ct][r]);
+          for (int s2 = 0; s2 < 4; ++s2) y = mfma4(tA[s2], acc[ct][s2], y);
+          acc[ct] = y;
         }
       }
 #pragma unroll
