@@ -38,7 +38,7 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3
 # taken on (sha256 prefix of gdn_kernels.hip); for any other source the
 # traffic field is reported as null.
 MEASURED_TRAFFIC = {
-    "be40735d4c1f27c8": {"k_rec": 612.6e6 + 134.2e6, "k_decode": 135.9e6 + 136.4e6},
+    "f56816315c954ec0": {"k_rec": 612.7e6 + 134.2e6, "k_decode": 135.9e6 + 136.4e6},
 }
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_rnn_gated_amd", "csrc", "gdn_kernels.hip")
 
